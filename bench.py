@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated delta rule hot path on one MI355X.
+
+One step = one pass over both forms of the path on synthetic inputs:
+  * decode:  one token for 64 sequences x 32 heads, dk = dv = 128, bf16 q/k/v,
+             fp32 state (128 MiB) updated in place, bf16 output;
+  * prefill: chunked prefill of 4 sequences x 4096 tokens, 16 heads,
+             dk = dv = 128, chunk 64, bf16 q/k/v, fp32 gates and states.
+The headline `value` is the decode state bandwidth (state bytes read + written
+per step / decode time); the prefill throughput is reported beside it.
+
+Decode is measured cold: four state buffers (512 MiB, more than the 256 MB
+Infinity Cache) are used in rotation.  Prefill writes a 1 GiB scrub buffer
+before every timed launch (outside the timed events).  Inputs are resident in
+HBM before timing starts.  Kernel times come from HIP events recorded on the
+stream the kernels are launched on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+
+# decode workload: N=64, H=32, d=128
+DEC_N, DEC_H, DEC_D = 64, 32, 128
+DEC_STATE_BYTES = DEC_N * DEC_H * DEC_D * DEC_D * 4 * 2          # read + write
+DEC_ALG_BYTES = DEC_STATE_BYTES + DEC_N * DEC_H * (3 * DEC_D * 2 + DEC_D * 2 + 8)
+# prefill workload: B=4, T=4096, H=16, d=128, C=64
+PRE_B, PRE_T, PRE_H, PRE_D, PRE_C = 4, 4096, 16, 128, 64
+PRE_TOKENS = PRE_B * PRE_T
+PRE_IO_BYTES = PRE_TOKENS * PRE_H * (3 * PRE_D * 2 + PRE_D * 2 + 8) \
+    + 2 * PRE_B * PRE_H * PRE_D * PRE_D * 4
+PRE_CHUNK_HEADS = PRE_B * (PRE_T // PRE_C) * PRE_H
+PRE_CP_BYTES = PRE_IO_BYTES + PRE_CHUNK_HEADS * 393216
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    return ap.parse_args()
+
+
+def to_dev(d, torch):
+    def io(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    out = {k: io(d[k]) for k in ("q", "k", "v")}
+    out["g"] = torch.from_numpy(d["g"]).cuda()
+    out["beta"] = torch.from_numpy(d["beta"]).cuda()
+    out["state0"] = None if d["state0"] is None else torch.from_numpy(d["state0"]).cuda()
+    out["cu"] = torch.from_numpy(d["cu_seqlens"].astype(np.int32)).cuda()
+    return out
+
+
+def bench_decode(torch, gdr, steps, warmup):
+    from gdr_synth import workload
+    d = workload(1)
+    di = to_dev(d, torch)
+    bufs = [di["state0"].clone() for _ in range(4)]
+    o = torch.empty(DEC_N, DEC_H, DEC_D, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def launch(i):
+        gdr.gdr_decode_step(di["q"], di["k"], di["v"], di["g"], di["beta"], bufs[i % 4], o,
+                            stream=stream)
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        launch(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [a.elapsed_time(b) for a, b in ev]
+    return dict(ms_mean=float(np.mean(ms)), ms_median=float(np.median(ms)),
+                ms_min=float(np.min(ms)), wall_s=wall)
+
+
+def bench_prefill(torch, gdr, steps, warmup):
+    from gdr_synth import workload
+    d = workload(2)
+    di = to_dev(d, torch)
+    T, H, D = PRE_TOKENS, PRE_H, PRE_D
+    o = torch.empty(T, H, D, dtype=torch.bfloat16, device="cuda")
+    sout = torch.empty_like(di["state0"])
+    ws = torch.empty(gdr.gdr_chunk_prefill_workspace_bytes(T, PRE_B, H, D, D, PRE_C),
+                     dtype=torch.uint8, device="cuda")
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        gdr.gdr_chunk_prefill(di["q"], di["k"], di["v"], di["g"], di["beta"], di["cu"],
+                              di["state0"], sout, o, chunk=PRE_C, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        scrub.fill_(float(i))
+        ev[i][0].record(stream)
+        launch()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [a.elapsed_time(b) for a, b in ev]
+    return dict(ms_mean=float(np.mean(ms)), ms_median=float(np.median(ms)),
+                ms_min=float(np.min(ms)), wall_s=wall)
+
+
+def cpu_baseline(budget_s):
+    """The fp64 oracle (token-by-token recurrence, OpenMP over (sequence, head))
+    on the host cores: the whole decode workload, repeated until about
+    budget_s/2 of work, and a sample of the prefill workload (whole sequences of
+    a subset of heads) for about budget_s/2."""
+    import oracle
+    from gdr_synth import workload
+    threads = oracle.max_threads()
+    d1 = workload(1)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.recurrent(d1["q"], d1["k"], d1["v"], d1["g"], d1["beta"], d1["cu_seqlens"],
+                         d1["state0"])
+        reps += 1
+        if time.perf_counter() - t0 > budget_s / 2 or reps >= 50:
+            break
+    dec_s = (time.perf_counter() - t0) / reps
+    d2 = workload(2, H=4)
+    # whole 4096-token sequences; every (sequence, head) pair costs the same
+    pairs = [(n, h) for n in range(PRE_B) for h in range(4)]
+    t0 = time.perf_counter()
+    done = 0
+    for i in range(0, len(pairs), max(threads, 1)):
+        chunk_pairs = pairs[i:i + max(threads, 1)]
+        oracle.recurrent(d2["q"], d2["k"], d2["v"], d2["g"], d2["beta"], d2["cu_seqlens"],
+                         d2["state0"], pairs=chunk_pairs)
+        done += len(chunk_pairs)
+        if time.perf_counter() - t0 > budget_s / 2:
+            break
+    pre_s = time.perf_counter() - t0
+    tok_heads_per_s = done * PRE_T / pre_s
+    return {
+        "value": DEC_STATE_BYTES / dec_s / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"fp64 recurrence over the whole decode workload (64x32 states, d=128), "
+                  f"{reps} repetition(s), {dec_s * 1e3:.1f} ms each; prefill sample: {done} "
+                  f"(sequence, head) pairs of 4096 tokens in {pre_s:.1f} s",
+        "prefill_tokens_per_s": tok_heads_per_s / PRE_H,
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards with no exchange across sequences/heads; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import torch
+    import gated_delta_rule_100_amd as gdr
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    print(f"[bench] decode: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
+    dec = bench_decode(torch, gdr, args.steps, args.warmup)
+    print(f"[bench] decode {dec}", file=sys.stderr, flush=True)
+    pre = bench_prefill(torch, gdr, args.steps, args.warmup)
+    print(f"[bench] prefill {pre}", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_seconds)
+        print(f"[bench] cpu {cpu}", file=sys.stderr, flush=True)
+
+    dec_s = dec["ms_mean"] / 1e3
+    pre_s = pre["ms_mean"] / 1e3
+    dec_gbs = DEC_STATE_BYTES / dec_s / 1e9
+    achieved = DEC_ALG_BYTES / dec_s / 1e9
+    out = {
+        "metric": "GDR decode state GB/s (% HBM peak); chunked-prefill tokens/s at H=16,d=128",
+        "value": round(dec_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_mean"] + pre["ms_mean"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 inputs, fp32 state and accumulation",
+        "data": "synthetic (seeded numpy PCG64; q,k L2-normalised; g=-softplus(N(0,1)); "
+                "beta=sigmoid(N(0,1)); S0~N(0,0.02))",
+        "config": {"workload": "decode N=64 H=32 dk=dv=128 bf16, state 128 MiB in place "
+                               "(cold: 4 rotating buffers) + chunked prefill B=4 T=4096 H=16 "
+                               "dk=dv=128 C=64 bf16",
+                   "decode_ms": round(dec["ms_mean"], 5), "prefill_ms": round(pre["ms_mean"], 5)},
+        "pct_hbm_peak": round(100.0 * dec_gbs / HBM_PEAK_GBS, 2),
+        "prefill": {
+            "value": round(PRE_TOKENS / pre_s, 1), "unit": "tokens/s",
+            "ms": round(pre["ms_mean"], 4),
+            "io_min_frac": round(PRE_IO_BYTES / pre_s / 1e9 / HBM_PEAK_GBS, 4),
+            "cp_form_frac": round(PRE_CP_BYTES / pre_s / 1e9 / HBM_PEAK_GBS, 4),
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "decode_kernel<128,128,bf16,bf16>",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

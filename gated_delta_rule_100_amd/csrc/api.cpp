@@ -1,0 +1,237 @@
+// api.cpp -- the C ABI of libgdr: host-side validation and dispatch.
+//
+// Every entry point validates its arguments on the host, records a message
+// for gdr_last_error() on failure and launches nothing in that case.  Nothing
+// here allocates, frees or synchronises; all work is enqueued on the caller's
+// stream.  The only global state is a per-device property cache (the
+// per-device attribute caching of the host launcher on the FlashInfer PR #4593
+// page, code analysis 1, follows the same pattern).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <mutex>
+#include <string_view>
+
+#include "../../include/gdr.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gdr_status fail(gdr_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+gdr_status ok() {
+  g_last_error[0] = '\0';
+  return GDR_OK;
+}
+
+gdr_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(GDR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_dims(int dk, int dv) { return (dk == 64 && dv == 64) || (dk == 128 && dv == 128); }
+
+bool valid_dtype(int d) { return d == GDR_BF16 || d == GDR_FP32; }
+
+// Per-device properties, filled once per device.
+struct DeviceProps {
+  bool filled = false;
+  bool gfx950 = false;
+  char arch[64] = "";
+};
+constexpr int kMaxDevices = 64;
+DeviceProps g_props[kMaxDevices];
+std::mutex g_props_mu;
+
+gdr_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(GDR_ERR_UNSUPPORTED, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_props_mu);
+  DeviceProps& p = g_props[dev];
+  if (!p.filled) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDeviceProperties");
+    snprintf(p.arch, sizeof p.arch, "%s", prop.gcnArchName);
+    p.gfx950 = std::string_view(prop.gcnArchName).substr(0, 6) == "gfx950";
+    p.filled = true;
+  }
+  if (!p.gfx950) return fail(GDR_ERR_UNSUPPORTED, "device %d is %s; libgdr is built for gfx950", dev, p.arch);
+  return GDR_OK;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+extern "C" {
+
+const char* gdr_status_string(gdr_status s) {
+  switch (s) {
+    case GDR_OK: return "GDR_OK";
+    case GDR_ERR_INVALID_ARG: return "GDR_ERR_INVALID_ARG";
+    case GDR_ERR_UNSUPPORTED: return "GDR_ERR_UNSUPPORTED";
+    case GDR_ERR_HIP: return "GDR_ERR_HIP";
+  }
+  return "unknown gdr_status";
+}
+
+const char* gdr_last_error(void) { return g_last_error; }
+
+gdr_status gdr_decode_step(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, float* state, void* o, int N, int H, int dk, int dv,
+                           gdr_dtype in_dtype, gdr_dtype out_dtype, gdr_stream_t stream) {
+  if (!q || !k || !v || !g || !beta || !state || !o)
+    return fail(GDR_ERR_INVALID_ARG, "gdr_decode_step: NULL tensor pointer");
+  if (N <= 0 || H <= 0) return fail(GDR_ERR_INVALID_ARG, "gdr_decode_step: N=%d H=%d must be > 0", N, H);
+  if (static_cast<int64_t>(N) * H > INT32_MAX)
+    return fail(GDR_ERR_INVALID_ARG, "gdr_decode_step: N*H too large");
+  if (!supported_dims(dk, dv))
+    return fail(GDR_ERR_UNSUPPORTED, "gdr_decode_step: (dk, dv) = (%d, %d) not in {(64,64), (128,128)}", dk, dv);
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(GDR_ERR_UNSUPPORTED, "gdr_decode_step: dtype codes must be GDR_BF16 or GDR_FP32");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(o) ||
+      !aligned16(g) || !aligned16(beta))
+    return fail(GDR_ERR_INVALID_ARG, "gdr_decode_step: pointers must be 16-byte aligned");
+  gdr_status s = check_device();
+  if (s != GDR_OK) return s;
+  return hip_status(gdr::launch_decode(q, k, v, g, beta, state, o, N * H, dk, dv, in_dtype,
+                                       out_dtype, static_cast<hipStream_t>(stream)),
+                    "gdr_decode_step launch");
+}
+
+int gdr_max_chunks(int T_total, int N, int chunk) {
+  if (T_total < 0 || N <= 0 || chunk <= 0) return -1;
+  const int64_t m = static_cast<int64_t>(T_total) / chunk + N;
+  return m > INT32_MAX ? -1 : static_cast<int>(m);
+}
+
+gdr_status gdr_chunk_layout(const int32_t* cu_seqlens, int N, int chunk, int32_t* chunk_offsets,
+                            int32_t* chunk_indices, int max_chunks, gdr_stream_t stream) {
+  if (!cu_seqlens || !chunk_offsets || (!chunk_indices && max_chunks > 0))
+    return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_layout: NULL pointer");
+  if (N <= 0 || N > 65536) return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_layout: N=%d not in [1, 65536]", N);
+  if (chunk <= 0) return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_layout: chunk=%d must be > 0", chunk);
+  if (max_chunks < 0) return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_layout: max_chunks < 0");
+  gdr_status s = check_device();
+  if (s != GDR_OK) return s;
+  return hip_status(gdr::launch_layout(cu_seqlens, N, chunk, chunk_offsets, chunk_indices,
+                                       max_chunks, static_cast<hipStream_t>(stream)),
+                    "gdr_chunk_layout launch");
+}
+
+size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int dv, int chunk) {
+  const int mc = gdr_max_chunks(T_total, N, chunk);
+  if (mc < 0 || H <= 0 || !supported_dims(dk, dv)) return 0;
+  size_t bytes = align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1));
+  bytes += align_up(sizeof(int32_t) * 2 * static_cast<size_t>(mc));
+  const size_t per = static_cast<size_t>(mc) * H * sizeof(float);
+  bytes += align_up(per * dv * dk);  // L
+  bytes += align_up(per * dk * dk);  // M
+  bytes += align_up(per * dv * dk);  // fixed
+  return bytes;
+}
+
+gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const int32_t* cu_seqlens, int N,
+                             const float* state_in, float* state_out, void* o, float* L_out,
+                             float* M_out, float* fixed_out, int T_total, int H, int dk, int dv,
+                             int chunk, gdr_dtype in_dtype, gdr_dtype out_dtype, void* workspace,
+                             size_t workspace_bytes, gdr_stream_t stream) {
+  if (!cu_seqlens || !state_out) return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: NULL cu_seqlens/state_out");
+  if (T_total > 0 && (!q || !k || !v || !g || !beta || !o))
+    return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: NULL tensor pointer");
+  if (T_total < 0 || N <= 0 || H <= 0)
+    return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: T_total=%d N=%d H=%d", T_total, N, H);
+  if (N > 65536 || H > 65535) return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: N or H too large");
+  if (!supported_dims(dk, dv))
+    return fail(GDR_ERR_UNSUPPORTED, "gdr_chunk_prefill: (dk, dv) = (%d, %d) not in {(64,64), (128,128)}", dk, dv);
+  if (chunk != 16 && chunk != 64)
+    return fail(GDR_ERR_UNSUPPORTED, "gdr_chunk_prefill: chunk=%d not in {16, 64}", chunk);
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(GDR_ERR_UNSUPPORTED, "gdr_chunk_prefill: dtype codes must be GDR_BF16 or GDR_FP32");
+  if (in_dtype == GDR_FP32 && chunk != 16)
+    return fail(GDR_ERR_UNSUPPORTED, "gdr_chunk_prefill: fp32 inputs need chunk=16");
+  const void* ptrs[] = {q, k, v, g, beta, state_in, state_out, o, L_out, M_out, fixed_out, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: pointers must be 16-byte aligned");
+  const int mc = gdr_max_chunks(T_total, N, chunk);
+  if (mc < 0) return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: too many chunks");
+  if (static_cast<int64_t>(T_total) * H > INT32_MAX || static_cast<int64_t>(mc) * H > INT32_MAX)
+    return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: T_total*H too large");
+
+  // workspace carve-up: offsets | indices | [L] | [M] | [fixed]
+  const size_t per = static_cast<size_t>(mc) * H * sizeof(float);
+  size_t need = align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1)) +
+                align_up(sizeof(int32_t) * 2 * static_cast<size_t>(mc));
+  if (!L_out) need += align_up(per * dv * dk);
+  if (!M_out) need += align_up(per * dk * dk);
+  if (!fixed_out) need += align_up(per * dv * dk);
+  if (workspace_bytes < need || (!workspace && need > 0))
+    return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: workspace of %zu bytes, need %zu", workspace_bytes, need);
+  gdr_status s = check_device();
+  if (s != GDR_OK) return s;
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* offs = reinterpret_cast<int32_t*>(ws);
+  ws += align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1));
+  int32_t* cidx = reinterpret_cast<int32_t*>(ws);
+  ws += align_up(sizeof(int32_t) * 2 * static_cast<size_t>(mc));
+  float* L = L_out;
+  if (!L) { L = reinterpret_cast<float*>(ws); ws += align_up(per * dv * dk); }
+  float* M = M_out;
+  if (!M) { M = reinterpret_cast<float*>(ws); ws += align_up(per * dk * dk); }
+  float* fixed = fixed_out;
+  if (!fixed) { fixed = reinterpret_cast<float*>(ws); ws += align_up(per * dv * dk); }
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = gdr::launch_layout(cu_seqlens, N, chunk, offs, cidx, mc, st);
+  if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: layout");
+  if (T_total > 0) {
+    e = gdr::launch_chunk_local(k, v, g, beta, cu_seqlens, cidx, L, M, mc, T_total, H, dk, dv,
+                                chunk, in_dtype, st);
+    if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: chunk_local");
+    e = gdr::launch_fixup(L, M, state_in, offs, N, fixed, mc, H, dk, dv, st);
+    if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: fixup");
+    e = gdr::launch_chunk_out(q, k, v, g, beta, cu_seqlens, cidx, state_in, fixed, o, mc, T_total,
+                              H, dk, dv, chunk, in_dtype, out_dtype, st);
+    if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: chunk_out");
+  }
+  e = gdr::launch_final_state(state_in, fixed, offs, N, H, dk, dv, mc, state_out, st);
+  return hip_status(e, "gdr_chunk_prefill: final state");
+}
+
+gdr_status gdr_state_fixup(const float* L, const float* M, const float* state_in,
+                           const int32_t* chunk_offsets, int N, float* fixed, int n_chunks, int H,
+                           int dk, int dv, gdr_stream_t stream) {
+  if (!L || !M || !chunk_offsets || !fixed)
+    return fail(GDR_ERR_INVALID_ARG, "gdr_state_fixup: NULL pointer");
+  if (N <= 0 || N > 65536 || H <= 0 || H > 65535 || n_chunks < 0)
+    return fail(GDR_ERR_INVALID_ARG, "gdr_state_fixup: N=%d H=%d n_chunks=%d", N, H, n_chunks);
+  if (!supported_dims(dk, dv))
+    return fail(GDR_ERR_UNSUPPORTED, "gdr_state_fixup: (dk, dv) = (%d, %d) not in {(64,64), (128,128)}", dk, dv);
+  if (!aligned16(L) || !aligned16(M) || !aligned16(fixed) || (state_in && !aligned16(state_in)))
+    return fail(GDR_ERR_INVALID_ARG, "gdr_state_fixup: pointers must be 16-byte aligned");
+  gdr_status s = check_device();
+  if (s != GDR_OK) return s;
+  if (n_chunks == 0) return ok();
+  return hip_status(gdr::launch_fixup(L, M, state_in, chunk_offsets, N, fixed, n_chunks, H, dk,
+                                      dv, static_cast<hipStream_t>(stream)),
+                    "gdr_state_fixup launch");
+}
+
+}  // extern "C"

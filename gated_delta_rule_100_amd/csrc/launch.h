@@ -1,0 +1,47 @@
+// launch.h -- host-side launchers of the gfx950 kernels (internal to libgdr).
+// Every launcher assumes its arguments were validated by the C ABI layer and
+// returns the HIP status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdr {
+
+// One decode token for NH = N*H states, in place.
+hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, float* state, void* o, int NH, int dk, int dv,
+                         int in_dtype, int out_dtype, hipStream_t stream);
+
+// Varlen layout: chunk_offsets [N+1], chunk_indices [max_chunks, 2].
+hipError_t launch_layout(const int32_t* cu_seqlens, int N, int chunk, int32_t* chunk_offsets,
+                         int32_t* chunk_indices, int max_chunks, hipStream_t stream);
+
+// Inter-chunk fixup: fixed[c] = fixed[c-1] M_c + L_c per (sequence, head).
+hipError_t launch_fixup(const float* L, const float* M, const float* state_in,
+                        const int32_t* chunk_offsets, int N, float* fixed, int n_chunks, int H,
+                        int dk, int dv, hipStream_t stream);
+
+// Chunk-local precompute: L_c and M_c for every chunk slot < max_chunks.
+hipError_t launch_chunk_local(const void* k, const void* v, const float* g, const float* beta,
+                              const int32_t* cu_seqlens, const int32_t* chunk_indices,
+                              float* L, float* M, int max_chunks, int T_total, int H, int dk,
+                              int dv, int chunk, int in_dtype, hipStream_t stream);
+
+// Chunk outputs from the fixed states (start state of chunk j of sequence n is
+// fixed[c-1] for j > 0 and state_in[n] (or zero) for j = 0).
+hipError_t launch_chunk_out(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const int32_t* cu_seqlens,
+                            const int32_t* chunk_indices, const float* state_in,
+                            const float* fixed, void* o, int max_chunks, int T_total, int H,
+                            int dk, int dv, int chunk, int in_dtype, int out_dtype,
+                            hipStream_t stream);
+
+// Final states: state_out[n] = fixed[last chunk of n], or state_in[n] (zero
+// without one) for an empty sequence.
+hipError_t launch_final_state(const float* state_in, const float* fixed,
+                              const int32_t* chunk_offsets, int N, int H, int dk, int dv,
+                              int n_chunks, float* state_out, hipStream_t stream);
+
+}  // namespace gdr

@@ -1,0 +1,120 @@
+// mfma_planes.h -- bf16 "plane" arithmetic on gfx950 matrix cores.
+//
+// The dense contractions of the chunked form run on v_mfma_f32_16x16x32_bf16
+// (16x16 output tile, 32-deep contraction, fp32 accumulate).  An fp32 operand
+// x is carried as P bf16 planes x = p0 + p1 + ... (p0 = RNE(x), p1 = RNE(x - p0),
+// ...): two planes keep ~16 significant bits, three keep all 24.  A product
+// of a PA-plane and a PB-plane operand issues the plane pairs (i, j) with
+// i + j < max(PA, PB), smallest terms first; the dropped pairs are below the
+// kept precision.  Operands that are exactly bf16 (the bf16 inputs q, k, v)
+// use one plane.
+//
+// Lane layout of the 16x16x32 instruction (wave64; c = lane % 16, g = lane / 16):
+//   A fragment: A[c][8g .. 8g+7]        (row c of the 16-row tile)
+//   B fragment: B[8g .. 8g+7][c]        (column c), i.e. row c of B^T
+//   D tile:     D[4g + e][c], e = 0..3  (floatx4 per lane)
+// The contraction index only has to agree between A and B; when an operand
+// comes straight from a D tile (rows 4g+e of two stacked 16-row tiles), the
+// other operand is read with the matching slot order (see load_*_perm).
+#pragma once
+
+#include "gdr_device.h"
+
+namespace gdr {
+
+typedef unsigned short ushort8 __attribute__((ext_vector_type(8)));
+typedef unsigned short ushort4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4 mfma16x16x32(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int PA, int PB>
+__device__ __forceinline__ void mma_planes(floatx4& acc, const bf16x8 (&a)[PA],
+                                           const bf16x8 (&b)[PB]) {
+  constexpr int PM = PA > PB ? PA : PB;
+#pragma unroll
+  for (int s = PM - 1; s >= 0; --s) {
+#pragma unroll
+    for (int i = 0; i < PA; ++i) {
+      const int j = s - i;
+      if (j >= 0 && j < PB) acc = mfma16x16x32(a[i], b[j], acc);
+    }
+  }
+}
+
+// Split one fp32 value into P bf16 planes (bit patterns).
+template <int P>
+__device__ __forceinline__ void split_planes(float x, uint16_t (&out)[P]) {
+  float r = x;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    out[p] = f32_to_bf16_bits(r);
+    r = r - bf16_bits_to_f32(out[p]);
+  }
+}
+
+// Split 8 fp32 values into P bf16x8 fragments.
+template <int P>
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 (&out)[P]) {
+  ushort8 w[P];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    uint16_t s[P];
+    split_planes<P>(x[e], s);
+#pragma unroll
+    for (int p = 0; p < P; ++p) w[p][e] = s[p];
+  }
+#pragma unroll
+  for (int p = 0; p < P; ++p) out[p] = __builtin_bit_cast(bf16x8, w[p]);
+}
+
+// 8 consecutive bf16 of each plane from LDS (16-byte aligned).
+template <int P>
+__device__ __forceinline__ void load_lds8(const uint16_t* base, int plane_stride,
+                                          bf16x8 (&out)[P]) {
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    out[p] = *reinterpret_cast<const bf16x8*>(base + p * plane_stride);
+}
+
+// Slot-permuted read: elements [0..3] and [16..19] from `base` (8-byte
+// aligned), matching a D-tile operand made of two stacked 16-row tiles.
+template <int P>
+__device__ __forceinline__ void load_lds8_perm(const uint16_t* base, int plane_stride,
+                                               bf16x8 (&out)[P]) {
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const ushort4 lo = *reinterpret_cast<const ushort4*>(base + p * plane_stride);
+    const ushort4 hi = *reinterpret_cast<const ushort4*>(base + p * plane_stride + 16);
+    const ushort8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    out[p] = __builtin_bit_cast(bf16x8, w);
+  }
+}
+
+// 8 consecutive input elements from global memory as P planes (zeros when
+// !valid).  bf16 inputs are exact in one plane; fp32 inputs are split.
+template <Dt IN, int P>
+__device__ __forceinline__ void load_global8(const void* base, size_t idx, bool valid,
+                                             bf16x8 (&out)[P]) {
+  if constexpr (IN == Dt::BF16) {
+    static_assert(P == 1, "bf16 inputs use one plane");
+    uint4 w = valid ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx)
+                    : make_uint4(0, 0, 0, 0);
+    out[0] = __builtin_bit_cast(bf16x8, w);
+  } else {
+    float x[8];
+    if (valid) {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+      const float4 a = p[0], b = p[1];
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+      x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+    split8<P>(x, out);
+  }
+}
+
+}  // namespace gdr

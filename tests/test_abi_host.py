@@ -1,0 +1,115 @@
+"""Host-side checks of libgdr that need no GPU: the library loads, exports
+every entry point that include/gdr.h declares, and rejects invalid arguments
+before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**(gdr_[a-z_0-9]+)\s*\(",
+                                 text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import gated_delta_rule_100_amd as g
+    if not os.path.exists(g.library_path()):
+        from gated_delta_rule_100_amd.build import build_library
+        build_library()
+    return g._load()
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for name in ("gdr_decode_step", "gdr_chunk_prefill", "gdr_state_fixup", "gdr_chunk_layout",
+                 "gdr_max_chunks", "gdr_chunk_prefill_workspace_bytes", "gdr_status_string",
+                 "gdr_last_error"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_no_oracle_in_product_library(lib):
+    import gated_delta_rule_100_amd as g
+    text = open(os.path.join(os.path.dirname(g.__file__), "__init__.py")).read()
+    assert "oracle" not in text.replace("no CPU path", "")
+    for name in ("oracle_recurrent",):
+        assert not hasattr(lib, name)
+
+
+def test_max_chunks_and_workspace(lib):
+    import gated_delta_rule_100_amd as g
+    assert g.gdr_max_chunks(131072, 1, 64) == 2049
+    assert g.gdr_max_chunks(0, 3, 16) == 3
+    assert g.gdr_max_chunks(-1, 1, 64) == -1
+    assert g.gdr_max_chunks(10, 0, 64) == -1
+    mc = g.gdr_max_chunks(16384, 4, 64)
+    ws = g.gdr_chunk_prefill_workspace_bytes(16384, 4, 16, 128, 128, 64)
+    assert ws >= mc * 16 * 128 * 128 * 4 * 3
+    assert g.gdr_chunk_prefill_workspace_bytes(16384, 4, 16, 96, 96, 64) == 0
+
+
+def _p(x):
+    return ctypes.c_void_p(x)
+
+
+def test_decode_rejects_bad_arguments(lib):
+    fake = 0x10000  # never dereferenced: validation fails first
+    args = [_p(fake)] * 7
+    assert lib.gdr_decode_step(*([None] + args[1:]), 2, 2, 128, 128, 0, 0, None) == 1
+    assert "NULL" in lib.gdr_last_error().decode()
+    assert lib.gdr_decode_step(*args, 0, 2, 128, 128, 0, 0, None) == 1
+    assert lib.gdr_decode_step(*args, 2, 2, 96, 96, 0, 0, None) == 2
+    assert lib.gdr_decode_step(*args, 2, 2, 128, 64, 0, 0, None) == 2
+    assert lib.gdr_decode_step(*args, 2, 2, 128, 128, 5, 0, None) == 2
+    bad = list(args)
+    bad[5] = _p(fake + 4)
+    assert lib.gdr_decode_step(*bad, 2, 2, 128, 128, 0, 0, None) == 1
+    assert "aligned" in lib.gdr_last_error().decode()
+
+
+def test_prefill_and_fixup_reject_bad_arguments(lib):
+    f = _p(0x10000)
+    base = dict(q=f, k=f, v=f, g=f, beta=f, cu=f, N=2, sin=None, sout=f, o=f, L=None, M=None,
+                fx=None, T=128, H=4, dk=128, dv=128, chunk=64, ind=0, outd=0, ws=f, wsb=1 << 40)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return lib.gdr_chunk_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"],
+                                     a["sin"], a["sout"], a["o"], a["L"], a["M"], a["fx"], a["T"],
+                                     a["H"], a["dk"], a["dv"], a["chunk"], a["ind"], a["outd"],
+                                     a["ws"], a["wsb"], None)
+
+    assert call(cu=None) == 1
+    assert call(chunk=32) == 2
+    assert call(dk=64, dv=128) == 2
+    assert call(ind=1, chunk=64) == 2       # fp32 inputs need chunk 16
+    assert call(T=-1) == 1
+    assert call(wsb=16) == 1
+    assert "workspace" in lib.gdr_last_error().decode()
+    assert call(o=_p(0x10002)) == 1
+    assert lib.gdr_state_fixup(None, f, None, f, 1, f, 4, 1, 128, 128, None) == 1
+    assert lib.gdr_state_fixup(f, f, None, f, 1, f, 4, 1, 64, 128, None) == 2
+    assert lib.gdr_chunk_layout(None, 1, 64, f, f, 4, None) == 1
+    assert lib.gdr_chunk_layout(f, 0, 64, f, f, 4, None) == 1
+    assert lib.gdr_status_string(2) == b"GDR_ERR_UNSUPPORTED"
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    import gated_delta_rule_100_amd as g
+    q = torch.zeros(2, 2, 64, dtype=torch.float32)
+    with pytest.raises(g.GdrError):
+        g.gdr_decode_step(q, q, q, torch.zeros(2, 2), torch.zeros(2, 2),
+                          torch.zeros(2, 2, 64, 64), torch.zeros(2, 2, 64))
