@@ -76,6 +76,41 @@ gdr_status check_device() {
 
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Segment size (in chunks) of the two-level fixup, or 0 for the single-level
+// scan.  Two levels pay off when sequences are long and there are too few
+// (sequence, head) pairs to fill the GPU: a chain of n chunks becomes about
+// 2*seg + n/seg dependent steps for three times the work.  Only host-side
+// sizes are known here, so the average sequence length decides.
+int fixup_segment(int T_total, int N, int H, int chunk) {
+  const int64_t avg_chunks = (static_cast<int64_t>(T_total) + static_cast<int64_t>(N) * chunk - 1) /
+                             (static_cast<int64_t>(N) * chunk);
+  if (avg_chunks < 256 || static_cast<int64_t>(N) * H > 64) return 0;
+  int seg = 16;
+  while (seg < 64 && static_cast<int64_t>(seg) * seg * 4 <= avg_chunks) seg *= 2;
+  return seg;
+}
+
+struct SegSizes {
+  int seg = 0, max_segs = 0;
+  size_t state_bytes = 0;  // bytes of one [max_segs, H, d, d] fp32 buffer
+};
+
+SegSizes seg_sizes(int T_total, int N, int H, int d, int chunk, int max_chunks) {
+  SegSizes z;
+  z.seg = fixup_segment(T_total, N, H, chunk);
+  if (z.seg > 0) {
+    z.max_segs = max_chunks / z.seg + N;
+    z.state_bytes = static_cast<size_t>(z.max_segs) * H * d * d * sizeof(float);
+  }
+  return z;
+}
+
+size_t seg_workspace(const SegSizes& z, int N) {
+  if (z.seg == 0) return 0;
+  return align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1)) +
+         align_up(sizeof(int32_t) * 2 * static_cast<size_t>(z.max_segs)) + 3 * align_up(z.state_bytes);
+}
+
 }  // namespace
 
 extern "C" {
@@ -143,6 +178,7 @@ size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int 
   bytes += align_up(per * dv * dk);  // L
   bytes += align_up(per * dk * dk);  // M
   bytes += align_up(per * dv * dk);  // fixed
+  bytes += seg_workspace(seg_sizes(T_total, N, H, dk, chunk, mc), N);
   return bytes;
 }
 
@@ -181,6 +217,8 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
   if (!L_out) need += align_up(per * dv * dk);
   if (!M_out) need += align_up(per * dk * dk);
   if (!fixed_out) need += align_up(per * dv * dk);
+  const SegSizes segz = seg_sizes(T_total, N, H, dk, chunk, mc);
+  need += seg_workspace(segz, N);
   if (workspace_bytes < need || (!workspace && need > 0))
     return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: workspace of %zu bytes, need %zu", workspace_bytes, need);
   gdr_status s = check_device();
@@ -197,6 +235,21 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
   if (!M) { M = reinterpret_cast<float*>(ws); ws += align_up(per * dk * dk); }
   float* fixed = fixed_out;
   if (!fixed) { fixed = reinterpret_cast<float*>(ws); ws += align_up(per * dv * dk); }
+  int32_t* seg_offs = nullptr;
+  int32_t* seg_idx = nullptr;
+  float *seg_L = nullptr, *seg_Mt = nullptr, *seg_fixed = nullptr;
+  if (segz.seg > 0) {
+    seg_offs = reinterpret_cast<int32_t*>(ws);
+    ws += align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1));
+    seg_idx = reinterpret_cast<int32_t*>(ws);
+    ws += align_up(sizeof(int32_t) * 2 * static_cast<size_t>(segz.max_segs));
+    seg_L = reinterpret_cast<float*>(ws);
+    ws += align_up(segz.state_bytes);
+    seg_Mt = reinterpret_cast<float*>(ws);
+    ws += align_up(segz.state_bytes);
+    seg_fixed = reinterpret_cast<float*>(ws);
+    ws += align_up(segz.state_bytes);
+  }
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = gdr::launch_layout(cu_seqlens, N, chunk, offs, cidx, mc, st);
@@ -205,8 +258,24 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
     e = gdr::launch_chunk_local(k, v, g, beta, cu_seqlens, cidx, L, M, mc, T_total, H, dk, dv,
                                 chunk, in_dtype, st);
     if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: chunk_local");
-    e = gdr::launch_fixup(L, M, state_in, offs, N, fixed, mc, H, dk, dv, st);
-    if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: fixup");
+    const int planes = in_dtype == GDR_BF16 ? 2 : 3;
+    if (segz.seg == 0) {
+      e = gdr::launch_fixup(L, M, state_in, offs, N, fixed, mc, H, dk, dv, planes, st);
+      if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: fixup");
+    } else {
+      // two-level scan: segments of segz.seg chunks
+      e = gdr::launch_layout(offs, N, segz.seg, seg_offs, seg_idx, segz.max_segs, st);
+      if (e == hipSuccess)
+        e = gdr::launch_fixup_mode(1, L, M, nullptr, offs, seg_idx, segz.seg, nullptr, seg_L,
+                                   seg_Mt, mc, H, segz.max_segs, dk, planes, st);
+      if (e == hipSuccess)
+        e = gdr::launch_fixup_mode(0, seg_L, seg_Mt, state_in, seg_offs, nullptr, 0, nullptr,
+                                   seg_fixed, nullptr, segz.max_segs, H, N, dk, planes, st);
+      if (e == hipSuccess)
+        e = gdr::launch_fixup_mode(2, L, M, state_in, offs, seg_idx, segz.seg, seg_fixed, fixed,
+                                   nullptr, mc, H, segz.max_segs, dk, planes, st);
+      if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: segmented fixup");
+    }
     e = gdr::launch_chunk_out(q, k, v, g, beta, cu_seqlens, cidx, state_in, fixed, o, mc, T_total,
                               H, dk, dv, chunk, in_dtype, out_dtype, st);
     if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: chunk_out");
@@ -230,7 +299,7 @@ gdr_status gdr_state_fixup(const float* L, const float* M, const float* state_in
   if (s != GDR_OK) return s;
   if (n_chunks == 0) return ok();
   return hip_status(gdr::launch_fixup(L, M, state_in, chunk_offsets, N, fixed, n_chunks, H, dk,
-                                      dv, static_cast<hipStream_t>(stream)),
+                                      dv, 3, static_cast<hipStream_t>(stream)),
                     "gdr_state_fixup launch");
 }
 

@@ -5,69 +5,77 @@
 // c <= C tokens starting from state S0 (dv x dk):
 //   G_t = sum_{s<=t} g_s,  gamma_t = exp(G_t),  Gamma_ts = exp(G_t - G_s) (s <= t),
 //   D_s = exp(G_C - G_s)                         (every exponent <= 0)
-//   A_ts = beta_t Gamma_ts (k_t . k_s)  (s < t),  T = (I + A)^{-1}
-//   W = T diag(beta gamma) K,  Ut = T diag(beta) V
-//   L = Ut^T diag(D) K,  M = gamma_C I - W^T diag(D) K    (S_end = S0 M + L)
-//   U = Ut - W S0^T,  O = diag(gamma) Q S0^T + (Q K^T (.) Gamma) U
+//   A_ts = beta_t Gamma_ts (k_t . k_s)  (s < t)
+//   (I + A) W = diag(beta gamma) K,   (I + A) Ut = diag(beta) V
+//   L = Ut^T diag(D) K,   M = gamma_C I - W^T diag(D) K      (S_end = S0 M + L)
+//   U = Ut - W S0^T,   O = diag(gamma) Q S0^T + (Q K^T (.) Gamma) U
 // This is the recurrence S_t = alpha_t S_{t-1}(I - beta_t k_t k_t^T) + beta_t v_t k_t^T
-// re-associated over a chunk (u_t = beta_t (v_t - alpha_t S_{t-1} k_t) obeys
-// (I + A) U = diag(beta) V - diag(beta gamma) K S0^T).  The chunk-parallel
-// split into local states, transfer matrices and a fixup follows the
-// FlashInfer PR #3866 page ("CP delta-rule precompute optimisation for ultra-
-// low parallelism"); the intra-chunk algebra is derived from the recurrence.
+// re-associated over a chunk: u_t = beta_t (v_t - alpha_t S_{t-1} k_t) obeys
+// (I + A) U = diag(beta) V - diag(beta gamma) K S0^T.  The chunk-parallel split
+// into local states, transfer matrices and a fixup follows the FlashInfer
+// PR #3866 page ("CP delta-rule precompute optimisation for ultra-low
+// parallelism"); the intra-chunk algebra is derived from the recurrence.
+//
+// The unit lower triangular systems are solved by block forward substitution
+// over 16-row blocks: the diagonal blocks are inverted by substitution (one
+// wave each, fp32), then every wave runs X_i = T_ii (B_i - sum_{j<i} A_ij X_j)
+// for its own feature columns on the matrix cores.  X_j comes out of one
+// 16x16x16 product in exactly the layout the next product takes as its B
+// operand, so the whole solve stays in registers; only A and the T_ii are
+// read from LDS.
 //
 // Padding: positions t >= c get g = 0, beta = 0 and zero k, v, q, which makes
 // them identity steps (no effect on L, M) -- masking in the kernel instead of
 // padded copies on the host (the out-of-bounds-fill idea on the FlashInfer
 // PR #6291 page, "Mamba-2 SSD optimisation, round 4", code analysis 3).
 //
-// Matrix products run on v_mfma_f32_16x16x32_bf16 with fp32 operands split
-// into bf16 planes (mfma_planes.h).  LDS holds K^T and V^T (chunk index
-// contiguous), A/T in fp32, T diag(beta gamma) and T diag(beta) as planes,
-// and, for the outputs, the masked decay-weighted Q K^T and W.  Outputs of
-// one product that feed the next stay in registers: the W/Ut tiles of a wave
-// are the A operand of L and M, and the U tiles the B operand of P U.
+// Products run on v_mfma_f32_16x16x{16,32}_bf16 with fp32 operands split into
+// bf16 planes (mfma_planes.h).  M is written transposed (row b of slot c holds
+// column b of M_c), which is the layout the fixup scan loads with 16-byte
+// reads.
 #include "launch.h"
 #include "mfma_planes.h"
 
 namespace gdr {
 namespace {
 
-template <int D, int C, Dt IN>
+template <int D, int C, Dt IN, bool OUT>
 struct ChunkCfg {
   static constexpr int Cp = C < 32 ? 32 : C;              // contraction extent over the chunk
   static constexpr int PI = IN == Dt::BF16 ? 1 : 3;       // planes of q, k, v
   static constexpr int PT = IN == Dt::BF16 ? 2 : 3;       // planes of fp32 intermediates
-  static constexpr int NT = C / 16;                       // 16-row tiles along the chunk
+  static constexpr int NT = C / 16;                       // 16-row blocks along the chunk
   static constexpr int ND = D / 16;                       // 16-wide tiles along features
   static constexpr int DPW = ND / 4;                      // feature tiles per wave
   static constexpr int KB = D / 32;                       // 32-deep blocks along features
   static constexpr int CB = Cp / 32;                      // 32-deep blocks along the chunk
-  static constexpr int LDC = Cp + 8;                      // row stride of chunk-indexed planes
-  static constexpr int LDD = D + 8;                       // row stride of W planes
-  static constexpr int LDA = C + 1;                       // row stride of fp32 A / T
-  static constexpr int KT_PS = D * LDC;                   // plane stride of K^T, V^T
-  static constexpr int TT_PS = C * LDC;                   // plane stride of T', T'', P
-  static constexpr int W_PS = C * LDD;                    // plane stride of W
-  static constexpr int KT_BYTES = PI * KT_PS * 2;
-  static constexpr int AF_BYTES = C * LDA * 4;
-  static constexpr int TT_BYTES = PT * TT_PS * 2;
-  static constexpr int RA_BYTES = ((AF_BYTES > TT_BYTES ? AF_BYTES : TT_BYTES) + 15) / 16 * 16;
-  static constexpr int W_BYTES = PT * W_PS * 2;
-  static constexpr int RAT_BYTES = 2 * RA_BYTES > W_BYTES ? 2 * RA_BYTES : (W_BYTES + 15) / 16 * 16;
-  static constexpr int GATE_BYTES = 5 * C * 4;
-  static constexpr int X_BYTES = NT > 1 ? 4 * 256 * 4 : 16;
-  // layout: Kt | Vt | RA (A, then T') | RT (T, then T'') [W overlays RA+RT] | P | gates | X
+  static constexpr int NOFF = NT * (NT - 1) / 2;          // strictly lower 16x16 blocks
+  static constexpr int LDC = Cp + 4;                      // row stride of K^T, V^T (8-byte reads)
+  static constexpr int LDP = Cp + 8;                      // row stride of P planes
+  static constexpr int LDD = D + 8;                       // row stride of W planes (16-byte reads)
+  static constexpr int LDB = 24;                          // row stride of 16x16 block planes
+  static constexpr int KT_PS = D * LDC;
+  static constexpr int P_PS = C * LDP;
+  static constexpr int W_PS = C * LDD;
+  static constexpr int BLK_PS = 16 * LDB;
+  static constexpr int r16(int x) { return (x + 15) / 16 * 16; }
+  static constexpr int mx(int a, int b) { return a > b ? a : b; }
+  static constexpr int KT_BYTES = r16(PI * KT_PS * 2);
+  static constexpr int KV_BYTES = 2 * KT_BYTES;
+  static constexpr int W_BYTES = r16(PT * W_PS * 2);
+  static constexpr int KVW_BYTES = OUT ? mx(KV_BYTES, W_BYTES) : KV_BYTES;
+  static constexpr int AOFF_BYTES = r16(mx(NOFF, 1) * PT * BLK_PS * 2);
+  static constexpr int DIAG_BLK = r16(mx(16 * 17 * 4, PT * BLK_PS * 2));  // A_ii fp32, then T_ii planes
+  static constexpr int P_BYTES = OUT ? r16(PT * P_PS * 2) : 0;
+  static constexpr int GATE_BYTES = 6 * C * 4;
   static constexpr int OFF_KT = 0;
-  static constexpr int OFF_VT = OFF_KT + KT_BYTES;
-  static constexpr int OFF_RA = OFF_VT + KT_BYTES;
-  static constexpr int OFF_RT = OFF_RA + RA_BYTES;
-  static constexpr int OFF_P = OFF_RA + RAT_BYTES;
-  static constexpr int OFF_GATE_LOCAL = OFF_P;  // chunk_local has no P
-  static constexpr int LOCAL_BYTES = OFF_GATE_LOCAL + GATE_BYTES + X_BYTES;
-  static constexpr int OFF_GATE_OUT = OFF_P + TT_BYTES;
-  static constexpr int OUT_BYTES = OFF_GATE_OUT + GATE_BYTES + X_BYTES;
-  static_assert(KT_BYTES % 16 == 0 && TT_BYTES % 16 == 0, "alignment");
+  static constexpr int OFF_VT = KT_BYTES;
+  static constexpr int OFF_W = 0;                         // W planes overlay K^T/V^T (outputs)
+  static constexpr int OFF_AOFF = KVW_BYTES;
+  static constexpr int OFF_DIAG = OFF_AOFF + AOFF_BYTES;
+  static constexpr int OFF_P = OFF_DIAG + NT * DIAG_BLK;
+  static constexpr int OFF_GATE = OFF_P + P_BYTES;
+  static constexpr int BYTES = OFF_GATE + GATE_BYTES;
   static_assert(D % 64 == 0 && (C == 16 || C == 64), "shape");
 };
 
@@ -93,27 +101,31 @@ __device__ __forceinline__ ChunkTokens chunk_tokens(const int32_t* cu, const int
   return r;
 }
 
-template <int D, int C, Dt IN>
+template <int D, int C, Dt IN, bool OUT>
 struct ChunkWork {
-  using Cfg = ChunkCfg<D, C, IN>;
-  static constexpr int PI = Cfg::PI, PT = Cfg::PT, NT = Cfg::NT, DPW = Cfg::DPW;
+  using Cfg = ChunkCfg<D, C, IN, OUT>;
+  static constexpr int PI = Cfg::PI, PT = Cfg::PT, NT = Cfg::NT, DPW = Cfg::DPW, KB = Cfg::KB;
 
   unsigned char* smem;
   int tok0, c, h, H;
   int tid, wave, c16, g4;
+  float *sg, *sb, *sG, *sgam, *sD, *sbg;
 
   __device__ uint16_t* Kt() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_KT); }
   __device__ uint16_t* Vt() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_VT); }
-  __device__ float* Af() const { return reinterpret_cast<float*>(smem + Cfg::OFF_RA); }
-  __device__ float* Tf() const { return reinterpret_cast<float*>(smem + Cfg::OFF_RT); }
-  __device__ uint16_t* Tp() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_RA); }
-  __device__ uint16_t* Tpp() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_RT); }
-  __device__ uint16_t* Wp() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_RA); }
+  __device__ uint16_t* Wp() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_W); }
+  __device__ uint16_t* Aoff(int blk) const {
+    return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_AOFF) + blk * PT * Cfg::BLK_PS;
+  }
+  __device__ float* Adiag(int i) const {
+    return reinterpret_cast<float*>(smem + Cfg::OFF_DIAG + i * Cfg::DIAG_BLK);
+  }
+  __device__ uint16_t* Tdiag(int i) const {
+    return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_DIAG + i * Cfg::DIAG_BLK);
+  }
   __device__ uint16_t* Pp() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_P); }
 
-  float *sg, *sb, *sG, *sgam, *sD, *X;
-
-  __device__ void init(unsigned char* s, int gate_off, int tok0_, int c_, int h_, int H_) {
+  __device__ void init(unsigned char* s, int tok0_, int c_, int h_, int H_) {
     smem = s;
     tok0 = tok0_;
     c = c_;
@@ -123,48 +135,83 @@ struct ChunkWork {
     wave = tid >> 6;
     c16 = tid & 15;
     g4 = (tid & 63) >> 4;
-    float* gate = reinterpret_cast<float*>(s + gate_off);
+    float* gate = reinterpret_cast<float*>(s + Cfg::OFF_GATE);
     sg = gate;
     sb = gate + C;
     sG = gate + 2 * C;
     sgam = gate + 3 * C;
     sD = gate + 4 * C;
-    X = gate + 5 * C;
+    sbg = gate + 5 * C;
   }
 
   __device__ size_t tok_off(int t) const { return (static_cast<size_t>(tok0 + t) * H + h) * D; }
 
-  // K^T, V^T planes (chunk index contiguous, zero for t >= c and t >= C),
-  // gates and their prefix quantities.
+  // Row fragments (8 consecutive features of one token row) of every chunk
+  // row, for the Gram products; zeros past the chunk.
+  __device__ void rows_frags(const void* base, bf16x8 (&f)[NT][KB][PI]) const {
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti) {
+      const int t = 16 * ti + c16;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        load_global8<IN, PI>(base, t < c ? tok_off(t) + 32 * kb + 8 * g4 : 0, t < c, f[ti][kb]);
+    }
+  }
+
+  // K^T and V^T planes (chunk index contiguous, zero for t >= c), gates and
+  // their prefix quantities.  Every global load is issued before the first
+  // LDS write; bf16 inputs are stored bit for bit.
   __device__ void load(const void* k, const void* v, const float* g, const float* beta) {
     constexpr int G8 = D / 8;
-    for (int idx = tid; idx < Cfg::Cp * G8; idx += 256) {
-      const int t = idx / G8;
-      const int d0 = (idx % G8) * 8;
-      float xk[8], xv[8];
-      if (t < c) {
-        load_vec<IN, 8>(k, tok_off(t) + d0, xk);
-        load_vec<IN, 8>(v, tok_off(t) + d0, xv);
-      } else {
+    constexpr int ITER = Cfg::Cp * G8 / 256;
+    static_assert(Cfg::Cp * G8 % 256 == 0, "load tiling");
+    constexpr int NW = IN == Dt::BF16 ? 1 : 2;  // 16-byte words per 8 elements
+    constexpr int ESZ = IN == Dt::BF16 ? 2 : 4;
+    uint4 rk[ITER][NW], rv[ITER][NW];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xk[e] = xv[e] = 0.f;
+    for (int it = 0; it < ITER; ++it) {
+      const int idx = tid + 256 * it;
+      const int t = idx / G8, d0 = (idx % G8) * 8;
+      const bool ok = t < c;
+      const size_t off = ok ? tok_off(t) + d0 : 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        rk[it][w] = ok ? reinterpret_cast<const uint4*>(static_cast<const char*>(k) + off * ESZ)[w]
+                       : make_uint4(0, 0, 0, 0);
+        rv[it][w] = ok ? reinterpret_cast<const uint4*>(static_cast<const char*>(v) + off * ESZ)[w]
+                       : make_uint4(0, 0, 0, 0);
       }
+    }
+    float gv = 0.f, bv = 0.f;
+    if (tid < c && tid < C) {
+      gv = g[static_cast<size_t>(tok0 + tid) * H + h];
+      bv = beta[static_cast<size_t>(tok0 + tid) * H + h];
+    }
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int idx = tid + 256 * it;
+      const int t = idx / G8, d0 = (idx % G8) * 8;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        uint16_t sk[PI], sv[PI];
-        split_planes<PI>(xk[e], sk);
-        split_planes<PI>(xv[e], sv);
+        if constexpr (IN == Dt::BF16) {
+          const uint32_t wk = (&rk[it][0].x)[e / 2], wv = (&rv[it][0].x)[e / 2];
+          Kt()[(d0 + e) * Cfg::LDC + t] = static_cast<uint16_t>((e & 1) ? (wk >> 16) : wk);
+          Vt()[(d0 + e) * Cfg::LDC + t] = static_cast<uint16_t>((e & 1) ? (wv >> 16) : wv);
+        } else {
+          uint16_t sk[PI], sv[PI];
+          split_planes<PI>(__uint_as_float((&rk[it][e / 4].x)[e % 4]), sk);
+          split_planes<PI>(__uint_as_float((&rv[it][e / 4].x)[e % 4]), sv);
 #pragma unroll
-        for (int p = 0; p < PI; ++p) {
-          Kt()[p * Cfg::KT_PS + (d0 + e) * Cfg::LDC + t] = sk[p];
-          Vt()[p * Cfg::KT_PS + (d0 + e) * Cfg::LDC + t] = sv[p];
+          for (int p = 0; p < PI; ++p) {
+            Kt()[p * Cfg::KT_PS + (d0 + e) * Cfg::LDC + t] = sk[p];
+            Vt()[p * Cfg::KT_PS + (d0 + e) * Cfg::LDC + t] = sv[p];
+          }
         }
       }
     }
     if (tid < C) {
-      const bool ok = tid < c;
-      sg[tid] = ok ? g[static_cast<size_t>(tok0 + tid) * H + h] : 0.f;
-      sb[tid] = ok ? beta[static_cast<size_t>(tok0 + tid) * H + h] : 0.f;
+      sg[tid] = gv;
+      sb[tid] = bv;
     }
     __syncthreads();
     if (tid < C) {
@@ -174,55 +221,56 @@ struct ChunkWork {
         G += sg[s];
         if (s == tid) Gt = G;
       }
+      const float gam = expf(Gt);
       sG[tid] = Gt;
-      sgam[tid] = expf(Gt);
+      sgam[tid] = gam;
       sD[tid] = expf(G - Gt);
+      sbg[tid] = sb[tid] * gam;
     }
     __syncthreads();
   }
 
-  // 8 consecutive features of token row t (zeros past the chunk) as planes.
-  __device__ void row_frag(const void* base, int t, int k0, bf16x8 (&out)[PI]) const {
-    const bool ok = t < c;
-    load_global8<IN, PI>(base, ok ? tok_off(t) + k0 : 0, ok, out);
-  }
-
-  // A = strictly lower beta_t Gamma_ts (k_t . k_s), fp32, into Af.
-  __device__ void gram_kk(const void* k) {
+  // A_ts = beta_t Gamma_ts (k_t . k_s), s < t: diagonal blocks in fp32
+  // (zero on and above the diagonal), strictly lower blocks as planes.
+  __device__ void gram_kk(const bf16x8 (&kf)[NT][KB][PI]) {
     int tcount = 0;
+#pragma unroll
     for (int ti = 0; ti < NT; ++ti) {
+#pragma unroll
       for (int tj = 0; tj <= ti; ++tj, ++tcount) {
         if ((tcount & 3) != wave) continue;
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < Cfg::KB; ++kb) {
-          bf16x8 a[PI], b[PI];
-          row_frag(k, 16 * ti + c16, 32 * kb + 8 * g4, a);
-          row_frag(k, 16 * tj + c16, 32 * kb + 8 * g4, b);
-          mma_planes<PI, PI>(acc, a, b);
-        }
+        for (int kb = 0; kb < KB; ++kb) mma_planes<PI, PI>(acc, kf[ti][kb], kf[tj][kb]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int t = 16 * ti + 4 * g4 + e, s = 16 * tj + c16;
-          Af()[t * Cfg::LDA + s] = s < t ? sb[t] * expf(sG[t] - sG[s]) * acc[e] : 0.f;
+          const int r = 4 * g4 + e;
+          const int t = 16 * ti + r, s = 16 * tj + c16;
+          const float a = s < t ? sb[t] * expf(sG[t] - sG[s]) * acc[e] : 0.f;
+          if (ti == tj) {
+            Adiag(ti)[r * 17 + c16] = a;
+          } else {
+            uint16_t sp[PT];
+            split_planes<PT>(a, sp);
+            uint16_t* blk = Aoff(ti * (ti - 1) / 2 + tj);
+#pragma unroll
+            for (int p = 0; p < PT; ++p) blk[p * Cfg::BLK_PS + r * Cfg::LDB + c16] = sp[p];
+          }
         }
       }
     }
   }
 
   // P = (Q K^T) (.) Gamma (s <= t, zero elsewhere and in padding columns), planes.
-  __device__ void gram_qk(const void* q, const void* k) {
-    for (int tile = wave; tile < NT * NT; tile += 4) {
+  __device__ void gram_qk(const bf16x8 (&qf)[NT][KB][PI], const bf16x8 (&kf)[NT][KB][PI]) {
+#pragma unroll
+    for (int tile = 0; tile < NT * NT; ++tile) {
+      if ((tile & 3) != wave) continue;
       const int ti = tile / NT, tj = tile % NT;
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
       if (tj <= ti) {
 #pragma unroll
-        for (int kb = 0; kb < Cfg::KB; ++kb) {
-          bf16x8 a[PI], b[PI];
-          row_frag(q, 16 * ti + c16, 32 * kb + 8 * g4, a);
-          row_frag(k, 16 * tj + c16, 32 * kb + 8 * g4, b);
-          mma_planes<PI, PI>(acc, a, b);
-        }
+        for (int kb = 0; kb < KB; ++kb) mma_planes<PI, PI>(acc, qf[ti][kb], kf[tj][kb]);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -231,124 +279,97 @@ struct ChunkWork {
         uint16_t sp[PT];
         split_planes<PT>(x, sp);
 #pragma unroll
-        for (int p = 0; p < PT; ++p) Pp()[p * Cfg::TT_PS + t * Cfg::LDC + s] = sp[p];
+        for (int p = 0; p < PT; ++p) Pp()[p * Cfg::P_PS + t * Cfg::LDP + s] = sp[p];
       }
     }
     if constexpr (Cfg::Cp > C) {
       for (int idx = tid; idx < C * (Cfg::Cp - C); idx += 256) {
         const int t = idx / (Cfg::Cp - C), s = C + idx % (Cfg::Cp - C);
 #pragma unroll
-        for (int p = 0; p < PT; ++p) Pp()[p * Cfg::TT_PS + t * Cfg::LDC + s] = 0;
+        for (int p = 0; p < PT; ++p) Pp()[p * Cfg::P_PS + t * Cfg::LDP + s] = 0;
       }
     }
   }
 
-  // T = (I + A)^{-1} (unit lower triangular), fp32, blockwise over 16x16 blocks:
-  // diagonal blocks by substitution, then T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
-  // one block diagonal at a time.  Reads Af, writes Tf (lower blocks only).
-  __device__ void solve() {
+  // T_ii = (I + A_ii)^{-1} for every diagonal block, by substitution in fp32
+  // (wave i, lane j computes column j), stored as planes over A_ii.
+  __device__ void invert_diagonal() {
     if (wave < NT && (tid & 63) < 16) {
-      const int j = tid & 15, base = 16 * wave;
+      const int j = tid & 15;
+      const float* A = Adiag(wave);
+      float a[16][16];
+#pragma unroll
+      for (int t = 1; t < 16; ++t)
+#pragma unroll
+        for (int s = 0; s < t; ++s) a[t][s] = A[t * 17 + s];
       float x[16];
 #pragma unroll
       for (int t = 0; t < 16; ++t) x[t] = t == j ? 1.f : 0.f;
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
 #pragma unroll
-        for (int t = s + 1; t < 16; ++t)
-          x[t] = fmaf(-Af()[(base + t) * Cfg::LDA + base + s], x[s], x[t]);
+        for (int t = s + 1; t < 16; ++t) x[t] = fmaf(-a[t][s], x[s], x[t]);
       }
+      uint16_t* T = Tdiag(wave);
 #pragma unroll
-      for (int t = 0; t < 16; ++t) Tf()[(base + t) * Cfg::LDA + base + j] = x[t];
-    }
-    __syncthreads();
-    for (int d = 1; d < NT; ++d) {
-      const int jb = wave, ib = wave + d;
-      const bool active = ib < NT;
-      if (active) {
+      for (int t = 0; t < 16; ++t) {
+        uint16_t sp[PT];
+        split_planes<PT>(x[t], sp);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          float acc = 0.f;
-          for (int kb = jb; kb < ib; ++kb) {
-#pragma unroll
-            for (int m = 0; m < 16; ++m)
-              acc = fmaf(Af()[(16 * ib + r) * Cfg::LDA + 16 * kb + m],
-                         Tf()[(16 * kb + m) * Cfg::LDA + 16 * jb + c16], acc);
-          }
-          X[wave * 256 + r * 16 + c16] = acc;
-        }
-      }
-      __syncthreads();
-      if (active) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          float acc = 0.f;
-#pragma unroll
-          for (int m = 0; m < 16; ++m)
-            acc = fmaf(Tf()[(16 * ib + r) * Cfg::LDA + 16 * ib + m], X[wave * 256 + m * 16 + c16],
-                       acc);
-          Tf()[(16 * ib + r) * Cfg::LDA + 16 * jb + c16] = -acc;
-        }
-      }
-      __syncthreads();
-    }
-  }
-
-  // T' = T diag(beta gamma) and T'' = T diag(beta) as planes over C x Cp.
-  __device__ void scale_t() {
-    constexpr int NE = C * Cfg::Cp;
-    constexpr int PER = (NE + 255) / 256;
-    float tv[PER];
-#pragma unroll
-    for (int qq = 0; qq < PER; ++qq) {
-      const int idx = tid + 256 * qq;
-      const int t = idx / Cfg::Cp, s = idx % Cfg::Cp;
-      tv[qq] = (idx < NE && s < C && s <= t) ? Tf()[t * Cfg::LDA + s] : 0.f;
-    }
-    __syncthreads();  // T is fully read before T'' overwrites it
-#pragma unroll
-    for (int qq = 0; qq < PER; ++qq) {
-      const int idx = tid + 256 * qq;
-      if (idx >= NE) break;
-      const int t = idx / Cfg::Cp, s = idx % Cfg::Cp;
-      const float bs = s < C ? sb[s] : 0.f;
-      const float gs = s < C ? sgam[s] : 0.f;
-      uint16_t a[PT], b[PT];
-      split_planes<PT>(tv[qq] * (bs * gs), a);
-      split_planes<PT>(tv[qq] * bs, b);
-#pragma unroll
-      for (int p = 0; p < PT; ++p) {
-        Tp()[p * Cfg::TT_PS + t * Cfg::LDC + s] = a[p];
-        Tpp()[p * Cfg::TT_PS + t * Cfg::LDC + s] = b[p];
+        for (int p = 0; p < PT; ++p) T[p * Cfg::BLK_PS + t * Cfg::LDB + j] = sp[p];
       }
     }
     __syncthreads();
   }
 
-  // W = T' K and Ut = T'' V for this wave's feature tiles (all chunk rows).
-  __device__ void wy(floatx4 (&Wacc)[NT][DPW], floatx4 (&Uacc)[NT][DPW]) const {
+  // Right-hand side of block row i for feature tile b in D-tile layout:
+  // rows t = 16 i + 4 g4 + e, column 16 b + c16, scaled by w_t.
+  __device__ floatx4 rhs(const uint16_t* Xt, const float* w, int i, int b) const {
+    floatx4 r;
+    const uint16_t* src = Xt + (16 * b + c16) * Cfg::LDC + 16 * i + 4 * g4;
 #pragma unroll
-    for (int a = 0; a < NT; ++a) {
+    for (int e = 0; e < 4; ++e) {
+      float x = 0.f;
+#pragma unroll
+      for (int p = 0; p < PI; ++p) x += bf16_bits_to_f32(src[p * Cfg::KT_PS + e]);
+      r[e] = w[16 * i + 4 * g4 + e] * x;
+    }
+    return r;
+  }
+
+  // Block forward substitution, all in this wave's registers:
+  // W = (I + A)^{-1} diag(beta gamma) K and Ut = (I + A)^{-1} diag(beta) V for
+  // the wave's feature tiles.
+  __device__ void solve_wy(floatx4 (&Wacc)[NT][DPW], floatx4 (&Uacc)[NT][DPW]) const {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      shortx4 tii[PT];
+      load_lds4<PT>(Tdiag(i) + c16 * Cfg::LDB + 4 * g4, Cfg::BLK_PS, tii);
 #pragma unroll
       for (int bb = 0; bb < DPW; ++bb) {
         const int b = wave + 4 * bb;
-        floatx4 w = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+        floatx4 rw = rhs(Kt(), sbg, i, b);
+        floatx4 ru = rhs(Vt(), sb, i, b);
+        floatx4 sw = {0.f, 0.f, 0.f, 0.f}, su = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < Cfg::CB; ++kb) {
-          bf16x8 ta[PT], tb[PT], kf[PI], vf[PI];
-          const int arow = (16 * a + c16) * Cfg::LDC + 32 * kb + 8 * g4;
-          const int brow = (16 * b + c16) * Cfg::LDC + 32 * kb + 8 * g4;
-          load_lds8<PT>(Tp() + arow, Cfg::TT_PS, ta);
-          load_lds8<PT>(Tpp() + arow, Cfg::TT_PS, tb);
-          load_lds8<PI>(Kt() + brow, Cfg::KT_PS, kf);
-          load_lds8<PI>(Vt() + brow, Cfg::KT_PS, vf);
-          mma_planes<PT, PI>(w, ta, kf);
-          mma_planes<PT, PI>(u, tb, vf);
+        for (int j = 0; j < i; ++j) {
+          shortx4 aij[PT], xw[PT], xu[PT];
+          load_lds4<PT>(Aoff(i * (i - 1) / 2 + j) + c16 * Cfg::LDB + 4 * g4, Cfg::BLK_PS, aij);
+          split4<PT>(Wacc[j][bb], xw);
+          split4<PT>(Uacc[j][bb], xu);
+          mma16_planes<PT, PT>(sw, aij, xw);
+          mma16_planes<PT, PT>(su, aij, xu);
         }
-        Wacc[a][bb] = w;
-        Uacc[a][bb] = u;
+        rw -= sw;
+        ru -= su;
+        shortx4 pw[PT], pu[PT];
+        split4<PT>(rw, pw);
+        split4<PT>(ru, pu);
+        floatx4 w = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+        mma16_planes<PT, PT>(w, tii, pw);
+        mma16_planes<PT, PT>(u, tii, pu);
+        Wacc[i][bb] = w;
+        Uacc[i][bb] = u;
       }
     }
   }
@@ -380,23 +401,28 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
     const float* __restrict__ beta, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ cidx, float* __restrict__ Lout, float* __restrict__ Mout, int H,
     int T_total) {
-  using Cfg = ChunkCfg<D, C, IN>;
-  __shared__ __align__(16) unsigned char smem[Cfg::LOCAL_BYTES];
+  using W_ = ChunkWork<D, C, IN, false>;
+  using Cfg = typename W_::Cfg;
+  __shared__ __align__(16) unsigned char smem[Cfg::BYTES];
   const int cid = blockIdx.x, h = blockIdx.y;
   const ChunkTokens ct = chunk_tokens(cu, cidx, cid, C, T_total);
   if (ct.c <= 0) return;
 
-  ChunkWork<D, C, IN> w;
-  w.init(smem, Cfg::OFF_GATE_LOCAL, ct.tok0, ct.c, h, H);
-  w.load(k, v, g, beta);
-  w.gram_kk(k);
+  W_ w;
+  w.init(smem, ct.tok0, ct.c, h, H);
+  {
+    bf16x8 kf[Cfg::NT][Cfg::KB][Cfg::PI];
+    w.rows_frags(k, kf);
+    w.load(k, v, g, beta);
+    w.gram_kk(kf);
+  }
   __syncthreads();
-  w.solve();
-  w.scale_t();
+  w.invert_diagonal();
 
   floatx4 Wacc[Cfg::NT][Cfg::DPW], Uacc[Cfg::NT][Cfg::DPW];
-  w.wy(Wacc, Uacc);
+  w.solve_wy(Wacc, Uacc);
 
+  // L = Ut^T diag(D) K (rows of this wave's feature tiles), M^T stored.
   const float gam_end = w.sgam[C - 1];
   const size_t base = (static_cast<size_t>(cid) * H + h) * D * D;
 #pragma unroll
@@ -418,41 +444,68 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
         mma_planes<Cfg::PT, Cfg::PI>(l, AU[kb], kf);
         mma_planes<Cfg::PT, Cfg::PI>(m, AW[kb], kf);
       }
+      const int i0 = 16 * b + 4 * w.g4, j = 16 * bj + w.c16;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * b + 4 * w.g4 + e, j = 16 * bj + w.c16;
-        Lout[base + static_cast<size_t>(i) * D + j] = l[e];
-        Mout[base + static_cast<size_t>(i) * D + j] = (i == j ? gam_end : 0.f) - m[e];
-      }
+      for (int e = 0; e < 4; ++e) Lout[base + static_cast<size_t>(i0 + e) * D + j] = l[e];
+      float4 mt;
+      mt.x = (i0 + 0 == j ? gam_end : 0.f) - m[0];
+      mt.y = (i0 + 1 == j ? gam_end : 0.f) - m[1];
+      mt.z = (i0 + 2 == j ? gam_end : 0.f) - m[2];
+      mt.w = (i0 + 3 == j ? gam_end : 0.f) - m[3];
+      *reinterpret_cast<float4*>(Mout + base + static_cast<size_t>(j) * D + i0) = mt;
     }
   }
 }
 
-template <int D, int C, Dt IN, Dt OUT>
+template <int D, int C, Dt IN, Dt OUTD>
 __global__ __launch_bounds__(256) void chunk_out_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ cidx, const float* __restrict__ state_in,
     const float* __restrict__ fixed, void* __restrict__ o, int H, int T_total) {
-  using Cfg = ChunkCfg<D, C, IN>;
-  constexpr int PI = Cfg::PI, PT = Cfg::PT, NT = Cfg::NT, DPW = Cfg::DPW;
-  __shared__ __align__(16) unsigned char smem[Cfg::OUT_BYTES];
+  using W_ = ChunkWork<D, C, IN, true>;
+  using Cfg = typename W_::Cfg;
+  constexpr int PI = Cfg::PI, PT = Cfg::PT, NT = Cfg::NT, DPW = Cfg::DPW, KB = Cfg::KB;
+  __shared__ __align__(16) unsigned char smem[Cfg::BYTES];
   const int cid = blockIdx.x, h = blockIdx.y;
   const ChunkTokens ct = chunk_tokens(cu, cidx, cid, C, T_total);
   if (ct.c <= 0) return;
 
-  ChunkWork<D, C, IN> w;
-  w.init(smem, Cfg::OFF_GATE_OUT, ct.tok0, ct.c, h, H);
-  w.load(k, v, g, beta);
-  w.gram_kk(k);
-  w.gram_qk(q, k);
+  W_ w;
+  w.init(smem, ct.tok0, ct.c, h, H);
+  bf16x8 qf[NT][KB][PI];
+  {
+    bf16x8 kf[NT][KB][PI];
+    w.rows_frags(k, kf);
+    w.rows_frags(q, qf);
+    w.load(k, v, g, beta);
+    w.gram_kk(kf);
+    w.gram_qk(qf, kf);
+  }
+
+  // Start-state rows of this wave's feature tiles as planes, loaded early
+  // (nothing before this point depends on them).
+  const float* S0 = nullptr;
+  if (ct.j > 0) {
+    S0 = fixed + (static_cast<size_t>(cid - 1) * H + h) * D * D;
+  } else if (state_in != nullptr) {
+    S0 = state_in + (static_cast<size_t>(ct.n) * H + h) * D * D;
+  }
+  bf16x8 SB[DPW][KB][PT];
+#pragma unroll
+  for (int bb = 0; bb < DPW; ++bb) {
+    const int i = 16 * (w.wave + 4 * bb) + w.c16;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      load_global8<Dt::F32, PT>(S0, S0 ? static_cast<size_t>(i) * D + 32 * kb + 8 * w.g4 : 0,
+                                S0 != nullptr, SB[bb][kb]);
+  }
   __syncthreads();
-  w.solve();
-  w.scale_t();
+  w.invert_diagonal();
 
   floatx4 Wacc[NT][DPW], Uacc[NT][DPW];
-  w.wy(Wacc, Uacc);
-  __syncthreads();  // T' and T'' are consumed; W planes take their place
+  w.solve_wy(Wacc, Uacc);
+  __syncthreads();  // K^T and V^T are consumed; W planes take their place
 
 #pragma unroll
   for (int a = 0; a < NT; ++a) {
@@ -469,23 +522,6 @@ __global__ __launch_bounds__(256) void chunk_out_kernel(
       }
     }
   }
-
-  // Start state rows of this wave's feature tiles, as planes.
-  const float* S0 = nullptr;
-  if (ct.j > 0) {
-    S0 = fixed + (static_cast<size_t>(cid - 1) * H + h) * D * D;
-  } else if (state_in != nullptr) {
-    S0 = state_in + (static_cast<size_t>(ct.n) * H + h) * D * D;
-  }
-  bf16x8 SB[DPW][Cfg::KB][PT];
-#pragma unroll
-  for (int bb = 0; bb < DPW; ++bb) {
-    const int i = 16 * (w.wave + 4 * bb) + w.c16;
-#pragma unroll
-    for (int kb = 0; kb < Cfg::KB; ++kb)
-      load_global8<Dt::F32, PT>(S0, static_cast<size_t>(i) * D + 32 * kb + 8 * w.g4,
-                                S0 != nullptr, SB[bb][kb]);
-  }
   __syncthreads();  // W planes visible
 
   // U = Ut - W S0^T
@@ -495,7 +531,7 @@ __global__ __launch_bounds__(256) void chunk_out_kernel(
     for (int bb = 0; bb < DPW; ++bb) {
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < Cfg::KB; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         bf16x8 wa[PT];
         load_lds8<PT>(w.Wp() + (16 * a + w.c16) * Cfg::LDD + 32 * kb + 8 * w.g4, Cfg::W_PS, wa);
         mma_planes<PT, PT>(acc, wa, SB[bb][kb]);
@@ -512,11 +548,7 @@ __global__ __launch_bounds__(256) void chunk_out_kernel(
     for (int bb = 0; bb < DPW; ++bb) {
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < Cfg::KB; ++kb) {
-        bf16x8 qa[PI];
-        w.row_frag(q, 16 * a + w.c16, 32 * kb + 8 * w.g4, qa);
-        mma_planes<PI, PT>(acc, qa, SB[bb][kb]);
-      }
+      for (int kb = 0; kb < KB; ++kb) mma_planes<PI, PT>(acc, qf[a][kb], SB[bb][kb]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) Oacc[a][bb][e] = w.sgam[16 * a + 4 * w.g4 + e] * acc[e];
     }
@@ -531,7 +563,7 @@ __global__ __launch_bounds__(256) void chunk_out_kernel(
 #pragma unroll
       for (int kb = 0; kb < Cfg::CB; ++kb) {
         bf16x8 pa[PT];
-        load_lds8_perm<PT>(w.Pp() + (16 * a + w.c16) * Cfg::LDC + 32 * kb + 4 * w.g4, Cfg::TT_PS,
+        load_lds8_perm<PT>(w.Pp() + (16 * a + w.c16) * Cfg::LDP + 32 * kb + 4 * w.g4, Cfg::P_PS,
                            pa);
         mma_planes<PT, PT>(Oacc[a][bb], pa, UB[kb]);
       }
@@ -546,7 +578,7 @@ __global__ __launch_bounds__(256) void chunk_out_kernel(
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * a + 4 * w.g4 + e;
         if (t < ct.c)
-          store_scalar<OUT>(o, w.tok_off(t) + 16 * (w.wave + 4 * bb) + w.c16, Oacc[a][bb][e]);
+          store_scalar<OUTD>(o, w.tok_off(t) + 16 * (w.wave + 4 * bb) + w.c16, Oacc[a][bb][e]);
       }
     }
   }
@@ -561,13 +593,13 @@ hipError_t local_t(const void* k, const void* v, const float* g, const float* be
   return hipGetLastError();
 }
 
-template <int D, int C, Dt IN, Dt OUT>
+template <int D, int C, Dt IN, Dt OUTD>
 hipError_t out_t(const void* q, const void* k, const void* v, const float* g, const float* beta,
                  const int32_t* cu, const int32_t* cidx, const float* state_in,
                  const float* fixed, void* o, int max_chunks, int T_total, int H,
                  hipStream_t stream) {
-  hipLaunchKernelGGL((chunk_out_kernel<D, C, IN, OUT>), dim3(max_chunks, H), dim3(256), 0, stream,
-                     q, k, v, g, beta, cu, cidx, state_in, fixed, o, H, T_total);
+  hipLaunchKernelGGL((chunk_out_kernel<D, C, IN, OUTD>), dim3(max_chunks, H), dim3(256), 0,
+                     stream, q, k, v, g, beta, cu, cidx, state_in, fixed, o, H, T_total);
   return hipGetLastError();
 }
 

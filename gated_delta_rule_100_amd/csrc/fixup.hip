@@ -14,8 +14,8 @@
 // with an initial state the scan begins at the sequence's first chunk; without
 // one the first fixed state is L of that chunk and the scan begins at the next.
 // All arithmetic is fp32 FMA.
-#include "gdr_device.h"
 #include "launch.h"
+#include "mfma_planes.h"
 
 namespace gdr {
 namespace {
@@ -72,11 +72,12 @@ __global__ __launch_bounds__(2 * DK) void fixup_kernel(const float* __restrict__
   __syncthreads();
   if (start >= c_end) return;
 
+  // M is stored transposed: the column `col` of M_c is row `col` of the slot.
   float m_cur[KH], l_cur[R];
   {
-    const float* Mc = M + m_base(start) + static_cast<size_t>(kh) * KH * DK + col;
+    const float* Mc = M + m_base(start) + static_cast<size_t>(col) * DK + kh * KH;
 #pragma unroll
-    for (int kk = 0; kk < KH; ++kk) m_cur[kk] = Mc[static_cast<size_t>(kk) * DK];
+    for (int kk = 0; kk < KH; ++kk) m_cur[kk] = Mc[kk];
 #pragma unroll
     for (int i = 0; i < R; ++i) l_cur[i] = kh == 0 ? L[l_at(start, i)] : 0.f;
   }
@@ -85,9 +86,9 @@ __global__ __launch_bounds__(2 * DK) void fixup_kernel(const float* __restrict__
     const bool more = c + 1 < c_end;
     float m_nxt[KH], l_nxt[R];
     if (more) {
-      const float* Mc = M + m_base(c + 1) + static_cast<size_t>(kh) * KH * DK + col;
+      const float* Mc = M + m_base(c + 1) + static_cast<size_t>(col) * DK + kh * KH;
 #pragma unroll
-      for (int kk = 0; kk < KH; ++kk) m_nxt[kk] = Mc[static_cast<size_t>(kk) * DK];
+      for (int kk = 0; kk < KH; ++kk) m_nxt[kk] = Mc[kk];
 #pragma unroll
       for (int i = 0; i < R; ++i) l_nxt[i] = kh == 0 ? L[l_at(c + 1, i)] : 0.f;
     }
@@ -129,6 +130,196 @@ __global__ __launch_bounds__(2 * DK) void fixup_kernel(const float* __restrict__
   }
 }
 
+// Matrix-core fixup: 16 state rows per workgroup (one 16-row MFMA tile) and
+// one wave per 16-wide output column tile (8 waves at d = 128).  Per chunk:
+// S' = S M_c + L_c with S as bf16 planes in LDS (double-buffered, so one
+// barrier per chunk).  M is read transposed (row b of a slot holds column b
+// of M_c), so lane (c, g) of the B operand -- M[32kb + 8g .. 8g+7][16w + c] --
+// is 32 contiguous bytes, loaded while the previous chunk is multiplied.  L
+// is loaded in the output layout.  Workgroups of one unit (and head) are
+// placed on one XCD (dispatch is round-robin over the 8 XCDs by workgroup
+// id), so M_c is fetched from HBM once and served to all of them from L2.
+//
+// Each chunk costs every workgroup a full M_c from L2, so a long chain is
+// bound by that per-step transfer; long sequences therefore use a two-level
+// scan over segments of `seg` chunks (the segment-size heuristic plays the
+// role of the CP chunking heuristic on the FlashInfer PR #3866 page, code
+// changes 3):
+//   kSeq      units are sequences; fixed[c] for every chunk;
+//   kCompose  units are segments; rows 0..D-1 run from a zero state and give
+//             the segment's local state L_s (written once), rows D..2D-1 start
+//             from the identity without L and give the segment's transfer
+//             M_s = M_c0 M_c1 ... (written transposed, like M);
+//   kApply    units are segments; the start state is the previous segment's
+//             scanned state (or the sequence's initial state) and fixed[c] is
+//             written for every chunk.
+// The scan over segments is kSeq on (L_s, M_s).
+constexpr int kXcds = 8;
+enum FixMode { kSeq = 0, kCompose = 1, kApply = 2 };
+
+template <int D, int P, int MODE>
+__global__ __launch_bounds__(D * 4) void fixup_mfma_kernel(
+    const float* __restrict__ L, const float* __restrict__ Mt, const float* __restrict__ state_in,
+    const int32_t* __restrict__ offs, const int32_t* __restrict__ seg_idx, int seg,
+    const float* __restrict__ seg_start, float* __restrict__ out, float* __restrict__ out_mt,
+    int n_chunks, int H, int n_units) {
+  constexpr int NTHR = D * 4;       // one wave per 16 output columns
+  constexpr int RB = D / 16;        // row blocks (workgroups) per state
+  constexpr int RBU = MODE == kCompose ? 2 * RB : RB;  // row blocks per unit
+  constexpr int KB = D / 32;        // 32-deep contraction blocks
+  constexpr int LDS_LD = D + 8;     // row stride of the state planes (bf16 elements)
+  constexpr int PS = 16 * LDS_LD;   // plane stride
+  __shared__ __align__(16) uint16_t s_planes[2][P * PS];
+
+  // XCD-aware placement of (unit x head, row block)
+  const int b = blockIdx.x;
+  const int xcd = b % kXcds, slot = b / kXcds;
+  const int pair = xcd + kXcds * (slot / RBU);
+  const int rbu = slot % RBU;
+  if (pair >= n_units * H) return;
+  const int u = pair / H, h = pair % H;
+  const bool trans_rows = MODE == kCompose && rbu >= RB;  // transfer-product rows
+  const int row0 = (rbu % RB) * 16;
+
+  int n, c_begin, c_end, sidx = 0;
+  if (MODE == kSeq) {
+    n = u;
+    c_begin = offs[n];
+    c_end = offs[n + 1];
+  } else {
+    n = seg_idx[2 * u];
+    sidx = seg_idx[2 * u + 1];
+    if (n < 0 || sidx < 0) return;
+    c_begin = offs[n] + sidx * seg;
+    c_end = offs[n + 1];
+    c_end = c_end < c_begin + seg ? c_end : c_begin + seg;
+  }
+  c_end = c_end < n_chunks ? c_end : n_chunks;
+  c_begin = c_begin < 0 ? 0 : c_begin;
+  if (c_begin >= c_end) return;
+
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int c16 = tid & 15, g4 = (tid & 63) >> 4;
+  const int col = 16 * wave + c16;
+  auto st_at = [&](int c, int i, int cc) -> size_t {  // element (row0+i, cc) of a state slot
+    return ((static_cast<size_t>(c) * H + h) * D + row0 + i) * D + cc;
+  };
+
+  // Start rows -> planes (buffer 0).
+  const float* init = nullptr;  // start state rows, or nullptr for "first local state"
+  if (MODE == kSeq) {
+    if (state_in != nullptr) init = state_in + (static_cast<size_t>(n) * H + h) * D * D;
+  } else if (MODE == kApply) {
+    if (sidx > 0) init = seg_start + (static_cast<size_t>(u - 1) * H + h) * D * D;
+    else if (state_in != nullptr) init = state_in + (static_cast<size_t>(n) * H + h) * D * D;
+  }
+  const bool from_L = !trans_rows && init == nullptr;
+  int start = from_L ? c_begin + 1 : c_begin;
+  for (int idx = tid; idx < 16 * D; idx += NTHR) {
+    const int i = idx / D, cc = idx % D;
+    float x;
+    if (trans_rows) {
+      x = (row0 + i == cc) ? 1.f : 0.f;
+    } else if (init != nullptr) {
+      x = init[static_cast<size_t>(row0 + i) * D + cc];
+    } else {
+      x = L[st_at(c_begin, i, cc)];
+      if (MODE != kCompose) out[st_at(c_begin, i, cc)] = x;
+    }
+    uint16_t sp[P];
+    split_planes<P>(x, sp);
+#pragma unroll
+    for (int p = 0; p < P; ++p) s_planes[0][p * PS + i * LDS_LD + cc] = sp[p];
+  }
+  __syncthreads();
+
+  typedef float4 MRaw[KB][2];
+  typedef float LRaw[4];
+  // Loads are unconditional (a chunk past the end re-reads the last one).
+  auto fetch = [&](int c, MRaw& m, LRaw& l) {
+    c = c < c_end ? c : c_end - 1;
+    const float4* src = reinterpret_cast<const float4*>(
+        Mt + (static_cast<size_t>(c) * H + h) * D * D + static_cast<size_t>(col) * D + 8 * g4);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      m[kb][0] = src[8 * kb];
+      m[kb][1] = src[8 * kb + 1];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) l[e] = trans_rows ? 0.f : L[st_at(c, 4 * g4 + e, col)];
+  };
+
+  MRaw m;
+  LRaw l;
+  fetch(start, m, l);
+  int buf = 0;
+  float last[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int c = start; c < c_end; ++c) {
+    bf16x8 mb[KB][P];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const float x[8] = {m[kb][0].x, m[kb][0].y, m[kb][0].z, m[kb][0].w,
+                          m[kb][1].x, m[kb][1].y, m[kb][1].z, m[kb][1].w};
+      split8<P>(x, mb[kb]);
+    }
+    float lc[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lc[e] = l[e];
+    // Keep the next loads below the conversion (the raw registers are free again).
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(c + 1, m, l);  // next chunk's operands are in flight during this one
+
+    // S' tile = S M_c: two accumulators (even / odd k blocks) keep the
+    // dependent MFMA chains short.
+    floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    const uint16_t* cur = s_planes[buf];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      bf16x8 sa[P];
+      load_lds8<P>(cur + c16 * LDS_LD + 32 * kb + 8 * g4, PS, sa);
+      mma_planes<P, P>((kb & 1) ? acc1 : acc0, sa, mb[kb]);
+    }
+    uint16_t* nxt = s_planes[buf ^ 1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = (acc0[e] + acc1[e]) + lc[e];
+      last[e] = x;
+      if (MODE != kCompose) out[st_at(c, 4 * g4 + e, col)] = x;
+      uint16_t sp[P];
+      split_planes<P>(x, sp);
+#pragma unroll
+      for (int p = 0; p < P; ++p) nxt[p * PS + (4 * g4 + e) * LDS_LD + col] = sp[p];
+    }
+    buf ^= 1;
+    __syncthreads();
+  }
+
+  if (MODE == kCompose) {
+    // Final rows of the segment: L_s rows in state layout, M_s transposed.
+    if (start >= c_end) {  // a one-chunk segment: L_s = L of that chunk, M_s = its M
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g4 + e;
+        if (trans_rows) {
+          const float* Mc = Mt + (static_cast<size_t>(c_begin) * H + h) * D * D;
+          last[e] = Mc[static_cast<size_t>(col) * D + row0 + r];
+        } else {
+          last[e] = L[st_at(c_begin, r, col)];
+        }
+      }
+    }
+    const size_t base = (static_cast<size_t>(u) * H + h) * D * D;
+    if (trans_rows) {
+      *reinterpret_cast<float4*>(out_mt + base + static_cast<size_t>(col) * D + row0 + 4 * g4) =
+          make_float4(last[0], last[1], last[2], last[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        out[base + static_cast<size_t>(row0 + 4 * g4 + e) * D + col] = last[e];
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void final_state_kernel(const float* __restrict__ state_in,
                                                           const float* __restrict__ fixed,
                                                           const int32_t* __restrict__ offs,
@@ -155,17 +346,50 @@ __global__ __launch_bounds__(256) void final_state_kernel(const float* __restric
 
 }  // namespace
 
+hipError_t launch_fixup_mode(int mode, const float* L, const float* Mt, const float* state_in,
+                             const int32_t* offs, const int32_t* seg_idx, int seg,
+                             const float* seg_start, float* out, float* out_mt, int n_chunks,
+                             int H, int n_units, int dk, int planes, hipStream_t stream) {
+  if (n_units <= 0) return hipSuccess;
+  const int pairs = n_units * H;
+  const int rbu = (dk / 16) * (mode == kCompose ? 2 : 1);
+  const dim3 grid(kXcds * ((pairs + kXcds - 1) / kXcds) * rbu);
+#define GDR_FIX(D_, P_, M_)                                                                     \
+  hipLaunchKernelGGL((fixup_mfma_kernel<D_, P_, M_>), grid, dim3(D_ * 4), 0, stream, L, Mt,      \
+                     state_in, offs, seg_idx, seg, seg_start, out, out_mt, n_chunks, H, n_units)
+#define GDR_FIX_P(D_, M_)                                                                       \
+  do {                                                                                          \
+    if (planes == 2) GDR_FIX(D_, 2, M_); else GDR_FIX(D_, 3, M_);                               \
+  } while (0)
+#define GDR_FIX_M(D_)                                                                           \
+  do {                                                                                          \
+    if (mode == kSeq) GDR_FIX_P(D_, kSeq);                                                      \
+    else if (mode == kCompose) GDR_FIX_P(D_, kCompose);                                         \
+    else GDR_FIX_P(D_, kApply);                                                                 \
+  } while (0)
+  if (dk == 128) GDR_FIX_M(128); else GDR_FIX_M(64);
+#undef GDR_FIX_M
+#undef GDR_FIX_P
+#undef GDR_FIX
+  return hipGetLastError();
+}
+
 hipError_t launch_fixup(const float* L, const float* M, const float* state_in,
                         const int32_t* chunk_offsets, int N, float* fixed, int n_chunks, int H,
-                        int dk, int dv, hipStream_t stream) {
-  if (dk == 128 && dv == 128) {
-    hipLaunchKernelGGL((fixup_kernel<128, 128, kFixupRows>), dim3(128 / kFixupRows, H, N),
-                       dim3(256), 0, stream, L, M, state_in, chunk_offsets, fixed, n_chunks, H);
-  } else {
-    hipLaunchKernelGGL((fixup_kernel<64, 64, kFixupRows>), dim3(64 / kFixupRows, H, N),
-                       dim3(128), 0, stream, L, M, state_in, chunk_offsets, fixed, n_chunks, H);
+                        int dk, int dv, int planes, hipStream_t stream) {
+  (void)dv;
+  if (planes == 0) {
+    if (dk == 128) {
+      hipLaunchKernelGGL((fixup_kernel<128, 128, kFixupRows>), dim3(128 / kFixupRows, H, N),
+                         dim3(256), 0, stream, L, M, state_in, chunk_offsets, fixed, n_chunks, H);
+    } else {
+      hipLaunchKernelGGL((fixup_kernel<64, 64, kFixupRows>), dim3(64 / kFixupRows, H, N),
+                         dim3(128), 0, stream, L, M, state_in, chunk_offsets, fixed, n_chunks, H);
+    }
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  return launch_fixup_mode(kSeq, L, M, state_in, chunk_offsets, nullptr, 0, nullptr, fixed,
+                           nullptr, n_chunks, H, N, dk, planes, stream);
 }
 
 hipError_t launch_final_state(const float* state_in, const float* fixed,

@@ -19,9 +19,21 @@ hipError_t launch_layout(const int32_t* cu_seqlens, int N, int chunk, int32_t* c
                          int32_t* chunk_indices, int max_chunks, hipStream_t stream);
 
 // Inter-chunk fixup: fixed[c] = fixed[c-1] M_c + L_c per (sequence, head).
+// planes = 2 or 3: matrix-core scan with the state and M carried as that many
+// bf16 planes (3 keeps fp32 precision); planes = 0: fp32 FMA scan.
 hipError_t launch_fixup(const float* L, const float* M, const float* state_in,
                         const int32_t* chunk_offsets, int N, float* fixed, int n_chunks, int H,
-                        int dk, int dv, hipStream_t stream);
+                        int dk, int dv, int planes, hipStream_t stream);
+
+// Fixup variants over units (sequences or segments of `seg` chunks); see
+// fixup.hip.  mode 0: per-sequence scan writing every chunk state to `out`;
+// mode 1: per-segment local state (out) and transposed transfer product
+// (out_mt); mode 2: per-segment scan from the scanned segment starts
+// (seg_start) writing every chunk state to `out`.
+hipError_t launch_fixup_mode(int mode, const float* L, const float* Mt, const float* state_in,
+                             const int32_t* offs, const int32_t* seg_idx, int seg,
+                             const float* seg_start, float* out, float* out_mt, int n_chunks,
+                             int H, int n_units, int dk, int planes, hipStream_t stream);
 
 // Chunk-local precompute: L_c and M_c for every chunk slot < max_chunks.
 hipError_t launch_chunk_local(const void* k, const void* v, const float* g, const float* beta,

@@ -25,8 +25,55 @@ namespace gdr {
 typedef unsigned short ushort8 __attribute__((ext_vector_type(8)));
 typedef unsigned short ushort4 __attribute__((ext_vector_type(4)));
 
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ floatx4 mfma16x16x32(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x16 variant (lane (c, g): A[c][4g .. 4g+3], B[4g .. 4g+3][c]); its
+// B operand has exactly the layout of a D tile, so an output tile feeds the
+// next product without leaving registers.
+__device__ __forceinline__ floatx4 mfma16x16x16(shortx4 a, shortx4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+template <int PA, int PB>
+__device__ __forceinline__ void mma16_planes(floatx4& acc, const shortx4 (&a)[PA],
+                                             const shortx4 (&b)[PB]) {
+  constexpr int PM = PA > PB ? PA : PB;
+#pragma unroll
+  for (int s = PM - 1; s >= 0; --s) {
+#pragma unroll
+    for (int i = 0; i < PA; ++i) {
+      const int j = s - i;
+      if (j >= 0 && j < PB) acc = mfma16x16x16(a[i], b[j], acc);
+    }
+  }
+}
+
+// Split 4 fp32 values (a D tile's floatx4) into P planes of 4 bf16.
+template <int P>
+__device__ __forceinline__ void split4(const floatx4& x, shortx4 (&out)[P]) {
+  floatx4 r = x;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const __bf16 hb = static_cast<__bf16>(r[e]);
+      out[p][e] = __builtin_bit_cast(short, hb);
+      r[e] = r[e] - static_cast<float>(hb);
+    }
+  }
+}
+
+// 4 consecutive bf16 of each plane from LDS (8-byte aligned).
+template <int P>
+__device__ __forceinline__ void load_lds4(const uint16_t* base, int plane_stride,
+                                          shortx4 (&out)[P]) {
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    out[p] = *reinterpret_cast<const shortx4*>(base + p * plane_stride);
 }
 
 template <int PA, int PB>
@@ -49,8 +96,9 @@ __device__ __forceinline__ void split_planes(float x, uint16_t (&out)[P]) {
   float r = x;
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-    out[p] = f32_to_bf16_bits(r);
-    r = r - bf16_bits_to_f32(out[p]);
+    const __bf16 hb = static_cast<__bf16>(r);
+    out[p] = __builtin_bit_cast(uint16_t, hb);
+    r = r - static_cast<float>(hb);
   }
 }
 
@@ -60,10 +108,10 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8 (&out)[P]) {
   ushort8 w[P];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    uint16_t s[P];
-    split_planes<P>(x[e], s);
+    uint16_t sp[P];
+    split_planes<P>(x[e], sp);
 #pragma unroll
-    for (int p = 0; p < P; ++p) w[p][e] = s[p];
+    for (int p = 0; p < P; ++p) w[p][e] = sp[p];
   }
 #pragma unroll
   for (int p = 0; p < P; ++p) out[p] = __builtin_bit_cast(bf16x8, w[p]);

@@ -141,7 +141,9 @@ size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int 
  *   L_out       [max_chunks, H, dv, dk] fp32 or NULL: local state of every chunk
  *               (the chunk run from a zero state)
  *   M_out       [max_chunks, H, dk, dk] fp32 or NULL: transfer matrix of every
- *               chunk, M_out[c][a][b] = M_c[a][b] with S_end = S_start M_c + L_c
+ *               chunk, stored TRANSPOSED: M_out[c][h][b][a] = M_c[a][b], where
+ *               S_end = S_start M_c + L_c (row b of a slot is column b of M_c,
+ *               the layout the fixup reads with contiguous loads)
  *   fixed_out   [max_chunks, H, dv, dk] fp32 or NULL: state at the end of every
  *               chunk
  *   (max_chunks = gdr_max_chunks(T_total, N, chunk); chunk slot
@@ -170,7 +172,8 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v,
  * gdr_state_fixup -- the inter-chunk fixup alone.
  *
  *   L             [n_chunks, H, dv, dk] fp32 local states
- *   M             [n_chunks, H, dk, dk] fp32 transfer matrices
+ *   M             [n_chunks, H, dk, dk] fp32 transfer matrices, transposed as
+ *                 in gdr_chunk_prefill: M[c][h][b][a] = M_c[a][b]
  *   state_in      [N, H, dv, dk] fp32, or NULL (no initial state)
  *   chunk_offsets [N+1] int32 device: sequence n owns chunk slots
  *                 [chunk_offsets[n], chunk_offsets[n+1])

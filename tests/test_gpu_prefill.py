@@ -54,7 +54,8 @@ def check_against_oracle(d, res, chunk, check_locals=True):
                             d["state0"])
         n = r2["L"].shape[0]
         errs["L"] = rel_err(host64(res["L"][:n]), r2["L"])
-        errs["M"] = rel_err(host64(res["M"][:n]), r2["M"])
+        # M is stored transposed: slot[c][h][b][a] = M_c[a][b]
+        errs["M"] = rel_err(host64(res["M"][:n].transpose(-1, -2)), r2["M"])
     say(f"  errors: {errs}")
     for key, e in errs.items():
         assert e <= tol, (key, e)
@@ -219,3 +220,23 @@ def test_split_prefill_resumes():
         state = r["state_out"].cpu().numpy()
     assert rel_err(host64(torch.cat(parts)), host64(full["o"])) <= 1e-3
     assert rel_err(state.astype(np.float64), host64(full["state_out"])) <= 1e-3
+
+
+# Long sequences with few heads take the two-level (segmented) fixup: fold
+# segments of chunks, scan the segments, then apply the scanned starts.
+LONG_CASES = {
+    "long-T32768-H1-slow": (4, dict(seqlens=[32768], H=1, gate="slow")),
+    "long-T32768-H1-unit-state": (4, dict(seqlens=[32768], H=1, gate="unit", state0=True)),
+    "long-T32768-H1-std-state": (4, dict(seqlens=[32768], H=1, state0=True)),
+    "long-varlen-ragged-empty-H1": (4, dict(seqlens=[30000, 0, 19500], H=1, gate="slow",
+                                            state0=True)),
+}
+
+
+@pytest.mark.parametrize("name", list(LONG_CASES))
+def test_prefill_long_two_level(name):
+    idx, ov = LONG_CASES[name]
+    d = workload(idx, seed=120, **ov)
+    say(f"prefill two-level {name}: T={d['T']} N={d['N']} H={d['H']}")
+    res = run_prefill(d)
+    check_against_oracle(d, res, d["chunk"], check_locals=False)
