@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+    ap.add_argument("--cpu-seconds", type=float, default=16.0,
                     help="approximate CPU time budget of the oracle baseline")
     return ap.parse_args()
 
@@ -82,18 +82,53 @@ def bench_decode(torch, gdr, steps, warmup):
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    # back-to-back launches between two events on the launch stream: the
+    # average is the kernel's launch duration over the timed region
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(steps):
-        ev[i][0].record(stream)
         launch(i)
-        ev[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = [a.elapsed_time(b) for a, b in ev]
-    return dict(ms_mean=float(np.mean(ms)), ms_median=float(np.median(ms)),
-                ms_min=float(np.min(ms)), wall_s=wall)
+    ms = e0.elapsed_time(e1) / steps
+    return dict(ms_mean=float(ms), wall_s=wall)
+
+
+def copy_bandwidth(torch, reps=10):
+    """Device-to-device copy of 1 GiB (read + write bytes per second), for context."""
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / reps / 1e3
+    del src, dst
+    return 2 * (1 << 30) / s / 1e9
+
+
+def recorded_traffic(kernel_file, record):
+    """HBM traffic of the decode kernel from the committed rocprofv3 counter
+    record, if it was taken on the current kernel source (else None)."""
+    import hashlib
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", record)
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gated_delta_rule_100_amd",
+                       "csrc", kernel_file)
+    try:
+        rec = json.load(open(path))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def bench_prefill(torch, gdr, steps, warmup):
@@ -132,9 +167,9 @@ def bench_prefill(torch, gdr, steps, warmup):
 
 def cpu_baseline(budget_s):
     """The fp64 oracle (token-by-token recurrence, OpenMP over (sequence, head))
-    on the host cores: the whole decode workload, repeated until about
-    budget_s/2 of work, and a sample of the prefill workload (whole sequences of
-    a subset of heads) for about budget_s/2."""
+    on the host cores: the whole decode workload repeated for about half the
+    budget, and whole 4096-token sequences of the prefill workload (every
+    (sequence, head) pair costs the same) for about the other half."""
     import oracle
     from gdr_synth import workload
     threads = oracle.max_threads()
@@ -145,34 +180,43 @@ def cpu_baseline(budget_s):
         oracle.recurrent(d1["q"], d1["k"], d1["v"], d1["g"], d1["beta"], d1["cu_seqlens"],
                          d1["state0"])
         reps += 1
-        if time.perf_counter() - t0 > budget_s / 2 or reps >= 50:
+        if time.perf_counter() - t0 > budget_s / 2 or reps >= 500:
             break
     dec_s = (time.perf_counter() - t0) / reps
-    d2 = workload(2, H=4)
-    # whole 4096-token sequences; every (sequence, head) pair costs the same
-    pairs = [(n, h) for n in range(PRE_B) for h in range(4)]
+    del d1
+    d2 = workload(2)
+    pairs = [(n, h) for n in range(PRE_B) for h in range(PRE_H)]
     t0 = time.perf_counter()
     done = 0
-    for i in range(0, len(pairs), max(threads, 1)):
-        chunk_pairs = pairs[i:i + max(threads, 1)]
+    while done < len(pairs):
+        batch = pairs[done:done + max(threads, 1)]
         oracle.recurrent(d2["q"], d2["k"], d2["v"], d2["g"], d2["beta"], d2["cu_seqlens"],
-                         d2["state0"], pairs=chunk_pairs)
-        done += len(chunk_pairs)
+                         d2["state0"], pairs=batch)
+        done += len(batch)
         if time.perf_counter() - t0 > budget_s / 2:
             break
     pre_s = time.perf_counter() - t0
-    tok_heads_per_s = done * PRE_T / pre_s
     return {
-        "value": DEC_STATE_BYTES / dec_s / 1e9,
+        "value": round(DEC_STATE_BYTES / dec_s / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"fp64 recurrence over the whole decode workload (64x32 states, d=128), "
-                  f"{reps} repetition(s), {dec_s * 1e3:.1f} ms each; prefill sample: {done} "
+        "sample": f"fp64 token-by-token recurrence: the whole decode workload (64x32 states, "
+                  f"d=128) {reps} time(s), {dec_s * 1e3:.1f} ms each; prefill: {done} of the 64 "
                   f"(sequence, head) pairs of 4096 tokens in {pre_s:.1f} s",
-        "prefill_tokens_per_s": tok_heads_per_s / PRE_H,
-        "cpu": platform.processor() or platform.machine(),
+        "prefill_tokens_per_s": round(done * PRE_T / pre_s / PRE_H, 1),
+        "cpu": _cpu_model(),
     }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def main():
@@ -193,6 +237,8 @@ def main():
     print(f"[bench] decode {dec}", file=sys.stderr, flush=True)
     pre = bench_prefill(torch, gdr, args.steps, args.warmup)
     print(f"[bench] prefill {pre}", file=sys.stderr, flush=True)
+    copy_gbs = copy_bandwidth(torch)
+    print(f"[bench] device copy {copy_gbs:.1f} GB/s", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_seconds)
@@ -221,6 +267,7 @@ def main():
                                "dk=dv=128 C=64 bf16",
                    "decode_ms": round(dec["ms_mean"], 5), "prefill_ms": round(pre["ms_mean"], 5)},
         "pct_hbm_peak": round(100.0 * dec_gbs / HBM_PEAK_GBS, 2),
+        "device_copy_gbs": round(copy_gbs, 1),
         "prefill": {
             "value": round(PRE_TOKENS / pre_s, 1), "unit": "tokens/s",
             "ms": round(pre["ms_mean"], 4),
@@ -230,7 +277,8 @@ def main():
         "roofline": {
             "bound": "hbm", "kernel": "decode_kernel<128,128,bf16,bf16>",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic("decode.hip", "decode_N64_H32_d128_traffic.json"),
         },
         "cpu_baseline": cpu,
     }

@@ -8,8 +8,9 @@
 //     vectors, so one wave-wide load covers four contiguous row segments of
 //     256 bytes -- fully used 128-byte lines;
 //   * every load of the state is issued before any arithmetic (64 KiB per
-//     workgroup in flight), the rank-1 update happens in registers and the
-//     rows are stored back in place; no LDS (the state has no reuse -- the
+//     workgroup in flight), non-temporal (the state is touched once), the
+//     rank-1 update happens in registers and the rows are stored back in
+//     place; no LDS (the state has no reuse -- the
 //     register-direct load of the FlashInfer PR #7156 page, code analysis 1);
 //   * the two row dot products (s.k before the update, s'.q after) are
 //     16-lane DPP reductions.
@@ -41,15 +42,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   const int lane16 = threadIdx.x & (LPR - 1);
   const int rg = threadIdx.x / LPR;
 
-  float4* S = reinterpret_cast<float4*>(state + static_cast<size_t>(pair) * DV * DK);
+  floatx4* S = reinterpret_cast<floatx4*>(state + static_cast<size_t>(pair) * DV * DK);
 
-  // Issue every state load first.
-  float4 st[RPT][VEC];
+  // Issue every state load first.  The state is touched exactly once, so the
+  // loads and stores are non-temporal (they do not displace reusable lines).
+  floatx4 st[RPT][VEC];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int row = rg + RG * i;
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) st[i][j] = S[(row * DK + 4 * lane16 + 64 * j) / 4];
+    for (int j = 0; j < VEC; ++j)
+      st[i][j] = __builtin_nontemporal_load(&S[(row * DK + 4 * lane16 + 64 * j) / 4]);
   }
 
   float kk[VEC][4], qq[VEC][4], vv[RPT];
@@ -70,20 +73,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     float a = 0.f;
 #pragma unroll
     for (int j = 0; j < VEC; ++j)
-      a += st[i][j].x * kk[j][0] + st[i][j].y * kk[j][1] + st[i][j].z * kk[j][2] +
-           st[i][j].w * kk[j][3];
+      a += st[i][j][0] * kk[j][0] + st[i][j][1] * kk[j][1] + st[i][j][2] * kk[j][2] +
+           st[i][j][3] * kk[j][3];
     a = row16_sum(a);
     const float u = b * (vv[i] - alpha * a);
     float p = 0.f;
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
-      float4 s = st[i][j];
-      s.x = alpha * s.x + u * kk[j][0];
-      s.y = alpha * s.y + u * kk[j][1];
-      s.z = alpha * s.z + u * kk[j][2];
-      s.w = alpha * s.w + u * kk[j][3];
+      floatx4 s = st[i][j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] = alpha * s[e] + u * kk[j][e];
       st[i][j] = s;
-      p += s.x * qq[j][0] + s.y * qq[j][1] + s.z * qq[j][2] + s.w * qq[j][3];
+      p += s[0] * qq[j][0] + s[1] * qq[j][1] + s[2] * qq[j][2] + s[3] * qq[j][3];
     }
     oi[i] = row16_sum(p);
   }
@@ -92,7 +93,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   for (int i = 0; i < RPT; ++i) {
     const int row = rg + RG * i;
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) S[(row * DK + 4 * lane16 + 64 * j) / 4] = st[i][j];
+    for (int j = 0; j < VEC; ++j)
+      __builtin_nontemporal_store(st[i][j], &S[(row * DK + 4 * lane16 + 64 * j) / 4]);
   }
   // lane i of each row group writes the output of its i-th row
 #pragma unroll
