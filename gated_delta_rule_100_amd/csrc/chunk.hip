@@ -146,6 +146,12 @@ struct ChunkWork {
 
   __device__ size_t tok_off(int t) const { return (static_cast<size_t>(tok0 + t) * H + h) * D; }
 
+  // 8 consecutive features of token row t (zeros past the chunk) as planes.
+  __device__ void row_frag(const void* base, int t, int k0, bf16x8 (&out)[PI]) const {
+    const bool ok = t < c;
+    load_global8<IN, PI>(base, ok ? tok_off(t) + k0 : 0, ok, out);
+  }
+
   // Row fragments (8 consecutive features of one token row) of every chunk
   // row, for the Gram products; zeros past the chunk.
   __device__ void rows_frags(const void* base, bf16x8 (&f)[NT][KB][PI]) const {
@@ -458,7 +464,7 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
 }
 
 template <int D, int C, Dt IN, Dt OUTD>
-__global__ __launch_bounds__(256) void chunk_out_kernel(
+__global__ __launch_bounds__(256, 2) void chunk_out_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ cidx, const float* __restrict__ state_in,
@@ -473,9 +479,8 @@ __global__ __launch_bounds__(256) void chunk_out_kernel(
 
   W_ w;
   w.init(smem, ct.tok0, ct.c, h, H);
-  bf16x8 qf[NT][KB][PI];
   {
-    bf16x8 kf[NT][KB][PI];
+    bf16x8 kf[NT][KB][PI], qf[NT][KB][PI];
     w.rows_frags(k, kf);
     w.rows_frags(q, qf);
     w.load(k, v, g, beta);
@@ -540,15 +545,18 @@ __global__ __launch_bounds__(256) void chunk_out_kernel(
     }
   }
 
-  // O = diag(gamma) Q S0^T + P U
+  // O = diag(gamma) Q S0^T + P U  (Q fragments re-read: cheaper than holding them)
   floatx4 Oacc[NT][DPW];
 #pragma unroll
   for (int a = 0; a < NT; ++a) {
+    bf16x8 qa[KB][PI];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) w.row_frag(q, 16 * a + w.c16, 32 * kb + 8 * w.g4, qa[kb]);
 #pragma unroll
     for (int bb = 0; bb < DPW; ++bb) {
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) mma_planes<PI, PT>(acc, qf[a][kb], SB[bb][kb]);
+      for (int kb = 0; kb < KB; ++kb) mma_planes<PI, PT>(acc, qa[kb], SB[bb][kb]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) Oacc[a][bb][e] = w.sgam[16 * a + 4 * w.g4 + e] * acc[e];
     }

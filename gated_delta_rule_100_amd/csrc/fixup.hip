@@ -130,8 +130,9 @@ __global__ __launch_bounds__(2 * DK) void fixup_kernel(const float* __restrict__
   }
 }
 
-// Matrix-core fixup: 16 state rows per workgroup (one 16-row MFMA tile) and
-// one wave per 16-wide output column tile (8 waves at d = 128).  Per chunk:
+// Matrix-core fixup: ROWS state rows per workgroup (16, 32 or 64: one to four
+// 16-row MFMA tiles) and one wave per 16-wide output column tile (8 waves at
+// d = 128).  Per chunk:
 // S' = S M_c + L_c with S as bf16 planes in LDS (double-buffered, so one
 // barrier per chunk).  M is read transposed (row b of a slot holds column b
 // of M_c), so lane (c, g) of the B operand -- M[32kb + 8g .. 8g+7][16w + c] --
@@ -157,18 +158,19 @@ __global__ __launch_bounds__(2 * DK) void fixup_kernel(const float* __restrict__
 constexpr int kXcds = 8;
 enum FixMode { kSeq = 0, kCompose = 1, kApply = 2 };
 
-template <int D, int P, int MODE>
+template <int D, int P, int MODE, int ROWS>
 __global__ __launch_bounds__(D * 4) void fixup_mfma_kernel(
     const float* __restrict__ L, const float* __restrict__ Mt, const float* __restrict__ state_in,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ seg_idx, int seg,
     const float* __restrict__ seg_start, float* __restrict__ out, float* __restrict__ out_mt,
     int n_chunks, int H, int n_units) {
   constexpr int NTHR = D * 4;       // one wave per 16 output columns
-  constexpr int RB = D / 16;        // row blocks (workgroups) per state
+  constexpr int RT = ROWS / 16;     // 16-row MFMA tiles per workgroup
+  constexpr int RB = D / ROWS;      // row blocks (workgroups) per state
   constexpr int RBU = MODE == kCompose ? 2 * RB : RB;  // row blocks per unit
   constexpr int KB = D / 32;        // 32-deep contraction blocks
   constexpr int LDS_LD = D + 8;     // row stride of the state planes (bf16 elements)
-  constexpr int PS = 16 * LDS_LD;   // plane stride
+  constexpr int PS = ROWS * LDS_LD; // plane stride
   __shared__ __align__(16) uint16_t s_planes[2][P * PS];
 
   // XCD-aware placement of (unit x head, row block)
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(D * 4) void fixup_mfma_kernel(
   if (pair >= n_units * H) return;
   const int u = pair / H, h = pair % H;
   const bool trans_rows = MODE == kCompose && rbu >= RB;  // transfer-product rows
-  const int row0 = (rbu % RB) * 16;
+  const int row0 = (rbu % RB) * ROWS;
 
   int n, c_begin, c_end, sidx = 0;
   if (MODE == kSeq) {
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(D * 4) void fixup_mfma_kernel(
   }
   const bool from_L = !trans_rows && init == nullptr;
   int start = from_L ? c_begin + 1 : c_begin;
-  for (int idx = tid; idx < 16 * D; idx += NTHR) {
+  for (int idx = tid; idx < ROWS * D; idx += NTHR) {
     const int i = idx / D, cc = idx % D;
     float x;
     if (trans_rows) {
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(D * 4) void fixup_mfma_kernel(
   __syncthreads();
 
   typedef float4 MRaw[KB][2];
-  typedef float LRaw[4];
+  typedef float LRaw[RT][4];
   // Loads are unconditional (a chunk past the end re-reads the last one).
   auto fetch = [&](int c, MRaw& m, LRaw& l) {
     c = c < c_end ? c : c_end - 1;
@@ -246,14 +248,17 @@ __global__ __launch_bounds__(D * 4) void fixup_mfma_kernel(
       m[kb][1] = src[8 * kb + 1];
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) l[e] = trans_rows ? 0.f : L[st_at(c, 4 * g4 + e, col)];
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        l[r][e] = trans_rows ? 0.f : L[st_at(c, 16 * r + 4 * g4 + e, col)];
   };
 
   MRaw m;
   LRaw l;
   fetch(start, m, l);
   int buf = 0;
-  float last[4] = {0.f, 0.f, 0.f, 0.f};
+  float last[RT][4] = {};
   for (int c = start; c < c_end; ++c) {
     bf16x8 mb[KB][P];
 #pragma unroll
@@ -262,33 +267,44 @@ __global__ __launch_bounds__(D * 4) void fixup_mfma_kernel(
                           m[kb][1].x, m[kb][1].y, m[kb][1].z, m[kb][1].w};
       split8<P>(x, mb[kb]);
     }
-    float lc[4];
+    float lc[RT][4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) lc[e] = l[e];
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lc[r][e] = l[r][e];
     // Keep the next loads below the conversion (the raw registers are free again).
     __builtin_amdgcn_sched_barrier(0);
     fetch(c + 1, m, l);  // next chunk's operands are in flight during this one
 
     // S' tile = S M_c: two accumulators (even / odd k blocks) keep the
     // dependent MFMA chains short.
-    floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    floatx4 acc[RT][2];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[r][0] = acc[r][1] = floatx4{0.f, 0.f, 0.f, 0.f};
     const uint16_t* cur = s_planes[buf];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      bf16x8 sa[P];
-      load_lds8<P>(cur + c16 * LDS_LD + 32 * kb + 8 * g4, PS, sa);
-      mma_planes<P, P>((kb & 1) ? acc1 : acc0, sa, mb[kb]);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        bf16x8 sa[P];
+        load_lds8<P>(cur + (16 * r + c16) * LDS_LD + 32 * kb + 8 * g4, PS, sa);
+        mma_planes<P, P>(acc[r][kb & 1], sa, mb[kb]);
+      }
     }
     uint16_t* nxt = s_planes[buf ^ 1];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x = (acc0[e] + acc1[e]) + lc[e];
-      last[e] = x;
-      if (MODE != kCompose) out[st_at(c, 4 * g4 + e, col)] = x;
-      uint16_t sp[P];
-      split_planes<P>(x, sp);
+    for (int r = 0; r < RT; ++r) {
 #pragma unroll
-      for (int p = 0; p < P; ++p) nxt[p * PS + (4 * g4 + e) * LDS_LD + col] = sp[p];
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * r + 4 * g4 + e;
+        const float x = (acc[r][0][e] + acc[r][1][e]) + lc[r][e];
+        last[r][e] = x;
+        if (MODE != kCompose) out[st_at(c, row, col)] = x;
+        uint16_t sp[P];
+        split_planes<P>(x, sp);
+#pragma unroll
+        for (int p = 0; p < P; ++p) nxt[p * PS + row * LDS_LD + col] = sp[p];
+      }
     }
     buf ^= 1;
     __syncthreads();
@@ -296,26 +312,23 @@ __global__ __launch_bounds__(D * 4) void fixup_mfma_kernel(
 
   if (MODE == kCompose) {
     // Final rows of the segment: L_s rows in state layout, M_s transposed.
-    if (start >= c_end) {  // a one-chunk segment: L_s = L of that chunk, M_s = its M
+    if (start >= c_end) {  // a one-chunk segment without transfer rows: L_s = L of that chunk
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g4 + e;
-        if (trans_rows) {
-          const float* Mc = Mt + (static_cast<size_t>(c_begin) * H + h) * D * D;
-          last[e] = Mc[static_cast<size_t>(col) * D + row0 + r];
-        } else {
-          last[e] = L[st_at(c_begin, r, col)];
-        }
-      }
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) last[r][e] = L[st_at(c_begin, 16 * r + 4 * g4 + e, col)];
     }
     const size_t base = (static_cast<size_t>(u) * H + h) * D * D;
-    if (trans_rows) {
-      *reinterpret_cast<float4*>(out_mt + base + static_cast<size_t>(col) * D + row0 + 4 * g4) =
-          make_float4(last[0], last[1], last[2], last[3]);
-    } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        out[base + static_cast<size_t>(row0 + 4 * g4 + e) * D + col] = last[e];
+    for (int r = 0; r < RT; ++r) {
+      const int row = row0 + 16 * r + 4 * g4;
+      if (trans_rows) {
+        *reinterpret_cast<float4*>(out_mt + base + static_cast<size_t>(col) * D + row) =
+            make_float4(last[r][0], last[r][1], last[r][2], last[r][3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[base + static_cast<size_t>(row + e) * D + col] = last[r][e];
+      }
     }
   }
 }
@@ -352,11 +365,24 @@ hipError_t launch_fixup_mode(int mode, const float* L, const float* Mt, const fl
                              int H, int n_units, int dk, int planes, hipStream_t stream) {
   if (n_units <= 0) return hipSuccess;
   const int pairs = n_units * H;
-  const int rbu = (dk / 16) * (mode == kCompose ? 2 : 1);
+  // Every workgroup moves a whole M_c from L2 into its CU per chunk, so more
+  // rows per workgroup means less traffic per row; take the most rows that
+  // still give every CU a workgroup.
+  const int copies = mode == kCompose ? 2 : 1;
+  int rows = 16;
+  while (rows < 64 && rows < dk && static_cast<int64_t>(pairs) * copies * (dk / (2 * rows)) >= 256)
+    rows *= 2;
+  const int rbu = (dk / rows) * copies;
   const dim3 grid(kXcds * ((pairs + kXcds - 1) / kXcds) * rbu);
-#define GDR_FIX(D_, P_, M_)                                                                     \
-  hipLaunchKernelGGL((fixup_mfma_kernel<D_, P_, M_>), grid, dim3(D_ * 4), 0, stream, L, Mt,      \
+#define GDR_FIX_R(D_, P_, M_, R_)                                                               \
+  hipLaunchKernelGGL((fixup_mfma_kernel<D_, P_, M_, R_>), grid, dim3(D_ * 4), 0, stream, L, Mt,  \
                      state_in, offs, seg_idx, seg, seg_start, out, out_mt, n_chunks, H, n_units)
+#define GDR_FIX(D_, P_, M_)                                                                     \
+  do {                                                                                          \
+    if (rows == 64) GDR_FIX_R(D_, P_, M_, 64);                                                  \
+    else if (rows == 32) GDR_FIX_R(D_, P_, M_, 32);                                             \
+    else GDR_FIX_R(D_, P_, M_, 16);                                                             \
+  } while (0)
 #define GDR_FIX_P(D_, M_)                                                                       \
   do {                                                                                          \
     if (planes == 2) GDR_FIX(D_, 2, M_); else GDR_FIX(D_, 3, M_);                               \
@@ -371,6 +397,7 @@ hipError_t launch_fixup_mode(int mode, const float* L, const float* Mt, const fl
 #undef GDR_FIX_M
 #undef GDR_FIX_P
 #undef GDR_FIX
+#undef GDR_FIX_R
   return hipGetLastError();
 }
 

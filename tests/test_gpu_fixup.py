@@ -30,15 +30,18 @@ def oracle_locals(d, chunk):
 
 
 @pytest.mark.parametrize("with_state", [True, False])
-@pytest.mark.parametrize("d_", [64, 128])
-def test_fixup_matches_oracle(with_state, d_):
+@pytest.mark.parametrize("d_,H,lens", [(64, 2, [700, 0, 130, 64, 1]),
+                                       (128, 2, [700, 0, 130, 64, 1]),
+                                       (128, 64, [200, 65]),     # 32 rows per workgroup
+                                       (128, 128, [130])])       # 64 rows per workgroup
+def test_fixup_matches_oracle(with_state, d_, H, lens):
     import gated_delta_rule_100_amd as gdr
     chunk = 64 if d_ == 128 else 16
-    d = generate([700, 0, 130, 64, 1], 2, d_, d_, dtype="f32", state0=True, seed=300 + d_,
+    d = generate(lens, H, d_, d_, dtype="f32", state0=True, seed=300 + d_ + H,
                  gate="slow")
     offs, L, M = oracle_locals(d, chunk)
     s0 = d["state0"].astype(np.float64) if with_state else None
-    say(f"fixup d={d_} chunk={chunk} with_state={with_state} n_chunks={L.shape[0]}")
+    say(f"fixup d={d_} H={H} chunk={chunk} with_state={with_state} n_chunks={L.shape[0]}")
     Lg = torch.from_numpy(L.astype(np.float32)).cuda()
     # the fixup takes M transposed: slot[c][h][b][a] = M_c[a][b]
     Mg = torch.from_numpy(np.ascontiguousarray(M.astype(np.float32).transpose(0, 1, 3, 2))).cuda()

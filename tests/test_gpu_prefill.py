@@ -74,6 +74,9 @@ CASES = {
     "d64-C64-bf16": (2, dict(seqlens=[150, 64, 3], H=3, dk=64, dv=64, gate="slow")),
     "d128-C16-bf16": (2, dict(seqlens=[70, 33], H=2, chunk=16, gate="slow")),
     "d128-C16-f32": (0, dict(seqlens=[40, 17, 0], H=2, dk=128, dv=128, gate="slow", state0=True)),
+    # many (sequence, head) pairs: the fixup takes 32 and 64 state rows per workgroup
+    "many-heads-H64-rows32": (2, dict(seqlens=[150, 70], H=64, gate="slow")),
+    "many-heads-H128-rows64": (2, dict(seqlens=[100], H=128, gate="slow")),
 }
 
 
