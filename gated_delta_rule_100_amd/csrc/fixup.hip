@@ -254,30 +254,34 @@ __global__ __launch_bounds__(D * 4) void fixup_mfma_kernel(
         l[r][e] = trans_rows ? 0.f : L[st_at(c, 16 * r + 4 * g4 + e, col)];
   };
 
+  // Raw operands of chunk c+1 are loaded at the top of iteration c and turned
+  // into planes at its end, after the barrier: the loaded registers never
+  // cross the loop back-edge, so nothing has to wait for them early.
   MRaw m;
   LRaw l;
-  fetch(start, m, l);
-  int buf = 0;
-  float last[RT][4] = {};
-  for (int c = start; c < c_end; ++c) {
-    bf16x8 mb[KB][P];
+  bf16x8 mb[KB][P];
+  float lc[RT][4];
+  auto convert = [&]() {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const float x[8] = {m[kb][0].x, m[kb][0].y, m[kb][0].z, m[kb][0].w,
                           m[kb][1].x, m[kb][1].y, m[kb][1].z, m[kb][1].w};
       split8<P>(x, mb[kb]);
     }
-    float lc[RT][4];
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
       for (int e = 0; e < 4; ++e) lc[r][e] = l[r][e];
-    // Keep the next loads below the conversion (the raw registers are free again).
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  fetch(start, m, l);
+  convert();
+  int buf = 0;
+  float last[RT][4] = {};
+  for (int c = start; c < c_end; ++c) {
     fetch(c + 1, m, l);  // next chunk's operands are in flight during this one
 
-    // S' tile = S M_c: two accumulators (even / odd k blocks) keep the
-    // dependent MFMA chains short.
+    // S' tiles = S M_c: two accumulators per tile (even / odd k blocks) keep
+    // the dependent MFMA chains short.
     floatx4 acc[RT][2];
 #pragma unroll
     for (int r = 0; r < RT; ++r) acc[r][0] = acc[r][1] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -308,6 +312,7 @@ __global__ __launch_bounds__(D * 4) void fixup_mfma_kernel(
     }
     buf ^= 1;
     __syncthreads();
+    convert();
   }
 
   if (MODE == kCompose) {
