@@ -111,6 +111,30 @@ size_t seg_workspace(const SegSizes& z, int N) {
          align_up(sizeof(int32_t) * 2 * static_cast<size_t>(z.max_segs)) + 3 * align_up(z.state_bytes);
 }
 
+size_t layout_workspace(int N, int mc) {
+  return align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1)) +
+         align_up(sizeof(int32_t) * 2 * static_cast<size_t>(mc));
+}
+
+size_t scan_workspace(int mc, int H, int d, int chunk) {
+  const gdr::ChunkFactorSizes z = gdr::chunk_factor_sizes(mc, H, d, chunk);
+  return align_up(z.w) + align_up(z.q) + align_up(z.kt) + align_up(z.p) + align_up(z.ut) +
+         align_up(z.gate);
+}
+
+// Schedule of gdr_chunk_prefill.  The sequential scan (scan.hip) keeps every
+// state in registers for a whole sequence and forms neither L, M nor the
+// per-chunk states; it takes bf16 inputs and chunk 64.  The chunk-parallel
+// form (chunk-local L and M, fixup, chunk outputs) serves requests for L or M,
+// fp32 inputs, chunk 16, and long sequences at low parallelism, where one
+// dependent chain per (sequence, head) would leave the GPU idle (the case the
+// two-level fixup is for).
+bool use_scan(const float* L_out, const float* M_out, int T_total, int N, int H, int chunk,
+              int in_dtype) {
+  return !L_out && !M_out && in_dtype == GDR_BF16 && chunk == 64 &&
+         fixup_segment(T_total, N, H, chunk) == 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -172,14 +196,14 @@ gdr_status gdr_chunk_layout(const int32_t* cu_seqlens, int N, int chunk, int32_t
 size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int dv, int chunk) {
   const int mc = gdr_max_chunks(T_total, N, chunk);
   if (mc < 0 || H <= 0 || !supported_dims(dk, dv)) return 0;
-  size_t bytes = align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1));
-  bytes += align_up(sizeof(int32_t) * 2 * static_cast<size_t>(mc));
+  size_t cp = 0;
   const size_t per = static_cast<size_t>(mc) * H * sizeof(float);
-  bytes += align_up(per * dv * dk);  // L
-  bytes += align_up(per * dk * dk);  // M
-  bytes += align_up(per * dv * dk);  // fixed
-  bytes += seg_workspace(seg_sizes(T_total, N, H, dk, chunk, mc), N);
-  return bytes;
+  cp += align_up(per * dv * dk);  // L
+  cp += align_up(per * dk * dk);  // M
+  cp += align_up(per * dv * dk);  // fixed
+  cp += seg_workspace(seg_sizes(T_total, N, H, dk, chunk, mc), N);
+  const size_t sc = chunk == 64 ? scan_workspace(mc, H, dk, chunk) : 0;
+  return layout_workspace(N, mc) + (cp > sc ? cp : sc);
 }
 
 gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
@@ -210,15 +234,21 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
   if (static_cast<int64_t>(T_total) * H > INT32_MAX || static_cast<int64_t>(mc) * H > INT32_MAX)
     return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: T_total*H too large");
 
-  // workspace carve-up: offsets | indices | [L] | [M] | [fixed]
+  // workspace carve-up: offsets | indices | factors (sequential scan), or
+  // offsets | indices | [L] | [M] | [fixed] | [segments] (chunk-parallel form)
+  const bool scan = use_scan(L_out, M_out, T_total, N, H, chunk, in_dtype);
   const size_t per = static_cast<size_t>(mc) * H * sizeof(float);
-  size_t need = align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1)) +
-                align_up(sizeof(int32_t) * 2 * static_cast<size_t>(mc));
-  if (!L_out) need += align_up(per * dv * dk);
-  if (!M_out) need += align_up(per * dk * dk);
-  if (!fixed_out) need += align_up(per * dv * dk);
-  const SegSizes segz = seg_sizes(T_total, N, H, dk, chunk, mc);
-  need += seg_workspace(segz, N);
+  size_t need = layout_workspace(N, mc);
+  SegSizes segz;
+  if (scan) {
+    need += scan_workspace(mc, H, dk, chunk);
+  } else {
+    if (!L_out) need += align_up(per * dv * dk);
+    if (!M_out) need += align_up(per * dk * dk);
+    if (!fixed_out) need += align_up(per * dv * dk);
+    segz = seg_sizes(T_total, N, H, dk, chunk, mc);
+    need += seg_workspace(segz, N);
+  }
   if (workspace_bytes < need || (!workspace && need > 0))
     return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: workspace of %zu bytes, need %zu", workspace_bytes, need);
   gdr_status s = check_device();
@@ -229,6 +259,34 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
   ws += align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1));
   int32_t* cidx = reinterpret_cast<int32_t*>(ws);
   ws += align_up(sizeof(int32_t) * 2 * static_cast<size_t>(mc));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = gdr::launch_layout(cu_seqlens, N, chunk, offs, cidx, mc, st);
+  if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: layout");
+
+  if (scan) {
+    const gdr::ChunkFactorSizes z = gdr::chunk_factor_sizes(mc, H, dk, chunk);
+    gdr::ChunkFactors f;
+    f.w = reinterpret_cast<uint16_t*>(ws);
+    ws += align_up(z.w);
+    f.q = reinterpret_cast<uint16_t*>(ws);
+    ws += align_up(z.q);
+    f.kt = reinterpret_cast<uint16_t*>(ws);
+    ws += align_up(z.kt);
+    f.p = reinterpret_cast<uint16_t*>(ws);
+    ws += align_up(z.p);
+    f.ut = reinterpret_cast<float*>(ws);
+    ws += align_up(z.ut);
+    f.gate = reinterpret_cast<float*>(ws);
+    if (T_total > 0) {
+      e = gdr::launch_chunk_factors(q, k, v, g, beta, cu_seqlens, cidx, f, mc, T_total, H, dk,
+                                    chunk, st);
+      if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: chunk factors");
+    }
+    e = gdr::launch_chunk_scan(cu_seqlens, offs, f, state_in, state_out, fixed_out, o, N, H, dk,
+                               chunk, mc, T_total, out_dtype, st);
+    return hip_status(e, "gdr_chunk_prefill: chunk scan");
+  }
+
   float* L = L_out;
   if (!L) { L = reinterpret_cast<float*>(ws); ws += align_up(per * dv * dk); }
   float* M = M_out;
@@ -251,9 +309,6 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
     ws += align_up(segz.state_bytes);
   }
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = gdr::launch_layout(cu_seqlens, N, chunk, offs, cidx, mc, st);
-  if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: layout");
   if (T_total > 0) {
     e = gdr::launch_chunk_local(k, v, g, beta, cu_seqlens, cidx, L, M, mc, T_total, H, dk, dv,
                                 chunk, in_dtype, st);

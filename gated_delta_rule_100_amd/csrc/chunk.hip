@@ -592,6 +592,128 @@ __global__ __launch_bounds__(256, 2) void chunk_out_kernel(
   }
 }
 
+// Per-chunk factors of the sequential schedule (bf16 inputs): the same
+// intra-chunk solve as above, but instead of L and M the chunk hands over
+// W (as two bf16 planes), Ut^T, Q, K^T, P = (Q K^T) (.) Gamma (two planes) and
+// the gates gamma_t, D_t, each laid out the way the scan kernel stages it.
+// With these, the state update S_end = S0 M + L is applied in factored form,
+//   S_end = gamma_C S0 + (Ut - W S0^T)^T diag(D) K,
+// so no dk x dk matrix is formed.
+//
+// The rows of W, Q, K^T and P are the A operands of the scan's products; their
+// contraction index is stored in operand-slot order: inside every 32-wide
+// block, lane group g's eight slots (elements 4g..4g+3 and 16+4g..16+4g+3,
+// the order in which D tiles stack, mfma_planes.h) are adjacent, so that the
+// scan reads each fragment with one 16-byte load.
+template <int D, int C>
+__global__ __launch_bounds__(256, 2) void chunk_factors_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ cidx, ChunkFactors f, int H, int T_total) {
+  using W_ = ChunkWork<D, C, Dt::BF16, true>;
+  using Cfg = typename W_::Cfg;
+  constexpr int PT = Cfg::PT, NT = Cfg::NT, DPW = Cfg::DPW, KB = Cfg::KB;
+  static_assert(PT == 2 && Cfg::Cp == C, "factored form: bf16 inputs, C >= 32");
+  __shared__ __align__(16) unsigned char smem[Cfg::BYTES];
+  // Chunks are produced last-first: the scan reads them first-first, so the
+  // earliest chunks are the most recently written (and still cache-resident)
+  // when it starts.
+  const int cid = gridDim.x - 1 - blockIdx.x, h = blockIdx.y;
+  const ChunkTokens ct = chunk_tokens(cu, cidx, cid, C, T_total);
+  if (ct.c <= 0) return;
+
+  W_ w;
+  w.init(smem, ct.tok0, ct.c, h, H);
+  {
+    bf16x8 kf[NT][KB][1], qf[NT][KB][1];
+    w.rows_frags(k, kf);
+    w.rows_frags(q, qf);
+    w.load(k, v, g, beta);
+    w.gram_kk(kf);
+    w.gram_qk(qf, kf);
+  }
+  __syncthreads();
+  w.invert_diagonal();
+
+  floatx4 Wacc[NT][DPW], Uacc[NT][DPW];
+  w.solve_wy(Wacc, Uacc);
+
+  const size_t slot = static_cast<size_t>(cid) * H + h;
+  // Row chunk n8 (16 bytes) of an operand row in slot order is made of the
+  // 4-element groups starting at 32 (n8/4) + 4 (n8%4) and 16 elements later.
+  auto slot_chunk = [](const uint16_t* row, int n8) {
+    const int c0 = 32 * (n8 >> 2) + 4 * (n8 & 3);
+    const uint2 lo = *reinterpret_cast<const uint2*>(row + c0);
+    const uint2 hi = *reinterpret_cast<const uint2*>(row + c0 + 16);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  };
+  // Ut^T: row v holds the chunk's column v of Ut (one float4 per D-tile row group).
+  float* ut = f.ut + slot * D * C;
+#pragma unroll
+  for (int a = 0; a < NT; ++a)
+#pragma unroll
+    for (int bb = 0; bb < DPW; ++bb) {
+      const int vrow = 16 * (w.wave + 4 * bb) + w.c16;
+      *reinterpret_cast<floatx4*>(ut + static_cast<size_t>(vrow) * C + 16 * a + 4 * w.g4) =
+          Uacc[a][bb];
+    }
+  if (w.tid < C) {
+    f.gate[slot * 2 * C + w.tid] = w.sgam[w.tid];
+    f.gate[slot * 2 * C + C + w.tid] = w.sD[w.tid];
+  }
+  // Q rows (zero past the chunk), K^T and the P planes, in slot order.
+  uint16_t* qg = f.q + slot * C * D;
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
+  for (int idx = w.tid; idx < C * D / 8; idx += 256) {
+    const int t = idx / (D / 8), n8 = idx % (D / 8);
+    *reinterpret_cast<uint4*>(qg + t * D + 8 * n8) =
+        t < ct.c ? slot_chunk(q16 + w.tok_off(t), n8) : make_uint4(0, 0, 0, 0);
+  }
+  uint16_t* kt = f.kt + slot * D * C;
+  for (int idx = w.tid; idx < D * C / 8; idx += 256) {
+    const int j = idx / (C / 8), n8 = idx % (C / 8);
+    *reinterpret_cast<uint4*>(kt + j * C + 8 * n8) = slot_chunk(w.Kt() + j * Cfg::LDC, n8);
+  }
+  uint16_t* pg = f.p + slot * PT * C * C;
+  for (int idx = w.tid; idx < PT * C * C / 8; idx += 256) {
+    const int pl = idx / (C * C / 8), r = idx % (C * C / 8);
+    const int t = r / (C / 8), n8 = r % (C / 8);
+    *reinterpret_cast<uint4*>(pg + (pl * C + t) * C + 8 * n8) =
+        slot_chunk(w.Pp() + pl * Cfg::P_PS + t * Cfg::LDP, n8);
+  }
+  __syncthreads();  // K^T and V^T are consumed; W planes take their place
+#pragma unroll
+  for (int a = 0; a < NT; ++a)
+#pragma unroll
+    for (int bb = 0; bb < DPW; ++bb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * a + 4 * w.g4 + e, d = 16 * (w.wave + 4 * bb) + w.c16;
+        uint16_t sp[PT];
+        split_planes<PT>(Wacc[a][bb][e], sp);
+#pragma unroll
+        for (int p = 0; p < PT; ++p) w.Wp()[p * Cfg::W_PS + t * Cfg::LDD + d] = sp[p];
+      }
+  __syncthreads();
+  uint16_t* wg = f.w + slot * PT * C * D;
+  for (int idx = w.tid; idx < PT * C * D / 8; idx += 256) {
+    const int pl = idx / (C * D / 8), r = idx % (C * D / 8);
+    const int t = r / (D / 8), n8 = r % (D / 8);
+    *reinterpret_cast<uint4*>(wg + (pl * C + t) * D + 8 * n8) =
+        slot_chunk(w.Wp() + pl * Cfg::W_PS + t * Cfg::LDD, n8);
+  }
+}
+
+template <int D, int C>
+hipError_t factors_t(const void* q, const void* k, const void* v, const float* g,
+                     const float* beta, const int32_t* cu, const int32_t* cidx,
+                     const ChunkFactors& f, int max_chunks, int T_total, int H,
+                     hipStream_t stream) {
+  hipLaunchKernelGGL((chunk_factors_kernel<D, C>), dim3(max_chunks, H), dim3(256), 0, stream, q,
+                     k, v, g, beta, cu, cidx, f, H, T_total);
+  return hipGetLastError();
+}
+
 template <int D, int C, Dt IN>
 hipError_t local_t(const void* k, const void* v, const float* g, const float* beta,
                    const int32_t* cu, const int32_t* cidx, float* L, float* M, int max_chunks,
@@ -669,6 +791,20 @@ hipError_t launch_chunk_out(const void* q, const void* k, const void* v, const f
   if (dk == 128) GDR_OUT(128, 16, Dt::F32);
   GDR_OUT(64, 16, Dt::F32);
 #undef GDR_OUT
+}
+
+hipError_t launch_chunk_factors(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, const int32_t* cu_seqlens,
+                                const int32_t* chunk_indices, const ChunkFactors& f,
+                                int max_chunks, int T_total, int H, int d, int chunk,
+                                hipStream_t stream) {
+  if (max_chunks <= 0) return hipSuccess;
+  if (chunk != 64) return hipErrorInvalidValue;
+  if (d == 128)
+    return factors_t<128, 64>(q, k, v, g, beta, cu_seqlens, chunk_indices, f, max_chunks, T_total,
+                              H, stream);
+  return factors_t<64, 64>(q, k, v, g, beta, cu_seqlens, chunk_indices, f, max_chunks, T_total, H,
+                           stream);
 }
 
 }  // namespace gdr

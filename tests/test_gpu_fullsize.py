@@ -14,17 +14,21 @@ from gpu_util import dev_inputs, host64, rel_err, say
 pytestmark = pytest.mark.gpu
 
 
-def run_full(d, keep_fixed=False):
+def run_full(d, keep_fixed=False, keep_lm=False):
     import gated_delta_rule_100_amd as gdr
     di = dev_inputs(d)
     T, H, D, N, C = d["T"], d["H"], d["dk"], d["N"], d["chunk"]
     o = torch.empty(T, H, D, dtype=torch.float32, device="cuda")
     sout = torch.empty(N, H, D, D, device="cuda")
-    F = None
+    F = L = M = None
+    mc = gdr.gdr_max_chunks(T, N, C)
     if keep_fixed:
-        F = torch.empty(gdr.gdr_max_chunks(T, N, C), H, D, D, device="cuda")
+        F = torch.empty(mc, H, D, D, device="cuda")
+    if keep_lm:  # asking for L and M selects the chunk-parallel schedule
+        L = torch.empty(mc, H, D, D, device="cuda")
+        M = torch.empty(mc, H, D, D, device="cuda")
     gdr.gdr_chunk_prefill(di["q"], di["k"], di["v"], di["g"], di["beta"], di["cu"], di["state0"],
-                          sout, o, chunk=C, fixed_out=F)
+                          sout, o, chunk=C, L_out=L, M_out=M, fixed_out=F)
     torch.cuda.synchronize()
     return o, sout, F
 
@@ -54,6 +58,13 @@ def test_full_prefill_B4_T4096_H16():
     say("full prefill B=4 T=4096 H=16 d=128 C=64")
     o, sout, _ = run_full(d)
     check_pairs(d, o, sout, [(0, 0), (1, 7), (2, 15), (3, 3)])
+
+
+def test_full_prefill_B4_T4096_H16_chunk_parallel():
+    d = workload(2)
+    say("full prefill B=4 T=4096 H=16 d=128 C=64, chunk-parallel schedule")
+    o, sout, F = run_full(d, keep_fixed=True, keep_lm=True)
+    check_pairs(d, o, sout, [(0, 1), (3, 14)], fixed=F)
 
 
 def test_full_varlen_32768_tokens_H32():

@@ -6,7 +6,13 @@ token-by-token recurrence (o, final states, chunk-end states) and with the
 chunked form's L and M; slow and unit gates make M far from zero so the fixup
 is exercised.  Tolerance: max|gpu - ref| / max|ref| <= 1e-3 for bf16 inputs,
 1e-5 for fp32 inputs, on fp32 outputs; bf16 outputs must equal the
-round-to-nearest-even of the fp32 outputs bit for bit."""
+round-to-nearest-even of the fp32 outputs bit for bit.
+
+Two schedules are covered: the chunk-parallel form (taken whenever L or M is
+requested) and the sequential chunk scan (taken for bf16 inputs at chunk 64
+when neither is requested, unless the sequences are long and few).  Each
+parity case runs both: "cp" asks for L, M and the chunk-end states, "scan"
+for the chunk-end states only, "none" for nothing optional."""
 import numpy as np
 import pytest
 import torch
@@ -18,7 +24,7 @@ from gpu_util import dev_inputs, host64, rel_err, say, tol_for
 pytestmark = pytest.mark.gpu
 
 
-def run_prefill(d, out_dtype=torch.float32, chunk=None, keep=True, state_in="given"):
+def run_prefill(d, out_dtype=torch.float32, chunk=None, schedule="cp", state_in="given"):
     import gated_delta_rule_100_amd as gdr
     chunk = chunk or d["chunk"]
     di = dev_inputs(d)
@@ -29,9 +35,10 @@ def run_prefill(d, out_dtype=torch.float32, chunk=None, keep=True, state_in="giv
     o = torch.full((T, H, dv), float("nan"), dtype=out_dtype, device="cuda")
     sout = torch.full((N, H, dv, dk), float("nan"), device="cuda")
     L = M = F = None
-    if keep:
+    if schedule == "cp":
         L = torch.full((mc, H, dv, dk), float("nan"), device="cuda")
         M = torch.full((mc, H, dk, dk), float("nan"), device="cuda")
+    if schedule in ("cp", "scan"):
         F = torch.full((mc, H, dv, dk), float("nan"), device="cuda")
     sin = di["state0"] if state_in == "given" else None
     gdr.gdr_chunk_prefill(di["q"], di["k"], di["v"], di["g"], di["beta"], di["cu"], sin, sout, o,
@@ -80,45 +87,54 @@ CASES = {
 }
 
 
+SCHEDULES = ["cp", "scan"]
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("name", list(CASES))
-def test_prefill_matches_oracle(name):
+def test_prefill_matches_oracle(name, schedule):
     idx, ov = CASES[name]
     d = workload(idx, seed=100 + idx, **ov)
-    say(f"prefill {name}: T={d['T']} N={d['N']} H={d['H']} d={d['dk']} C={d['chunk']} {d['dtype']}")
-    res = run_prefill(d)
+    say(f"prefill {name} [{schedule}]: T={d['T']} N={d['N']} H={d['H']} d={d['dk']} "
+        f"C={d['chunk']} {d['dtype']}")
+    res = run_prefill(d, schedule=schedule)
     check_against_oracle(d, res, d["chunk"], check_locals=d["T"] <= 20000)
 
 
-def test_prefill_without_initial_state():
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_prefill_without_initial_state(schedule):
     d = workload(2, seed=110, seqlens=[130, 64, 0, 5], H=2, gate="slow")
-    say("prefill without initial state")
-    res = run_prefill(d, state_in=None)
+    say(f"prefill without initial state [{schedule}]")
+    res = run_prefill(d, schedule=schedule, state_in=None)
     d0 = dict(d)
     d0["state0"] = None
     check_against_oracle(d0, res, d["chunk"])
 
 
-def test_prefill_bf16_output_is_rne_of_fp32_and_deterministic():
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_prefill_bf16_output_is_rne_of_fp32_and_deterministic(schedule):
     d = workload(3, seed=111, seqlens=[300, 1, 64, 129], H=2)
-    say("prefill bf16-vs-fp32 output and determinism")
-    r32 = run_prefill(d, torch.float32)
-    r32b = run_prefill(d, torch.float32)
-    r16 = run_prefill(d, torch.bfloat16)
+    say(f"prefill bf16-vs-fp32 output and determinism [{schedule}]")
+    r32 = run_prefill(d, torch.float32, schedule=schedule)
+    r32b = run_prefill(d, torch.float32, schedule=schedule)
+    r16 = run_prefill(d, torch.bfloat16, schedule=schedule)
     n_chunks = int(oracle.layout(d["cu_seqlens"], d["chunk"])[0][-1])
     for key in ("o", "state_out"):
         assert torch.equal(r32[key], r32b[key]), key
     for key in ("L", "M", "fixed"):  # slots past the real chunk count are never written
-        assert torch.equal(r32[key][:n_chunks], r32b[key][:n_chunks]), key
+        if r32[key] is not None:
+            assert torch.equal(r32[key][:n_chunks], r32b[key][:n_chunks]), key
     assert torch.equal(r16["o"], r32["o"].to(torch.bfloat16))
     assert torch.equal(r16["state_out"], r32["state_out"])
 
 
-def test_prefill_packing_invariance():
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_prefill_packing_invariance(schedule):
     # a packed varlen batch gives bit-identical results to separate calls
     lens = [77, 0, 130, 64, 1]
     d = workload(3, seed=112, seqlens=lens, H=2)
-    say("prefill packing invariance")
-    packed = run_prefill(d)
+    say(f"prefill packing invariance [{schedule}]")
+    packed = run_prefill(d, schedule=schedule)
     cu = d["cu_seqlens"]
     for n, ln in enumerate(lens):
         a, b = int(cu[n]), int(cu[n + 1])
@@ -128,7 +144,7 @@ def test_prefill_packing_invariance():
         sub["state0"] = np.ascontiguousarray(d["state0"][n:n + 1])
         sub["cu_seqlens"] = np.array([0, b - a], dtype=np.int32)
         sub["N"], sub["T"] = 1, b - a
-        single = run_prefill(sub, keep=False)
+        single = run_prefill(sub, schedule=schedule)
         assert torch.equal(single["o"], packed["o"][a:b])
         assert torch.equal(single["state_out"][0], packed["state_out"][n])
 
@@ -155,7 +171,7 @@ def test_prefill_in_place_state():
     say("prefill in-place state")
     import gated_delta_rule_100_amd as gdr
     di = dev_inputs(d)
-    ref = run_prefill(d, keep=False)
+    ref = run_prefill(d, schedule="none")
     st = di["state0"].clone()
     o = torch.empty_like(ref["o"])
     gdr.gdr_chunk_prefill(di["q"], di["k"], di["v"], di["g"], di["beta"], di["cu"], st, st, o,
@@ -191,7 +207,7 @@ def test_decode_steps_equal_prefill():
     d = workload(2, seed=115, seqlens=[40], H=2, gate="slow")
     say("decode chain vs prefill")
     di = dev_inputs(d)
-    res = run_prefill(d, keep=False)
+    res = run_prefill(d, schedule="none")
     st = di["state0"].clone()
     outs = []
     for t in range(d["T"]):
@@ -207,7 +223,7 @@ def test_decode_steps_equal_prefill():
 def test_split_prefill_resumes():
     d = workload(2, seed=116, seqlens=[300], H=2, gate="slow")
     say("split prefill resume")
-    full = run_prefill(d, keep=False)
+    full = run_prefill(d, schedule="none")
     T1 = 130
     parts = []
     state = d["state0"]
@@ -218,7 +234,7 @@ def test_split_prefill_resumes():
         sub["state0"] = state
         sub["cu_seqlens"] = np.array([0, b - a], dtype=np.int32)
         sub["T"] = b - a
-        r = run_prefill(sub, keep=False)
+        r = run_prefill(sub, schedule="none")
         parts.append(r["o"])
         state = r["state_out"].cpu().numpy()
     assert rel_err(host64(torch.cat(parts)), host64(full["o"])) <= 1e-3
