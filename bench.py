@@ -41,6 +41,13 @@ PRE_IO_BYTES = PRE_TOKENS * PRE_H * (3 * PRE_D * 2 + PRE_D * 2 + 8) \
     + 2 * PRE_B * PRE_H * PRE_D * PRE_D * 4
 PRE_CHUNK_HEADS = PRE_B * (PRE_T // PRE_C) * PRE_H
 PRE_CP_BYTES = PRE_IO_BYTES + PRE_CHUNK_HEADS * 393216
+# The sequential-scan schedule (taken for this workload) moves per chunk-head
+# the factors the chunk kernel writes (W planes 32 KiB, Q 16 KiB, K^T 16 KiB,
+# P planes 16 KiB, Ut^T 32 KiB, gates 512 B) and the scan reads back once (P
+# only below the diagonal: 12 KiB) on top of the unavoidable input/output.
+PRE_FACTOR_W = 32768 + 16384 + 16384 + 16384 + 32768 + 512
+PRE_FACTOR_R = PRE_FACTOR_W - 4096
+PRE_SCAN_BYTES = PRE_IO_BYTES + PRE_CHUNK_HEADS * (PRE_FACTOR_W + PRE_FACTOR_R)
 
 
 def parse():
@@ -51,6 +58,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=16.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--prefill-only", type=int, default=None, metavar="IDX",
+                    help="time only the chunked prefill of synthetic workload IDX (2: B=4 T=4096 "
+                         "H=16; 3: varlen 8 sequences 32768 tokens H=32; 4: B=1 T=131072 H=4) and "
+                         "print one JSON line; for per-kernel profiles")
     return ap.parse_args()
 
 
@@ -131,21 +142,21 @@ def recorded_traffic(kernel_file, record):
     return rec.get("hbm_bytes_per_launch")
 
 
-def bench_prefill(torch, gdr, steps, warmup):
+def bench_prefill(torch, gdr, steps, warmup, idx=2):
     from gdr_synth import workload
-    d = workload(2)
+    d = workload(idx)
     di = to_dev(d, torch)
-    T, H, D = PRE_TOKENS, PRE_H, PRE_D
+    T, H, D, N, C = d["T"], d["H"], d["dk"], d["N"], d["chunk"]
     o = torch.empty(T, H, D, dtype=torch.bfloat16, device="cuda")
-    sout = torch.empty_like(di["state0"])
-    ws = torch.empty(gdr.gdr_chunk_prefill_workspace_bytes(T, PRE_B, H, D, D, PRE_C),
+    sout = torch.empty(N, H, D, D, device="cuda")
+    ws = torch.empty(gdr.gdr_chunk_prefill_workspace_bytes(T, N, H, D, D, C),
                      dtype=torch.uint8, device="cuda")
     scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
     stream = torch.cuda.current_stream()
 
     def launch():
         gdr.gdr_chunk_prefill(di["q"], di["k"], di["v"], di["g"], di["beta"], di["cu"],
-                              di["state0"], sout, o, chunk=PRE_C, workspace=ws, stream=stream)
+                              di["state0"], sout, o, chunk=C, workspace=ws, stream=stream)
 
     for _ in range(warmup):
         launch()
@@ -162,7 +173,7 @@ def bench_prefill(torch, gdr, steps, warmup):
     wall = time.perf_counter() - t0
     ms = [a.elapsed_time(b) for a, b in ev]
     return dict(ms_mean=float(np.mean(ms)), ms_median=float(np.median(ms)),
-                ms_min=float(np.min(ms)), wall_s=wall)
+                ms_min=float(np.min(ms)), wall_s=wall, workload=d["name"], tokens=T)
 
 
 def cpu_baseline(budget_s):
@@ -232,6 +243,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.prefill_only is not None:
+        pre = bench_prefill(torch, gdr, args.steps, args.warmup, args.prefill_only)
+        print(json.dumps({"workload": pre["workload"], "prefill_ms": round(pre["ms_mean"], 4),
+                          "tokens_per_s": round(pre["tokens"] / (pre["ms_mean"] / 1e3), 1),
+                          "steps": args.steps, "warmup": args.warmup}))
+        return
     print(f"[bench] decode: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
     dec = bench_decode(torch, gdr, args.steps, args.warmup)
     print(f"[bench] decode {dec}", file=sys.stderr, flush=True)
@@ -271,7 +288,9 @@ def main():
         "prefill": {
             "value": round(PRE_TOKENS / pre_s, 1), "unit": "tokens/s",
             "ms": round(pre["ms_mean"], 4),
+            "schedule": "chunk factors + sequential chunk scan (factored fixup)",
             "io_min_frac": round(PRE_IO_BYTES / pre_s / 1e9 / HBM_PEAK_GBS, 4),
+            "scan_form_frac": round(PRE_SCAN_BYTES / pre_s / 1e9 / HBM_PEAK_GBS, 4),
             "cp_form_frac": round(PRE_CP_BYTES / pre_s / 1e9 / HBM_PEAK_GBS, 4),
         },
         "roofline": {

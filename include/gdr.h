@@ -122,8 +122,8 @@ gdr_status gdr_chunk_layout(const int32_t* cu_seqlens, int N, int chunk,
 
 /*
  * gdr_chunk_prefill_workspace_bytes -- device workspace that gdr_chunk_prefill
- * needs when L_out, M_out and fixed_out are all NULL (an upper bound for
- * every other case).  Returns 0 on bad arguments.
+ * needs when L_out, M_out and fixed_out are all NULL, for either schedule (an
+ * upper bound for every other case).  Returns 0 on bad arguments.
  */
 size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int dv,
                                          int chunk);
@@ -155,8 +155,17 @@ size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int 
  *               bound is 0
  * Sequences of length 0 are allowed: their final state is the initial state
  * (or zero).  q, k, v, g, beta and o must not overlap each other or the
- * state/L/M/fixed buffers.  Steps: layout, chunk-local L/M, fixup over the
- * chunks of each sequence, chunk outputs, final states -- all on `stream`.
+ * state/L/M/fixed buffers.  All work is enqueued on `stream`, in one of two
+ * schedules with the same results up to rounding order:
+ *   - chunk-parallel: layout, chunk-local L/M, fixup over the chunks of each
+ *     sequence (two-level for long sequences with few heads), chunk outputs,
+ *     final states.  Taken when L_out or M_out is given, for fp32 inputs or
+ *     chunk 16, and for long sequences at low parallelism;
+ *   - sequential scan: layout, per-chunk factors, then one pass per (sequence,
+ *     head, block of state rows) that applies the fixup in factored form
+ *     (S M_c + L_c = gamma_C S - (S W^T) diag(D) K + L_c, without forming M)
+ *     and writes the outputs, the final states and, when given, fixed_out.
+ *     Taken otherwise.
  */
 gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v,
                              const float* g, const float* beta,
