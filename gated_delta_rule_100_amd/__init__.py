@@ -23,6 +23,7 @@ __all__ = [
     "GDR_FP32",
     "library_path",
     "gdr_decode_step",
+    "gdr_decode_mtp",
     "gdr_chunk_prefill",
     "gdr_chunk_prefill_workspace_bytes",
     "gdr_state_fixup",
@@ -58,6 +59,7 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.gdr_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P]
+    lib.gdr_decode_mtp.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
     lib.gdr_decode_step.restype = I
     lib.gdr_max_chunks.argtypes = [I, I, I]
     lib.gdr_max_chunks.restype = I
@@ -142,6 +144,31 @@ def gdr_decode_step(q, k, v, g, beta, state, o, stream=None) -> None:
         _dev_ptr(g, "g", _F32), _dev_ptr(beta, "beta", _F32), _dev_ptr(state, "state", _F32),
         _dev_ptr(o, "o", _IO), N, H, dk, dv, _code(q.dtype), _code(o.dtype), _stream(stream))
     _check(st, "gdr_decode_step")
+
+
+def gdr_decode_mtp(q, k, v, g, beta, state_in, state_out, o, inter=None, stream=None) -> None:
+    """T decode tokens per (sequence, head).  q, k [N, T, H, dk], v [N, T, H, dv]
+    (bf16 or fp32, one dtype); g, beta [N, T, H] fp32; state_in [N, H, dv, dk]
+    fp32; state_out like state_in, the same tensor (in place) or None (no final
+    state written); o [N, T, H, dv] bf16 or fp32; inter [N, T, H, dv, dk] fp32
+    or None (the state after every token)."""
+    N, T, H, dk = q.shape
+    dv = v.shape[3]
+    if k.shape != q.shape or v.shape[:3] != (N, T, H) or g.shape != (N, T, H) \
+            or beta.shape != (N, T, H) or state_in.shape != (N, H, dv, dk) \
+            or o.shape != (N, T, H, dv) \
+            or (state_out is not None and state_out.shape != state_in.shape) \
+            or (inter is not None and inter.shape != (N, T, H, dv, dk)):
+        raise GdrError("gdr_decode_mtp: inconsistent shapes")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise GdrError("gdr_decode_mtp: q, k, v must share a dtype")
+    st = _load().gdr_decode_mtp(
+        _dev_ptr(q, "q", _IO), _dev_ptr(k, "k", _IO), _dev_ptr(v, "v", _IO),
+        _dev_ptr(g, "g", _F32), _dev_ptr(beta, "beta", _F32),
+        _dev_ptr(state_in, "state_in", _F32), _dev_ptr(state_out, "state_out", _F32, optional=True),
+        _dev_ptr(o, "o", _IO), _dev_ptr(inter, "inter", _F32, optional=True), N, T, H, dk, dv,
+        _code(q.dtype), _code(o.dtype), _stream(stream))
+    _check(st, "gdr_decode_mtp")
 
 
 def gdr_max_chunks(T_total: int, N: int, chunk: int) -> int:

@@ -173,6 +173,30 @@ gdr_status gdr_decode_step(const void* q, const void* k, const void* v, const fl
                     "gdr_decode_step launch");
 }
 
+gdr_status gdr_decode_mtp(const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const float* state_in, float* state_out, void* o,
+                          float* inter, int N, int T, int H, int dk, int dv, gdr_dtype in_dtype,
+                          gdr_dtype out_dtype, gdr_stream_t stream) {
+  if (!q || !k || !v || !g || !beta || !state_in || !o)
+    return fail(GDR_ERR_INVALID_ARG, "gdr_decode_mtp: NULL tensor pointer");
+  if (N <= 0 || H <= 0) return fail(GDR_ERR_INVALID_ARG, "gdr_decode_mtp: N=%d H=%d must be > 0", N, H);
+  if (T < 1 || T > 64) return fail(GDR_ERR_INVALID_ARG, "gdr_decode_mtp: T=%d not in [1, 64]", T);
+  if (static_cast<int64_t>(N) * H > INT32_MAX || static_cast<int64_t>(N) * T * H > INT32_MAX)
+    return fail(GDR_ERR_INVALID_ARG, "gdr_decode_mtp: N*T*H too large");
+  if (!supported_dims(dk, dv))
+    return fail(GDR_ERR_UNSUPPORTED, "gdr_decode_mtp: (dk, dv) = (%d, %d) not in {(64,64), (128,128)}", dk, dv);
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(GDR_ERR_UNSUPPORTED, "gdr_decode_mtp: dtype codes must be GDR_BF16 or GDR_FP32");
+  const void* ptrs[] = {q, k, v, g, beta, state_in, state_out, o, inter};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(GDR_ERR_INVALID_ARG, "gdr_decode_mtp: pointers must be 16-byte aligned");
+  gdr_status s = check_device();
+  if (s != GDR_OK) return s;
+  return hip_status(gdr::launch_mtp(q, k, v, g, beta, state_in, state_out, o, inter, N, T, H, dk,
+                                    dv, in_dtype, out_dtype, static_cast<hipStream_t>(stream)),
+                    "gdr_decode_mtp launch");
+}
+
 int gdr_max_chunks(int T_total, int N, int chunk) {
   if (T_total < 0 || N <= 0 || chunk <= 0) return -1;
   const int64_t m = static_cast<int64_t>(T_total) / chunk + N;

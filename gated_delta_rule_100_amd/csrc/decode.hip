@@ -102,6 +102,130 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     if (lane16 == i) store_scalar<OUT>(o, static_cast<size_t>(pair) * DV + rg + RG * i, oi[i]);
 }
 
+// Multi-token decode: T tokens per (sequence, head) applied in order to a state
+// that stays in registers, so the state is read once and written once whatever
+// T is.  Token t of sequence n is row n*T + t of q, k, v, g, beta and o (a
+// packed batch of N sequences of T tokens).  Optionally the state after every
+// token is written to `inter` (for rolling back rejected draft tokens), and the
+// final state to `state_out` (which may be the input state; NULL keeps the
+// input state as it is).  The per-token arithmetic is that of decode_kernel.
+template <int DK, int DV, Dt IN, Dt OUT>
+__global__ __launch_bounds__(kDecodeThreads) void mtp_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const float* state_in,
+    float* state_out, void* __restrict__ o, float* __restrict__ inter, int NH, int H, int T) {
+  constexpr int LPR = 16;
+  constexpr int CPL = DK / LPR;
+  constexpr int VEC = CPL / 4;
+  constexpr int RG = kDecodeThreads / LPR;
+  constexpr int RPT = DV / RG;
+  static_assert(CPL % 4 == 0 && DV % RG == 0, "shape");
+
+  const int pair = blockIdx.x;
+  if (pair >= NH) return;
+  const int n = pair / H, h = pair % H;
+  const int lane16 = threadIdx.x & (LPR - 1);
+  const int rg = threadIdx.x / LPR;
+
+  const floatx4* Sin = reinterpret_cast<const floatx4*>(state_in + static_cast<size_t>(pair) * DV * DK);
+  floatx4 st[RPT][VEC];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int row = rg + RG * i;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j)
+      st[i][j] = __builtin_nontemporal_load(&Sin[(row * DK + 4 * lane16 + 64 * j) / 4]);
+  }
+
+  // inputs of token t, loaded one token ahead
+  float kk[VEC][4], qq[VEC][4], vv[RPT], gg, bb;
+  auto load_token = [&](int t, float (&k_)[VEC][4], float (&q_)[VEC][4], float (&v_)[RPT],
+                        float& g_, float& b_) {
+    const size_t row = static_cast<size_t>(n) * T + t;  // token row
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      load_vec<IN, 4>(k, (row * H + h) * DK + 4 * lane16 + 64 * j, k_[j]);
+      load_vec<IN, 4>(q, (row * H + h) * DK + 4 * lane16 + 64 * j, q_[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) v_[i] = load_scalar<IN>(v, (row * H + h) * DV + rg + RG * i);
+    g_ = g[row * H + h];
+    b_ = beta[row * H + h];
+  };
+  load_token(0, kk, qq, vv, gg, bb);
+
+  for (int t = 0; t < T; ++t) {
+    float nk[VEC][4], nq[VEC][4], nv[RPT], ng, nb;
+    load_token(t + 1 < T ? t + 1 : t, nk, nq, nv, ng, nb);
+    const float alpha = expf(gg);
+    const size_t orow = ((static_cast<size_t>(n) * T + t) * H + h) * DV;
+    float oi[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < VEC; ++j)
+        a += st[i][j][0] * kk[j][0] + st[i][j][1] * kk[j][1] + st[i][j][2] * kk[j][2] +
+             st[i][j][3] * kk[j][3];
+      a = row16_sum(a);
+      const float u = bb * (vv[i] - alpha * a);
+      float p = 0.f;
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        floatx4 s = st[i][j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[e] = alpha * s[e] + u * kk[j][e];
+        st[i][j] = s;
+        p += s[0] * qq[j][0] + s[1] * qq[j][1] + s[2] * qq[j][2] + s[3] * qq[j][3];
+      }
+      oi[i] = row16_sum(p);
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+      if (lane16 == i) store_scalar<OUT>(o, orow + rg + RG * i, oi[i]);
+    if (inter) {
+      floatx4* I = reinterpret_cast<floatx4*>(inter + orow * DK);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int row = rg + RG * i;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) I[(row * DK + 4 * lane16 + 64 * j) / 4] = st[i][j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < VEC; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kk[j][e] = nk[j][e];
+        qq[j][e] = nq[j][e];
+      }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) vv[i] = nv[i];
+    gg = ng;
+    bb = nb;
+  }
+
+  if (state_out) {
+    floatx4* Sout = reinterpret_cast<floatx4*>(state_out + static_cast<size_t>(pair) * DV * DK);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = rg + RG * i;
+#pragma unroll
+      for (int j = 0; j < VEC; ++j)
+        __builtin_nontemporal_store(st[i][j], &Sout[(row * DK + 4 * lane16 + 64 * j) / 4]);
+    }
+  }
+}
+
+template <int DK, int DV, Dt IN, Dt OUT>
+hipError_t launch_mtp_t(const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const float* state_in, float* state_out, void* o,
+                        float* inter, int NH, int H, int T, hipStream_t stream) {
+  hipLaunchKernelGGL((mtp_kernel<DK, DV, IN, OUT>), dim3(NH), dim3(kDecodeThreads), 0, stream, q,
+                     k, v, g, beta, state_in, state_out, o, inter, NH, H, T);
+  return hipGetLastError();
+}
+
 template <int DK, int DV, Dt IN, Dt OUT>
 hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* g,
                            const float* beta, float* state, void* o, int NH,
@@ -132,6 +256,28 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
   if (dk == 128 && dv == 128)
     return dispatch_dtypes<128, 128>(q, k, v, g, beta, state, o, NH, in_dtype, out_dtype, stream);
   return dispatch_dtypes<64, 64>(q, k, v, g, beta, state, o, NH, in_dtype, out_dtype, stream);
+}
+
+hipError_t launch_mtp(const void* q, const void* k, const void* v, const float* g,
+                      const float* beta, const float* state_in, float* state_out, void* o,
+                      float* inter, int N, int T, int H, int dk, int dv, int in_dtype,
+                      int out_dtype, hipStream_t stream) {
+  (void)dv;
+  const int NH = N * H;
+#define GDR_MTP(D_, IN_, OUT_)                                                                \
+  return launch_mtp_t<D_, D_, IN_, OUT_>(q, k, v, g, beta, state_in, state_out, o, inter, NH, H, \
+                                         T, stream)
+  if (dk == 128) {
+    if (in_dtype == 0 && out_dtype == 0) GDR_MTP(128, Dt::BF16, Dt::BF16);
+    if (in_dtype == 0) GDR_MTP(128, Dt::BF16, Dt::F32);
+    if (out_dtype == 0) GDR_MTP(128, Dt::F32, Dt::BF16);
+    GDR_MTP(128, Dt::F32, Dt::F32);
+  }
+  if (in_dtype == 0 && out_dtype == 0) GDR_MTP(64, Dt::BF16, Dt::BF16);
+  if (in_dtype == 0) GDR_MTP(64, Dt::BF16, Dt::F32);
+  if (out_dtype == 0) GDR_MTP(64, Dt::F32, Dt::BF16);
+  GDR_MTP(64, Dt::F32, Dt::F32);
+#undef GDR_MTP
 }
 
 }  // namespace gdr

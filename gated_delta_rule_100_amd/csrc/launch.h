@@ -14,6 +14,14 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
                          const float* beta, float* state, void* o, int NH, int dk, int dv,
                          int in_dtype, int out_dtype, hipStream_t stream);
 
+// T decode tokens per (sequence, head): state_in read once, state_out (may be
+// state_in, or NULL) written once, `inter` (or NULL) gets the state after every
+// token.
+hipError_t launch_mtp(const void* q, const void* k, const void* v, const float* g,
+                      const float* beta, const float* state_in, float* state_out, void* o,
+                      float* inter, int N, int T, int H, int dk, int dv, int in_dtype,
+                      int out_dtype, hipStream_t stream);
+
 // Varlen layout: chunk_offsets [N+1], chunk_indices [max_chunks, 2].
 hipError_t launch_layout(const int32_t* cu_seqlens, int N, int chunk, int32_t* chunk_offsets,
                          int32_t* chunk_indices, int max_chunks, hipStream_t stream);

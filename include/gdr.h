@@ -94,6 +94,38 @@ gdr_status gdr_decode_step(const void* q, const void* k, const void* v,
                            gdr_stream_t stream);
 
 /*
+ * gdr_decode_mtp -- T decode tokens for each of N x H (sequence, head) states
+ * (multi-token decode, e.g. verifying T draft tokens).
+ *
+ * The FlashInfer PR #7156 page ("Cake GDP kernel optimisation: less shared
+ * memory, direct register loads", introduction) optimises the T = 1 variant of
+ * a multi-token ("MTP") decode kernel; this entry point is the general T.
+ * Token t of sequence n applies the recurrence to the state after token t-1
+ * (state_in for t = 0), and its output uses the updated state.  The result is
+ * that of gdr_chunk_prefill over N packed sequences of T tokens, and T = 1 is
+ * gdr_decode_step.  The state is read once and written once whatever T is.
+ *
+ *   q, k       [N, T, H, dk]     in_dtype (row n*T + t is token t of sequence n)
+ *   v          [N, T, H, dv]     in_dtype
+ *   g, beta    [N, T, H]         fp32; alpha = exp(g), used as given
+ *   state_in   [N, H, dv, dk]    fp32 input states
+ *   state_out  [N, H, dv, dk]    fp32 final states; may equal state_in (updated
+ *                                in place); NULL: no final state is written
+ *   o          [N, T, H, dv]     out_dtype
+ *   inter      [N, T, H, dv, dk] fp32 or NULL: the state after every token
+ *                                (inter[n][T-1] is the final state), e.g. to
+ *                                restart from the last accepted draft token
+ *   N, H > 0; 1 <= T <= 64
+ * q, k, v, g, beta, o and inter must not overlap state_in or state_out.
+ */
+gdr_status gdr_decode_mtp(const void* q, const void* k, const void* v,
+                          const float* g, const float* beta,
+                          const float* state_in, float* state_out, void* o,
+                          float* inter, int N, int T, int H, int dk, int dv,
+                          gdr_dtype in_dtype, gdr_dtype out_dtype,
+                          gdr_stream_t stream);
+
+/*
  * gdr_max_chunks -- host-only upper bound on the number of chunks of a packed
  * batch of N sequences with T_total tokens: T_total / chunk + N (every
  * sequence adds at most one partial chunk).  Returns -1 on bad arguments.

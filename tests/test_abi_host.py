@@ -28,7 +28,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
-    for name in ("gdr_decode_step", "gdr_chunk_prefill", "gdr_state_fixup", "gdr_chunk_layout",
+    for name in ("gdr_decode_step", "gdr_decode_mtp", "gdr_chunk_prefill", "gdr_state_fixup", "gdr_chunk_layout",
                  "gdr_max_chunks", "gdr_chunk_prefill_workspace_bytes", "gdr_status_string",
                  "gdr_last_error"):
         assert name in syms
@@ -75,6 +75,21 @@ def test_decode_rejects_bad_arguments(lib):
     bad = list(args)
     bad[5] = _p(fake + 4)
     assert lib.gdr_decode_step(*bad, 2, 2, 128, 128, 0, 0, None) == 1
+    assert "aligned" in lib.gdr_last_error().decode()
+
+
+def test_mtp_rejects_bad_arguments(lib):
+    fake = 0x10000  # never dereferenced: validation fails first
+    P9 = [_p(fake)] * 9  # q k v g beta state_in state_out o inter
+    assert lib.gdr_decode_mtp(*([None] + P9[1:]), 2, 4, 2, 128, 128, 0, 0, None) == 1
+    assert lib.gdr_decode_mtp(*P9, 2, 0, 2, 128, 128, 0, 0, None) == 1
+    assert "T=" in lib.gdr_last_error().decode()
+    assert lib.gdr_decode_mtp(*P9, 2, 65, 2, 128, 128, 0, 0, None) == 1
+    assert lib.gdr_decode_mtp(*P9, 2, 4, 2, 96, 96, 0, 0, None) == 2
+    assert lib.gdr_decode_mtp(*P9, 2, 4, 2, 128, 128, 0, 7, None) == 2
+    bad = list(P9)
+    bad[8] = _p(fake + 8)  # misaligned intermediate states
+    assert lib.gdr_decode_mtp(*bad, 2, 4, 2, 128, 128, 0, 0, None) == 1
     assert "aligned" in lib.gdr_last_error().decode()
 
 
