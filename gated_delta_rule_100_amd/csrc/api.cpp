@@ -118,8 +118,7 @@ size_t layout_workspace(int N, int mc) {
 
 size_t scan_workspace(int mc, int H, int d, int chunk) {
   const gdr::ChunkFactorSizes z = gdr::chunk_factor_sizes(mc, H, d, chunk);
-  return align_up(z.w) + align_up(z.q) + align_up(z.kt) + align_up(z.p) + align_up(z.ut) +
-         align_up(z.gate);
+  return align_up(z.w) + align_up(z.p) + align_up(z.ut) + align_up(z.gate);
 }
 
 // Schedule of gdr_chunk_prefill.  The sequential scan (scan.hip) keeps every
@@ -292,10 +291,6 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
     gdr::ChunkFactors f;
     f.w = reinterpret_cast<uint16_t*>(ws);
     ws += align_up(z.w);
-    f.q = reinterpret_cast<uint16_t*>(ws);
-    ws += align_up(z.q);
-    f.kt = reinterpret_cast<uint16_t*>(ws);
-    ws += align_up(z.kt);
     f.p = reinterpret_cast<uint16_t*>(ws);
     ws += align_up(z.p);
     f.ut = reinterpret_cast<float*>(ws);
@@ -306,7 +301,7 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
                                     chunk, st);
       if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: chunk factors");
     }
-    e = gdr::launch_chunk_scan(cu_seqlens, offs, f, state_in, state_out, fixed_out, o, N, H, dk,
+    e = gdr::launch_chunk_scan(q, k, cu_seqlens, offs, f, state_in, state_out, fixed_out, o, N, H, dk,
                                chunk, mc, T_total, out_dtype, st);
     return hip_status(e, "gdr_chunk_prefill: chunk scan");
   }

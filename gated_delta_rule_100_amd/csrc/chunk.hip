@@ -50,17 +50,17 @@ struct ChunkCfg {
   static constexpr int KB = D / 32;                       // 32-deep blocks along features
   static constexpr int CB = Cp / 32;                      // 32-deep blocks along the chunk
   static constexpr int NOFF = NT * (NT - 1) / 2;          // strictly lower 16x16 blocks
-  static constexpr int LDC = Cp + 4;                      // row stride of K^T, V^T (8-byte reads)
   static constexpr int LDP = Cp + 8;                      // row stride of P planes
   static constexpr int LDD = D + 8;                       // row stride of W planes (16-byte reads)
   static constexpr int LDB = 24;                          // row stride of 16x16 block planes
-  static constexpr int KT_PS = D * LDC;
+  static constexpr int CHD = D / 8;                       // 16-byte chunks per K/V row
+  static constexpr int KR_PS = Cp * D;                    // K, V rows per plane (dense, swz_tr)
   static constexpr int P_PS = C * LDP;
   static constexpr int W_PS = C * LDD;
   static constexpr int BLK_PS = 16 * LDB;
   static constexpr int r16(int x) { return (x + 15) / 16 * 16; }
   static constexpr int mx(int a, int b) { return a > b ? a : b; }
-  static constexpr int KT_BYTES = r16(PI * KT_PS * 2);
+  static constexpr int KT_BYTES = r16(PI * KR_PS * 2);
   static constexpr int KV_BYTES = 2 * KT_BYTES;
   static constexpr int W_BYTES = r16(PT * W_PS * 2);
   static constexpr int KVW_BYTES = OUT ? mx(KV_BYTES, W_BYTES) : KV_BYTES;
@@ -68,9 +68,9 @@ struct ChunkCfg {
   static constexpr int DIAG_BLK = r16(mx(16 * 17 * 4, PT * BLK_PS * 2));  // A_ii fp32, then T_ii planes
   static constexpr int P_BYTES = OUT ? r16(PT * P_PS * 2) : 0;
   static constexpr int GATE_BYTES = 6 * C * 4;
-  static constexpr int OFF_KT = 0;
-  static constexpr int OFF_VT = KT_BYTES;
-  static constexpr int OFF_W = 0;                         // W planes overlay K^T/V^T (outputs)
+  static constexpr int OFF_KR = 0;
+  static constexpr int OFF_VR = KT_BYTES;
+  static constexpr int OFF_W = 0;                         // W planes overlay K/V (outputs)
   static constexpr int OFF_AOFF = KVW_BYTES;
   static constexpr int OFF_DIAG = OFF_AOFF + AOFF_BYTES;
   static constexpr int OFF_P = OFF_DIAG + NT * DIAG_BLK;
@@ -111,8 +111,8 @@ struct ChunkWork {
   int tid, wave, c16, g4;
   float *sg, *sb, *sG, *sgam, *sD, *sbg;
 
-  __device__ uint16_t* Kt() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_KT); }
-  __device__ uint16_t* Vt() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_VT); }
+  __device__ uint16_t* Kr() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_KR); }
+  __device__ uint16_t* Vr() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_VR); }
   __device__ uint16_t* Wp() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_W); }
   __device__ uint16_t* Aoff(int blk) const {
     return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_AOFF) + blk * PT * Cfg::BLK_PS;
@@ -164,9 +164,11 @@ struct ChunkWork {
     }
   }
 
-  // K^T and V^T planes (chunk index contiguous, zero for t >= c), gates and
-  // their prefix quantities.  Every global load is issued before the first
-  // LDS write; bf16 inputs are stored bit for bit.
+  // K and V rows as planes (row-major, zero for t >= c, 16-byte chunks
+  // permuted by swz_tr for the transpose reads), gates and their prefix
+  // quantities.  Every global load is issued before the first LDS write; a
+  // 16-byte load becomes one 16-byte LDS write per plane, and bf16 inputs are
+  // stored bit for bit.
   __device__ void load(const void* k, const void* v, const float* g, const float* beta) {
     constexpr int G8 = D / 8;
     constexpr int ITER = Cfg::Cp * G8 / 256;
@@ -196,22 +198,25 @@ struct ChunkWork {
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
       const int idx = tid + 256 * it;
-      const int t = idx / G8, d0 = (idx % G8) * 8;
+      const int t = idx / G8, ch = idx % G8;
+      const int dst = t * D + 8 * (ch ^ swz_tr(t, G8));
+      if constexpr (IN == Dt::BF16) {
+        *reinterpret_cast<uint4*>(Kr() + dst) = rk[it][0];
+        *reinterpret_cast<uint4*>(Vr() + dst) = rv[it][0];
+      } else {
+        float xk[8], xv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if constexpr (IN == Dt::BF16) {
-          const uint32_t wk = (&rk[it][0].x)[e / 2], wv = (&rv[it][0].x)[e / 2];
-          Kt()[(d0 + e) * Cfg::LDC + t] = static_cast<uint16_t>((e & 1) ? (wk >> 16) : wk);
-          Vt()[(d0 + e) * Cfg::LDC + t] = static_cast<uint16_t>((e & 1) ? (wv >> 16) : wv);
-        } else {
-          uint16_t sk[PI], sv[PI];
-          split_planes<PI>(__uint_as_float((&rk[it][e / 4].x)[e % 4]), sk);
-          split_planes<PI>(__uint_as_float((&rv[it][e / 4].x)[e % 4]), sv);
+        for (int e = 0; e < 8; ++e) {
+          xk[e] = __uint_as_float((&rk[it][e / 4].x)[e % 4]);
+          xv[e] = __uint_as_float((&rv[it][e / 4].x)[e % 4]);
+        }
+        bf16x8 pk[PI], pv[PI];
+        split8<PI>(xk, pk);
+        split8<PI>(xv, pv);
 #pragma unroll
-          for (int p = 0; p < PI; ++p) {
-            Kt()[p * Cfg::KT_PS + (d0 + e) * Cfg::LDC + t] = sk[p];
-            Vt()[p * Cfg::KT_PS + (d0 + e) * Cfg::LDC + t] = sv[p];
-          }
+        for (int p = 0; p < PI; ++p) {
+          *reinterpret_cast<bf16x8*>(Kr() + p * Cfg::KR_PS + dst) = pk[p];
+          *reinterpret_cast<bf16x8*>(Vr() + p * Cfg::KR_PS + dst) = pv[p];
         }
       }
     }
@@ -329,18 +334,33 @@ struct ChunkWork {
   }
 
   // Right-hand side of block row i for feature tile b in D-tile layout:
-  // rows t = 16 i + 4 g4 + e, column 16 b + c16, scaled by w_t.
-  __device__ floatx4 rhs(const uint16_t* Xt, const float* w, int i, int b) const {
-    floatx4 r;
-    const uint16_t* src = Xt + (16 * b + c16) * Cfg::LDC + 16 * i + 4 * g4;
+  // rows t = 16 i + 4 g4 + e, column 16 b + c16, scaled by w_t (a transpose
+  // read of the K or V rows per plane).
+  __device__ floatx4 rhs(const uint16_t* Xr, const float* w, int i, int b) const {
+    float x[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float x = 0.f;
+    for (int p = 0; p < PI; ++p) {
+      const shortx4 v = read_tr4(Xr + p * Cfg::KR_PS, D, Cfg::CHD, 16 * i, 16 * b, c16, g4);
 #pragma unroll
-      for (int p = 0; p < PI; ++p) x += bf16_bits_to_f32(src[p * Cfg::KT_PS + e]);
-      r[e] = w[16 * i + 4 * g4 + e] * x;
+      for (int e = 0; e < 4; ++e) x[e] += bf16_bits_to_f32(static_cast<uint16_t>(v[e]));
     }
+    floatx4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = w[16 * i + 4 * g4 + e] * x[e];
     return r;
+  }
+
+  // Slot-permuted K^T fragment (rows: features 16 bj + c16; contraction slots:
+  // chunk rows 32 kb + 4 g4 + e and 32 kb + 16 + 4 g4 + e), two transpose reads
+  // per plane.
+  __device__ void kt_frag(int kb, int bj, bf16x8 (&out)[PI]) const {
+#pragma unroll
+    for (int p = 0; p < PI; ++p) {
+      const uint16_t* base = Kr() + p * Cfg::KR_PS;
+      const shortx4 lo = read_tr4(base, D, Cfg::CHD, 32 * kb, 16 * bj, c16, g4);
+      const shortx4 hi = read_tr4(base, D, Cfg::CHD, 32 * kb + 16, 16 * bj, c16, g4);
+      out[p] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
   }
 
   // Block forward substitution, all in this wave's registers:
@@ -354,8 +374,8 @@ struct ChunkWork {
 #pragma unroll
       for (int bb = 0; bb < DPW; ++bb) {
         const int b = wave + 4 * bb;
-        floatx4 rw = rhs(Kt(), sbg, i, b);
-        floatx4 ru = rhs(Vt(), sb, i, b);
+        floatx4 rw = rhs(Kr(), sbg, i, b);
+        floatx4 ru = rhs(Vr(), sb, i, b);
         floatx4 sw = {0.f, 0.f, 0.f, 0.f}, su = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < i; ++j) {
@@ -445,8 +465,7 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
 #pragma unroll
       for (int kb = 0; kb < Cfg::CB; ++kb) {
         bf16x8 kf[Cfg::PI];
-        load_lds8_perm<Cfg::PI>(w.Kt() + (16 * bj + w.c16) * Cfg::LDC + 32 * kb + 4 * w.g4,
-                                Cfg::KT_PS, kf);
+        w.kt_frag(kb, bj, kf);
         mma_planes<Cfg::PT, Cfg::PI>(l, AU[kb], kf);
         mma_planes<Cfg::PT, Cfg::PI>(m, AW[kb], kf);
       }
@@ -510,7 +529,7 @@ __global__ __launch_bounds__(256, 2) void chunk_out_kernel(
 
   floatx4 Wacc[NT][DPW], Uacc[NT][DPW];
   w.solve_wy(Wacc, Uacc);
-  __syncthreads();  // K^T and V^T are consumed; W planes take their place
+  __syncthreads();  // K and V are consumed; W planes take their place
 
 #pragma unroll
   for (int a = 0; a < NT; ++a) {
@@ -594,17 +613,19 @@ __global__ __launch_bounds__(256, 2) void chunk_out_kernel(
 
 // Per-chunk factors of the sequential schedule (bf16 inputs): the same
 // intra-chunk solve as above, but instead of L and M the chunk hands over
-// W (as two bf16 planes), Ut^T, Q, K^T, P = (Q K^T) (.) Gamma (two planes) and
-// the gates gamma_t, D_t, each laid out the way the scan kernel stages it.
-// With these, the state update S_end = S0 M + L is applied in factored form,
+// W (as two bf16 planes), Ut^T, P = (Q K^T) (.) Gamma (two planes) and the
+// gates gamma_t, D_t, each laid out the way the scan kernel stages it (the
+// scan takes Q and K straight from the inputs).  With these, the state update
+// S_end = S0 M + L is applied in factored form,
 //   S_end = gamma_C S0 + (Ut - W S0^T)^T diag(D) K,
 // so no dk x dk matrix is formed.
 //
-// The rows of W, Q, K^T and P are the A operands of the scan's products; their
-// contraction index is stored in operand-slot order: inside every 32-wide
-// block, lane group g's eight slots (elements 4g..4g+3 and 16+4g..16+4g+3,
-// the order in which D tiles stack, mfma_planes.h) are adjacent, so that the
-// scan reads each fragment with one 16-byte load.
+// W rows are stored as they are; P rows (the A operand of a product whose
+// other operand comes from D tiles) store their contraction index in
+// operand-slot order: inside every 32-wide block, lane group g's eight slots
+// (elements 4g..4g+3 and 16+4g..16+4g+3, the order in which D tiles stack,
+// mfma_planes.h) are adjacent, so that the scan reads each fragment with one
+// 16-byte load.
 template <int D, int C>
 __global__ __launch_bounds__(256, 2) void chunk_factors_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
@@ -639,8 +660,8 @@ __global__ __launch_bounds__(256, 2) void chunk_factors_kernel(
   w.solve_wy(Wacc, Uacc);
 
   const size_t slot = static_cast<size_t>(cid) * H + h;
-  // Row chunk n8 (16 bytes) of an operand row in slot order is made of the
-  // 4-element groups starting at 32 (n8/4) + 4 (n8%4) and 16 elements later.
+  // Row chunk n8 (16 bytes) of a row in slot order is made of the 4-element
+  // groups starting at 32 (n8/4) + 4 (n8%4) and 16 elements later.
   auto slot_chunk = [](const uint16_t* row, int n8) {
     const int c0 = 32 * (n8 >> 2) + 4 * (n8 & 3);
     const uint2 lo = *reinterpret_cast<const uint2*>(row + c0);
@@ -661,19 +682,7 @@ __global__ __launch_bounds__(256, 2) void chunk_factors_kernel(
     f.gate[slot * 2 * C + w.tid] = w.sgam[w.tid];
     f.gate[slot * 2 * C + C + w.tid] = w.sD[w.tid];
   }
-  // Q rows (zero past the chunk), K^T and the P planes, in slot order.
-  uint16_t* qg = f.q + slot * C * D;
-  const uint16_t* q16 = static_cast<const uint16_t*>(q);
-  for (int idx = w.tid; idx < C * D / 8; idx += 256) {
-    const int t = idx / (D / 8), n8 = idx % (D / 8);
-    *reinterpret_cast<uint4*>(qg + t * D + 8 * n8) =
-        t < ct.c ? slot_chunk(q16 + w.tok_off(t), n8) : make_uint4(0, 0, 0, 0);
-  }
-  uint16_t* kt = f.kt + slot * D * C;
-  for (int idx = w.tid; idx < D * C / 8; idx += 256) {
-    const int j = idx / (C / 8), n8 = idx % (C / 8);
-    *reinterpret_cast<uint4*>(kt + j * C + 8 * n8) = slot_chunk(w.Kt() + j * Cfg::LDC, n8);
-  }
+  // P planes, in slot order.
   uint16_t* pg = f.p + slot * PT * C * C;
   for (int idx = w.tid; idx < PT * C * C / 8; idx += 256) {
     const int pl = idx / (C * C / 8), r = idx % (C * C / 8);
@@ -681,7 +690,7 @@ __global__ __launch_bounds__(256, 2) void chunk_factors_kernel(
     *reinterpret_cast<uint4*>(pg + (pl * C + t) * C + 8 * n8) =
         slot_chunk(w.Pp() + pl * Cfg::P_PS + t * Cfg::LDP, n8);
   }
-  __syncthreads();  // K^T and V^T are consumed; W planes take their place
+  __syncthreads();  // K and V are consumed; W planes take their place
 #pragma unroll
   for (int a = 0; a < NT; ++a)
 #pragma unroll
@@ -700,7 +709,7 @@ __global__ __launch_bounds__(256, 2) void chunk_factors_kernel(
     const int pl = idx / (C * D / 8), r = idx % (C * D / 8);
     const int t = r / (D / 8), n8 = r % (D / 8);
     *reinterpret_cast<uint4*>(wg + (pl * C + t) * D + 8 * n8) =
-        slot_chunk(w.Wp() + pl * Cfg::W_PS + t * Cfg::LDD, n8);
+        *reinterpret_cast<const uint4*>(w.Wp() + pl * Cfg::W_PS + t * Cfg::LDD + 8 * n8);
   }
 }
 

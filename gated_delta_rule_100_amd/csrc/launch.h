@@ -65,18 +65,14 @@ hipError_t launch_final_state(const float* state_in, const float* fixed,
                               int n_chunks, float* state_out, hipStream_t stream);
 
 // Per-chunk factors of the sequential schedule, one slot per (chunk slot,
-// head) (d = dk = dv, C = chunk); rows marked * store their contraction index
-// in operand-slot order (chunk.hip):
-//   w     [slots][H][2][C][d]  W = (I + A)^{-1} diag(beta gamma) K as bf16 hi/lo planes *
-//   q     [slots][H][C][d]     Q rows, zero past the chunk, bf16 *
-//   kt    [slots][H][d][C]     K^T, bf16 *
-//   p     [slots][H][2][C][C]  P = (Q K^T) (.) Gamma (s <= t) as bf16 hi/lo planes *
+// head) (d = dk = dv, C = chunk); P rows store their contraction index in
+// operand-slot order (chunk.hip):
+//   w     [slots][H][2][C][d]  W = (I + A)^{-1} diag(beta gamma) K as bf16 hi/lo planes
+//   p     [slots][H][2][C][C]  P = (Q K^T) (.) Gamma (s <= t) as bf16 hi/lo planes
 //   ut    [slots][H][d][C]     Ut^T, Ut = (I + A)^{-1} diag(beta) V, fp32
 //   gate  [slots][H][2][C]     gamma_t and D_t, fp32
 struct ChunkFactors {
   uint16_t* w;
-  uint16_t* q;
-  uint16_t* kt;
   uint16_t* p;
   float* ut;
   float* gate;
@@ -84,13 +80,12 @@ struct ChunkFactors {
 
 // Bytes of each ChunkFactors array for `slots` chunk slots (host helper).
 struct ChunkFactorSizes {
-  size_t w, q, kt, p, ut, gate;
+  size_t w, p, ut, gate;
 };
 inline ChunkFactorSizes chunk_factor_sizes(int slots, int H, int d, int chunk) {
   const size_t n = static_cast<size_t>(slots) * H;
   const size_t c = static_cast<size_t>(chunk), dd = static_cast<size_t>(d);
-  return {n * 2 * c * dd * 2, n * c * dd * 2, n * dd * c * 2, n * 2 * c * c * 2, n * dd * c * 4,
-          n * 2 * c * 4};
+  return {n * 2 * c * dd * 2, n * 2 * c * c * 2, n * dd * c * 4, n * 2 * c * 4};
 }
 
 // Factors of every chunk slot < max_chunks (bf16 inputs, chunk 64).
@@ -102,7 +97,7 @@ hipError_t launch_chunk_factors(const void* q, const void* k, const void* v, con
 
 // Sequential scan over the chunks of every sequence from the factors: outputs
 // o, final states, and (when fixed != NULL) the state at every chunk end.
-hipError_t launch_chunk_scan(const int32_t* cu_seqlens,
+hipError_t launch_chunk_scan(const void* q, const void* k, const int32_t* cu_seqlens,
                              const int32_t* chunk_offsets, const ChunkFactors& f,
                              const float* state_in, float* state_out, float* fixed, void* o,
                              int N, int H, int d, int chunk, int n_slots, int T_total,

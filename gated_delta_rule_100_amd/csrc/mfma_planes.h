@@ -76,6 +76,29 @@ __device__ __forceinline__ void load_lds4(const uint16_t* base, int plane_stride
     out[p] = *reinterpret_cast<const shortx4*>(base + p * plane_stride);
 }
 
+// Chunk permutation for row-major bf16 tiles that are read with 16-bit
+// transpose reads (read_tr4): the 8 rows a half-wave's transpose read touches
+// get distinct pairs of 16-byte chunks, so the read is free of bank conflicts.
+// ch = 16-byte chunks per row (8 or 16); the result is even.
+__device__ __forceinline__ int swz_tr(int row, int ch) {
+  return 2 * ((row * ch / 16) & (ch / 2 - 1));
+}
+
+// Transposed 4-element read with gfx950's ds_read_b64_tr_b16.  Within each
+// 16-lane group that instruction hands output lane m element e of input lane
+// 4e + m/4 (that lane's element m % 4).  With the addresses formed here, lane
+// (c, g) receives X[r0 + 4g + e][col0 + c], e = 0..3, of a row-major bf16 tile
+// X (ld elements per row, 16-byte chunks permuted by swz_tr), i.e. a column
+// slice of four consecutive rows: the 16x16x16 A/B fragment of X^T, or half of
+// a slot-permuted 16x16x32 fragment.  col0 is a multiple of 16.
+__device__ __forceinline__ shortx4 read_tr4(const uint16_t* tile, int ld, int ch, int r0, int col0,
+                                            int c16, int g4) {
+  const int r = r0 + 4 * g4 + (c16 >> 2);
+  const int col = col0 + 4 * (c16 & 3);
+  const uint16_t* p = tile + r * ld + 8 * ((col >> 3) ^ swz_tr(r, ch)) + (col & 7);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)p);
+}
+
 template <int PA, int PB>
 __device__ __forceinline__ void mma_planes(floatx4& acc, const bf16x8 (&a)[PA],
                                            const bf16x8 (&b)[PB]) {

@@ -128,6 +128,22 @@ __device__ __forceinline__ void read_slots(const uint16_t* row0, int plane_strid
     out[p] = *reinterpret_cast<const bf16x8*>(row0 + p * plane_stride + off);
 }
 
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+// A fragment in slot order (two stacked D tiles: lane group g holds columns
+// 4g..4g+3 of the first tile in slots 0-3 and of the second in slots 4-7) to
+// natural order (lane group g holds columns 8g..8g+7).  Dwords 0-1 carry the
+// first tile, 2-3 the second; a 32-lane swap then a 16-lane swap (gfx950
+// v_permlane32_swap, v_permlane16_swap) route each pair of 16-lane groups.
+__device__ __forceinline__ bf16x8 slot_to_natural(bf16x8 x) {
+  const u32x4v w = __builtin_bit_cast(u32x4v, x);
+  const auto a = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(a[0], a[1], false, false);
+  const auto c = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(c[0], c[1], false, false);
+  return __builtin_bit_cast(bf16x8, u32x4v{b[0], d[0], b[1], d[1]});
+}
+
 // Four consecutive outputs into LDS (8 bytes bf16, round to nearest even; 16
 // bytes fp32).
 template <Dt OUTD>
@@ -157,6 +173,7 @@ __device__ __forceinline__ void copy16(const void* src, void* lds) {
 
 template <int D, int C, Dt OUTD>
 __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ offs, ChunkFactors f,
     const float* state_in, float* state_out, float* __restrict__ fixed, void* __restrict__ o,
     int N, int H, int n_slots, int T_total) {
@@ -180,6 +197,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
   int c0 = offs[n], c1 = offs[n + 1];
   c0 = c0 < 0 ? 0 : (c0 > n_slots ? n_slots : c0);
   c1 = c1 < c0 ? c0 : (c1 > n_slots ? n_slots : c1);
+  if (T_total <= 0) c1 = c0;  // no token to read, whatever the offsets claim
   int tb = cu[n], te = cu[n + 1];
   tb = tb < 0 ? 0 : (tb > T_total ? T_total : tb);
   te = te < tb ? tb : (te > T_total ? T_total : te);
@@ -206,6 +224,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
     // per-lane source offsets of this wave's copies (bytes from the chunk's base)
     uint32_t woff[Cfg::SW], qoff[Cfg::SQ], koff[Cfg::SK], uoff[Cfg::SU], poff[Cfg::SP];
     int wdst[Cfg::SW], qdst[Cfg::SQ], kdst[Cfg::SK], udst[Cfg::SU], pdst[Cfg::SP];
+    int qrow[Cfg::SQ], krow[Cfg::SK];  // chunk row each Q / K copy lane reads
 #pragma unroll
     for (int k = 0; k < Cfg::SW; ++k) {
       const int i = pick(k, Cfg::NW), p = 64 * i + lane, row = p / CHD, pc = p % CHD;
@@ -213,17 +232,20 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
       wdst[k] = Cfg::OFF_W + 1024 * i;
     }
 #pragma unroll
-    for (int k = 0; k < Cfg::SQ; ++k) {
-      const int i = pick(k, Cfg::NQ), p = 64 * i + lane, t = p / CHD, pc = p % CHD;
-      qoff[k] = 2u * (t * D + 8 * (pc ^ swz(t, CHD)));
-      qdst[k] = Cfg::OFF_Q + 1024 * i;
+    for (int x = 0; x < Cfg::SQ; ++x) {
+      const int i = pick(x, Cfg::NQ), p = 64 * i + lane, t = p / CHD, pc = p % CHD;
+      qrow[x] = t;
+      qoff[x] = 16u * (pc ^ swz(t, CHD));
+      qdst[x] = Cfg::OFF_Q + 1024 * i;
     }
 #pragma unroll
-    for (int k = 0; k < Cfg::SK; ++k) {
-      const int i = pick(k, Cfg::NK), p = 64 * i + lane, j = p / CHC, pc = p % CHC;
-      koff[k] = 2u * (j * C + 8 * (pc ^ swz(j, CHC)));
-      kdst[k] = Cfg::OFF_K + 1024 * i;
+    for (int x = 0; x < Cfg::SK; ++x) {
+      const int i = pick(x, Cfg::NK), p = 64 * i + lane, t = p / CHD, pc = p % CHD;
+      krow[x] = t;
+      koff[x] = 16u * (pc ^ swz_tr(t, CHD));
+      kdst[x] = Cfg::OFF_K + 1024 * i;
     }
+    const uint32_t row_bytes = 2u * static_cast<uint32_t>(H) * D;  // one token row of q or k
 #pragma unroll
     for (int k = 0; k < Cfg::SU; ++k) {
       const int i = pick(k, Cfg::NU), p = 64 * i + lane, vl = p / CHU, pc = p % CHU;
@@ -247,20 +269,38 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
       poff[k] = 2u * ((pl * C + t) * C + 8 * (pc ^ swz(t, ch)));
       pdst[k] = Cfg::OFF_P + 1024 * i;
     }
+    // First token of chunk s and the last row a copy may read: rows past the
+    // chunk repeat its last token (their outputs are never stored, and their
+    // K rows meet zero rows of U), and the row stays inside the input.
+    auto token_rows = [&](int s, int& tok, int& last) {
+      const int sc = s < c1 ? s : c1 - 1;
+      const int cl = chunk_range(sc, tok);
+      tok = tok < T_total ? tok : T_total - 1;
+      last = cl > 0 ? cl - 1 : 0;
+      last = tok + last < T_total ? last : T_total - 1 - tok;
+    };
     auto copy_wq = [&](int s) {
       const size_t slot = slot_of(s);
       const char* w = reinterpret_cast<const char*>(f.w + slot * 2 * C * D);
-      const char* q = reinterpret_cast<const char*>(f.q + slot * C * D);
+      int tok, last;
+      token_rows(s, tok, last);
+      const char* qs = reinterpret_cast<const char*>(q + (static_cast<size_t>(tok) * H + h) * D);
       unsigned char* buf = smem + ((s - c0) & 1) * Cfg::WQ_BYTES;
 #pragma unroll
-      for (int k = 0; k < Cfg::SW; ++k) copy16(w + woff[k], buf + wdst[k]);
+      for (int x = 0; x < Cfg::SW; ++x) copy16(w + woff[x], buf + wdst[x]);
 #pragma unroll
-      for (int k = 0; k < Cfg::SQ; ++k) copy16(q + qoff[k], buf + qdst[k]);
+      for (int x = 0; x < Cfg::SQ; ++x)
+        copy16(qs + static_cast<uint32_t>(qrow[x] < last ? qrow[x] : last) * row_bytes + qoff[x],
+               buf + qdst[x]);
     };
     auto copy_k = [&](int s) {
-      const char* k = reinterpret_cast<const char*>(f.kt + slot_of(s) * D * C);
+      int tok, last;
+      token_rows(s, tok, last);
+      const char* ks = reinterpret_cast<const char*>(k + (static_cast<size_t>(tok) * H + h) * D);
 #pragma unroll
-      for (int i = 0; i < Cfg::SK; ++i) copy16(k + koff[i], smem + kdst[i]);
+      for (int x = 0; x < Cfg::SK; ++x)
+        copy16(ks + static_cast<uint32_t>(krow[x] < last ? krow[x] : last) * row_bytes + koff[x],
+               smem + kdst[x]);
     };
     auto copy_upg = [&](int s) {
       const size_t slot = slot_of(s);
@@ -340,10 +380,11 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
       const uint16_t* Wl = reinterpret_cast<const uint16_t*>(wq + Cfg::OFF_W);
       const uint16_t* Ql = reinterpret_cast<const uint16_t*>(wq + Cfg::OFF_Q);
 
-      // S^T as operand planes, 32 state columns per block (slot-permuted).
-      // The 16x16x32 A and B fragments have the same lane layout, so these
-      // registers serve as B (rows of S^T) in W S^T and as A (rows of S) in
-      // S Q^T.
+      // S^T as operand planes, 32 state columns per block, in natural order
+      // (lane group g holds columns 32 kb + 8 g .. +7): split the two stacked D
+      // tiles, then regroup with permlane swaps.  The 16x16x32 A and B
+      // fragments have the same lane layout, so these registers serve as B
+      // (rows of S^T) in W S^T and as A (rows of S) in S Q^T.
       bf16x8 sb[KB][2];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -351,6 +392,8 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
 #pragma unroll
         for (int e2 = 0; e2 < 8; ++e2) x[e2] = S[2 * kb + e2 / 4][e2 & 3];
         split8<2>(x, sb[kb]);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) sb[kb][p] = slot_to_natural(sb[kb][p]);
       }
       // X = W S^T (rows: tokens) and Y^T = S Q^T (rows: state rows); the four
       // token tiles are interleaved so that consecutive products are
@@ -431,11 +474,13 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
 #pragma unroll
       for (int jt = 0; jt < ND; ++jt) {
         S[jt] *= gam_end;
-        const int j = 16 * jt + c16;
 #pragma unroll
         for (int kb = 0; kb < CB; ++kb) {
-          bf16x8 ka[1];
-          read_slots<1>(Kl + j * C, 0, j, CHC, 4 * kb + g4, ka);
+          // K^T fragment: features 16 jt + c16, slots = tokens 32 kb + 4 g4 + e
+          // and 32 kb + 16 + 4 g4 + e (transpose reads of the K rows)
+          const shortx4 lo = read_tr4(Kl, D, CHD, 32 * kb, 16 * jt, c16, g4);
+          const shortx4 hi = read_tr4(Kl, D, CHD, 32 * kb + 16, 16 * jt, c16, g4);
+          bf16x8 ka[1] = {__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7))};
           mma_planes<1, 2>(S[jt], ka, udb[kb]);
         }
       }
@@ -455,7 +500,8 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
 }
 
 template <int D, int C, Dt OUTD>
-hipError_t scan_t(const int32_t* cu, const int32_t* offs, const ChunkFactors& f,
+hipError_t scan_t(const void* q, const void* k, const int32_t* cu, const int32_t* offs,
+                  const ChunkFactors& f,
                   const float* state_in, float* state_out, float* fixed, void* o, int N, int H,
                   int n_slots, int T_total, hipStream_t stream) {
   constexpr int NVB = D / (16 * kComputeWaves);
@@ -463,20 +509,22 @@ hipError_t scan_t(const int32_t* cu, const int32_t* offs, const ChunkFactors& f,
   const int64_t groups = (pairs + kXcds - 1) / kXcds * kXcds * NVB;
   if (groups > INT32_MAX) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((chunk_scan_kernel<D, C, OUTD>), dim3(static_cast<unsigned>(groups)),
-                     dim3(kThreads), 0, stream, cu, offs, f, state_in, state_out, fixed, o, N, H,
-                     n_slots, T_total);
+                     dim3(kThreads), 0, stream, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k), cu, offs, f, state_in, state_out, fixed, o,
+                     N, H, n_slots, T_total);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_chunk_scan(const int32_t* cu_seqlens, const int32_t* chunk_offsets,
+hipError_t launch_chunk_scan(const void* q, const void* k, const int32_t* cu_seqlens,
+                             const int32_t* chunk_offsets,
                              const ChunkFactors& f, const float* state_in, float* state_out,
                              float* fixed, void* o, int N, int H, int d, int chunk, int n_slots,
                              int T_total, int out_dtype, hipStream_t stream) {
   if (chunk != 64) return hipErrorInvalidValue;
 #define GDR_SCAN(D_, OUT_)                                                                      \
-  return scan_t<D_, 64, OUT_>(cu_seqlens, chunk_offsets, f, state_in, state_out, fixed, o, N, \
+  return scan_t<D_, 64, OUT_>(q, k, cu_seqlens, chunk_offsets, f, state_in, state_out, fixed, o, N, \
                               H, n_slots, T_total, stream)
   if (d == 128) {
     if (out_dtype == 0) GDR_SCAN(128, Dt::BF16);
