@@ -42,11 +42,12 @@ PRE_IO_BYTES = PRE_TOKENS * PRE_H * (3 * PRE_D * 2 + PRE_D * 2 + 8) \
 PRE_CHUNK_HEADS = PRE_B * (PRE_T // PRE_C) * PRE_H
 PRE_CP_BYTES = PRE_IO_BYTES + PRE_CHUNK_HEADS * 393216
 # The sequential-scan schedule (taken for this workload) moves per chunk-head
-# the factors the chunk kernel writes (W planes 32 KiB, Q 16 KiB, K^T 16 KiB,
-# P planes 16 KiB, Ut^T 32 KiB, gates 512 B) and the scan reads back once (P
-# only below the diagonal: 12 KiB) on top of the unavoidable input/output.
-PRE_FACTOR_W = 32768 + 16384 + 16384 + 16384 + 32768 + 512
-PRE_FACTOR_R = PRE_FACTOR_W - 4096
+# the factors the chunk kernel writes (W planes 32 KiB, P planes 16 KiB, Ut^T
+# 32 KiB, gates 512 B), which the scan reads back once (P only below the
+# diagonal: 12 KiB) together with a second read of the chunk's q and k rows
+# (16 KiB each), on top of the unavoidable input/output.
+PRE_FACTOR_W = 32768 + 16384 + 32768 + 512
+PRE_FACTOR_R = PRE_FACTOR_W - 4096 + 2 * 16384
 PRE_SCAN_BYTES = PRE_IO_BYTES + PRE_CHUNK_HEADS * (PRE_FACTOR_W + PRE_FACTOR_R)
 
 

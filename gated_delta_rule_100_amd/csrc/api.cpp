@@ -118,7 +118,8 @@ size_t layout_workspace(int N, int mc) {
 
 size_t scan_workspace(int mc, int H, int d, int chunk) {
   const gdr::ChunkFactorSizes z = gdr::chunk_factor_sizes(mc, H, d, chunk);
-  return align_up(z.w) + align_up(z.p) + align_up(z.ut) + align_up(z.gate);
+  return align_up(z.w) + align_up(z.p) + align_up(z.ut) + align_up(z.gate) +
+         align_up(gdr::kScanSinkBytes);
 }
 
 // Schedule of gdr_chunk_prefill.  The sequential scan (scan.hip) keeps every
@@ -296,6 +297,8 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
     f.ut = reinterpret_cast<float*>(ws);
     ws += align_up(z.ut);
     f.gate = reinterpret_cast<float*>(ws);
+    ws += align_up(z.gate);
+    f.sink = reinterpret_cast<unsigned char*>(ws);
     if (T_total > 0) {
       e = gdr::launch_chunk_factors(q, k, v, g, beta, cu_seqlens, cidx, f, mc, T_total, H, dk,
                                     chunk, st);

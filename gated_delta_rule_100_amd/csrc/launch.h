@@ -71,11 +71,15 @@ hipError_t launch_final_state(const float* state_in, const float* fixed,
 //   p     [slots][H][2][C][C]  P = (Q K^T) (.) Gamma (s <= t) as bf16 hi/lo planes
 //   ut    [slots][H][d][C]     Ut^T, Ut = (I + A)^{-1} diag(beta) V, fp32
 //   gate  [slots][H][2][C]     gamma_t and D_t, fp32
+//   sink  kScanSinkBytes       scratch that output rows past a chunk's end are
+//                              written to (never read)
+constexpr size_t kScanSinkBytes = 4096;
 struct ChunkFactors {
   uint16_t* w;
   uint16_t* p;
   float* ut;
   float* gate;
+  unsigned char* sink;
 };
 
 // Bytes of each ChunkFactors array for `slots` chunk slots (host helper).

@@ -32,8 +32,8 @@
 // over the four.  An LDS region is refilled for a later chunk as soon as the
 // compute waves are done with it; three barriers per chunk mark the phases:
 //     compute:  [W S^T, S Q^T] B1 [U, O] B2 [state update] B3
-//     copy:     B1: W, Q of c+2 (double-buffered);  B2: write O of c, Ut^T, P,
-//               gates of c+1;  B3: K^T of c+1
+//     copy:     B1: W, Q of c+2 (double-buffered);  B2: Ut^T, P, gates of c+1;
+//               B3: write O of c, K of c+1
 // A copy is waited for just before the barrier that precedes its first use;
 // loads complete in order, so the loads issued after it stay in flight.
 // (Touching the lines of later chunks to warm L2 was measured to slow this
@@ -108,7 +108,7 @@ struct ScanCfg {
                     C * OPR % 64 == 0,
                 "copy tiling");
   static_assert(NO % kCopyWaves == 0, "copy shares");
-  static_assert(SW + SQ + SU + SP + SK + 2 <= 63, "vmcnt range");
+  static_assert(SW + SQ + SU + SP + SK + SO + 2 <= 63, "vmcnt range");
   static_assert(BYTES <= 160 * 1024, "LDS");
 };
 
@@ -314,18 +314,22 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
       if (lane < Cfg::G_BYTES / 16)
         copy16(f.gate + slot * 2 * C + 4 * lane, smem + Cfg::OFF_G + ((s - c0) & 1) * Cfg::G_BYTES);
     };
-    // outputs of chunk s: this wave's share of the staged 16-byte pieces
+    // outputs of chunk s: this wave's share of the staged 16-byte pieces.
+    // Every lane stores (rows past the chunk go to the sink), so that the
+    // number of loads and stores in flight, and with it every wait count
+    // below, is the same on every path.
     auto write_out = [&](int s) {
       int tok0;
       const int cl = chunk_range(s, tok0);
 #pragma unroll
-      for (int k = 0; k < Cfg::SO; ++k) {
-        const int p = 64 * (cw + kCopyWaves * k) + lane, t = p / Cfg::OPR, x = p % Cfg::OPR;
-        const uint4 v = *reinterpret_cast<const uint4*>(smem + Cfg::OFF_O + t * Cfg::O_LD + 16 * x);
-        if (t < cl)
-          *reinterpret_cast<uint4*>(static_cast<char*>(o) +
-                                    ((static_cast<size_t>(tok0 + t) * H + h) * D + Cfg::ROWS * vb) * OB +
-                                    16 * x) = v;
+      for (int x = 0; x < Cfg::SO; ++x) {
+        const int p = 64 * (cw + kCopyWaves * x) + lane, t = p / Cfg::OPR, pc = p % Cfg::OPR;
+        const uint4 v = *reinterpret_cast<const uint4*>(smem + Cfg::OFF_O + t * Cfg::O_LD + 16 * pc);
+        char* dst = t < cl ? static_cast<char*>(o) +
+                                 ((static_cast<size_t>(tok0 + t) * H + h) * D + Cfg::ROWS * vb) * OB +
+                                 16 * pc
+                           : reinterpret_cast<char*>(f.sink) + 16 * lane;
+        *reinterpret_cast<uint4*>(dst) = v;
       }
     };
 
@@ -338,16 +342,16 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
     for (int s = c0; s < c1; ++s) {
       copy_barrier();  // B1: W S^T and S Q^T of chunk s are done
       copy_wq(s + 2);  // into the buffer chunk s has just released
-      // K^T of chunk s (issued after B3 of chunk s-1) has landed, and with it
+      // K of chunk s (issued after B3 of chunk s-1) has landed, and with it
       // everything older: W, Q of chunk s+1 (issued after B1 of chunk s-1)
       __builtin_amdgcn_s_waitcnt(wait_vmcnt(Cfg::SW + Cfg::SQ));
       copy_barrier();  // B2: U and the outputs of chunk s are done and staged
-      write_out(s);
       copy_upg(s + 1);
       copy_barrier();  // B3: the state update of chunk s is done
+      write_out(s);    // the staging tile is rewritten only after B1 of chunk s+1
       copy_k(s + 1);
       // Ut^T, P, gates of chunk s+1 have landed (and the older W, Q of s+2)
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt(Cfg::SK));
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(Cfg::SO + Cfg::SK));
     }
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));  // nothing may land after the workgroup ends
     return;
