@@ -116,10 +116,9 @@ size_t layout_workspace(int N, int mc) {
          align_up(sizeof(int32_t) * 2 * static_cast<size_t>(mc));
 }
 
-size_t scan_workspace(int mc, int H, int d, int chunk) {
-  const gdr::ChunkFactorSizes z = gdr::chunk_factor_sizes(mc, H, d, chunk);
-  return align_up(z.w) + align_up(z.p) + align_up(z.ut) + align_up(z.gate) +
-         align_up(gdr::kScanSinkBytes);
+size_t scan_workspace(int mc, int H, int chunk) {
+  const gdr::ChunkFactorSizes z = gdr::chunk_factor_sizes(mc, H, chunk);
+  return align_up(z.t) + align_up(z.p) + align_up(z.gate);
 }
 
 // Schedule of gdr_chunk_prefill.  The sequential scan (scan.hip) keeps every
@@ -226,7 +225,7 @@ size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int 
   cp += align_up(per * dk * dk);  // M
   cp += align_up(per * dv * dk);  // fixed
   cp += seg_workspace(seg_sizes(T_total, N, H, dk, chunk, mc), N);
-  const size_t sc = chunk == 64 ? scan_workspace(mc, H, dk, chunk) : 0;
+  const size_t sc = chunk == 64 ? scan_workspace(mc, H, chunk) : 0;
   return layout_workspace(N, mc) + (cp > sc ? cp : sc);
 }
 
@@ -265,7 +264,7 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
   size_t need = layout_workspace(N, mc);
   SegSizes segz;
   if (scan) {
-    need += scan_workspace(mc, H, dk, chunk);
+    need += scan_workspace(mc, H, chunk);
   } else {
     if (!L_out) need += align_up(per * dv * dk);
     if (!M_out) need += align_up(per * dk * dk);
@@ -288,24 +287,20 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
   if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: layout");
 
   if (scan) {
-    const gdr::ChunkFactorSizes z = gdr::chunk_factor_sizes(mc, H, dk, chunk);
+    const gdr::ChunkFactorSizes z = gdr::chunk_factor_sizes(mc, H, chunk);
     gdr::ChunkFactors f;
-    f.w = reinterpret_cast<uint16_t*>(ws);
-    ws += align_up(z.w);
+    f.t = reinterpret_cast<uint16_t*>(ws);
+    ws += align_up(z.t);
     f.p = reinterpret_cast<uint16_t*>(ws);
     ws += align_up(z.p);
-    f.ut = reinterpret_cast<float*>(ws);
-    ws += align_up(z.ut);
     f.gate = reinterpret_cast<float*>(ws);
-    ws += align_up(z.gate);
-    f.sink = reinterpret_cast<unsigned char*>(ws);
     if (T_total > 0) {
-      e = gdr::launch_chunk_factors(q, k, v, g, beta, cu_seqlens, cidx, f, mc, T_total, H, dk,
-                                    chunk, st);
+      e = gdr::launch_chunk_factors(q, k, g, beta, cu_seqlens, cidx, f, mc, T_total, H, dk, chunk,
+                                    st);
       if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: chunk factors");
     }
-    e = gdr::launch_chunk_scan(q, k, cu_seqlens, offs, f, state_in, state_out, fixed_out, o, N, H, dk,
-                               chunk, mc, T_total, out_dtype, st);
+    e = gdr::launch_chunk_scan(q, k, v, cu_seqlens, offs, f, state_in, state_out, fixed_out, o, N,
+                               H, dk, chunk, mc, T_total, out_dtype, st);
     return hip_status(e, "gdr_chunk_prefill: chunk scan");
   }
 

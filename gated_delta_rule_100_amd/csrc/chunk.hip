@@ -39,7 +39,7 @@
 namespace gdr {
 namespace {
 
-template <int D, int C, Dt IN, bool OUT>
+template <int D, int C, Dt IN, bool OUT, bool TF = false>
 struct ChunkCfg {
   static constexpr int Cp = C < 32 ? 32 : C;              // contraction extent over the chunk
   static constexpr int PI = IN == Dt::BF16 ? 1 : 3;       // planes of q, k, v
@@ -60,17 +60,21 @@ struct ChunkCfg {
   static constexpr int BLK_PS = 16 * LDB;
   static constexpr int r16(int x) { return (x + 15) / 16 * 16; }
   static constexpr int mx(int a, int b) { return a > b ? a : b; }
-  static constexpr int KT_BYTES = r16(PI * KR_PS * 2);
+  static constexpr int KT_BYTES = TF ? 0 : r16(PI * KR_PS * 2);
   static constexpr int KV_BYTES = 2 * KT_BYTES;
   static constexpr int W_BYTES = r16(PT * W_PS * 2);
-  static constexpr int KVW_BYTES = OUT ? mx(KV_BYTES, W_BYTES) : KV_BYTES;
+  // lower-triangular C x C matrix, compact: rows t < C/2 keep C/2 columns
+  static constexpr int TL_PLANE = (C / 2) * (C / 2) + (C / 2) * C;
+  static constexpr int TL_BYTES = TF ? r16(PT * TL_PLANE * 2) : 0;
+  static constexpr int KVW_BYTES = TF ? TL_BYTES : OUT ? mx(KV_BYTES, W_BYTES) : KV_BYTES;
   static constexpr int AOFF_BYTES = r16(mx(NOFF, 1) * PT * BLK_PS * 2);
   static constexpr int DIAG_BLK = r16(mx(16 * 17 * 4, PT * BLK_PS * 2));  // A_ii fp32, then T_ii planes
-  static constexpr int P_BYTES = OUT ? r16(PT * P_PS * 2) : 0;
+  static constexpr int P_BYTES = OUT || TF ? r16(PT * P_PS * 2) : 0;
   static constexpr int GATE_BYTES = 6 * C * 4;
   static constexpr int OFF_KR = 0;
   static constexpr int OFF_VR = KT_BYTES;
   static constexpr int OFF_W = 0;                         // W planes overlay K/V (outputs)
+  static constexpr int OFF_TL = 0;                        // T planes (factors of the scan)
   static constexpr int OFF_AOFF = KVW_BYTES;
   static constexpr int OFF_DIAG = OFF_AOFF + AOFF_BYTES;
   static constexpr int OFF_P = OFF_DIAG + NT * DIAG_BLK;
@@ -101,9 +105,9 @@ __device__ __forceinline__ ChunkTokens chunk_tokens(const int32_t* cu, const int
   return r;
 }
 
-template <int D, int C, Dt IN, bool OUT>
+template <int D, int C, Dt IN, bool OUT, bool TF = false>
 struct ChunkWork {
-  using Cfg = ChunkCfg<D, C, IN, OUT>;
+  using Cfg = ChunkCfg<D, C, IN, OUT, TF>;
   static constexpr int PI = Cfg::PI, PT = Cfg::PT, NT = Cfg::NT, DPW = Cfg::DPW, KB = Cfg::KB;
 
   unsigned char* smem;
@@ -114,6 +118,7 @@ struct ChunkWork {
   __device__ uint16_t* Kr() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_KR); }
   __device__ uint16_t* Vr() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_VR); }
   __device__ uint16_t* Wp() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_W); }
+  __device__ uint16_t* Tl() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_TL); }
   __device__ uint16_t* Aoff(int blk) const {
     return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_AOFF) + blk * PT * Cfg::BLK_PS;
   }
@@ -190,11 +195,8 @@ struct ChunkWork {
                        : make_uint4(0, 0, 0, 0);
       }
     }
-    float gv = 0.f, bv = 0.f;
-    if (tid < c && tid < C) {
-      gv = g[static_cast<size_t>(tok0 + tid) * H + h];
-      bv = beta[static_cast<size_t>(tok0 + tid) * H + h];
-    }
+    float gv, bv;
+    read_gates(g, beta, gv, bv);
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
       const int idx = tid + 256 * it;
@@ -220,6 +222,21 @@ struct ChunkWork {
         }
       }
     }
+    finish_gates(gv, bv);
+  }
+
+  // g_t and beta_t of this chunk (zero past it), as load() reads them.
+  __device__ void read_gates(const float* g, const float* beta, float& gv, float& bv) const {
+    gv = 0.f;
+    bv = 0.f;
+    if (tid < c && tid < C) {
+      gv = g[static_cast<size_t>(tok0 + tid) * H + h];
+      bv = beta[static_cast<size_t>(tok0 + tid) * H + h];
+    }
+  }
+
+  // Gates into LDS and their prefix quantities G, gamma, D, beta gamma.
+  __device__ void finish_gates(float gv, float bv) {
     if (tid < C) {
       sg[tid] = gv;
       sb[tid] = bv;
@@ -396,6 +413,72 @@ struct ChunkWork {
         mma16_planes<PT, PT>(u, tii, pu);
         Wacc[i][bb] = w;
         Uacc[i][bb] = u;
+      }
+    }
+  }
+
+  // Offset of row t in the compact lower-triangular layout of a C x C plane
+  // (rows t < C/2 keep their first C/2 columns, the others all C).
+  static __device__ __forceinline__ int tl_row(int t) {
+    return t < C / 2 ? t * (C / 2) : (C / 2) * (C / 2) + (t - C / 2) * C;
+  }
+
+  // T = (I + A)^{-1}, lower triangular, into the compact planes at Tl(): wave
+  // j forms column block j by block forward substitution,
+  //   T_jj from the diagonal inversion,  T_ij = -T_ii sum_{j <= m < i} A_im T_mj,
+  // every block in D-tile layout, which is the B operand of the next product.
+  // The blocks of the compact layout above the diagonal are zeroed.
+  __device__ void solve_t() {
+    static_assert(NT <= 4, "one column block per wave");
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      if (j != wave) continue;
+      floatx4 X[NT];
+      {
+        // T_jj in D-tile layout: its planes times the identity
+        shortx4 tjj[PT], id[1];
+        load_lds4<PT>(Tdiag(j) + c16 * Cfg::LDB + 4 * g4, Cfg::BLK_PS, tjj);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) id[0][e] = 4 * g4 + e == c16 ? short(0x3F80) : short(0);
+        X[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        mma16_planes<PT, 1>(X[j], tjj, id);
+      }
+#pragma unroll
+      for (int i = j + 1; i < NT; ++i) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = j; m < i; ++m) {
+          shortx4 aim[PT], xm[PT];
+          load_lds4<PT>(Aoff(i * (i - 1) / 2 + m) + c16 * Cfg::LDB + 4 * g4, Cfg::BLK_PS, aim);
+          split4<PT>(X[m], xm);
+          mma16_planes<PT, PT>(acc, aim, xm);
+        }
+        shortx4 tii[PT], ap[PT];
+        load_lds4<PT>(Tdiag(i) + c16 * Cfg::LDB + 4 * g4, Cfg::BLK_PS, tii);
+        split4<PT>(acc, ap);
+        floatx4 x = {0.f, 0.f, 0.f, 0.f};
+        mma16_planes<PT, PT>(x, tii, ap);
+        X[i] = -x;
+      }
+#pragma unroll
+      for (int i = j; i < NT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint16_t sp[PT];
+          split_planes<PT>(X[i][e], sp);
+          const int t = 16 * i + 4 * g4 + e;
+#pragma unroll
+          for (int p = 0; p < PT; ++p) Tl()[p * Cfg::TL_PLANE + tl_row(t) + 16 * j + c16] = sp[p];
+        }
+      // blocks above the diagonal that the compact layout stores: zeros
+#pragma unroll
+      for (int i = 0; i < j; ++i) {
+        if (i < NT / 2 && j >= NT / 2) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int p = 0; p < PT; ++p)
+            Tl()[p * Cfg::TL_PLANE + tl_row(16 * i + 4 * g4 + e) + 16 * j + c16] = 0;
       }
     }
   }
@@ -611,16 +694,17 @@ __global__ __launch_bounds__(256, 2) void chunk_out_kernel(
   }
 }
 
-// Per-chunk factors of the sequential schedule (bf16 inputs): the same
-// intra-chunk solve as above, but instead of L and M the chunk hands over
-// W (as two bf16 planes), Ut^T, P = (Q K^T) (.) Gamma (two planes) and the
-// gates gamma_t, D_t, each laid out the way the scan kernel stages it (the
-// scan takes Q and K straight from the inputs).  With these, the state update
-// S_end = S0 M + L is applied in factored form,
-//   S_end = gamma_C S0 + (Ut - W S0^T)^T diag(D) K,
-// so no dk x dk matrix is formed.
+// Per-chunk factors of the sequential schedule (bf16 inputs, C = 64): the
+// matrices of the chunk that do not depend on the state,
+//   T = (I + A)^{-1}  and  P = (Q K^T) (.) Gamma  (both lower triangular,
+//   two bf16 planes each, compact rows),  gamma_t, D_t, beta_t,
+// laid out the way the scan kernel stages them.  The scan takes q, k, v
+// straight from the inputs and applies the UT transform itself:
+//   U = T diag(beta) (V - diag(gamma) K S0^T),
+// which is (I + A) U = diag(beta) V - diag(beta gamma) K S0^T solved with the
+// inverse instead of forming W and Ut here.
 //
-// W rows are stored as they are; P rows (the A operand of a product whose
+// T rows are stored as they are; P rows (the B operand of a product whose
 // other operand comes from D tiles) store their contraction index in
 // operand-slot order: inside every 32-wide block, lane group g's eight slots
 // (elements 4g..4g+3 and 16+4g..16+4g+3, the order in which D tiles stack,
@@ -628,13 +712,13 @@ __global__ __launch_bounds__(256, 2) void chunk_out_kernel(
 // 16-byte load.
 template <int D, int C>
 __global__ __launch_bounds__(256, 2) void chunk_factors_kernel(
-    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ cidx, ChunkFactors f, int H, int T_total) {
-  using W_ = ChunkWork<D, C, Dt::BF16, true>;
+    const void* __restrict__ q, const void* __restrict__ k, const float* __restrict__ g,
+    const float* __restrict__ beta, const int32_t* __restrict__ cu, const int32_t* __restrict__ cidx,
+    ChunkFactors f, int H, int T_total) {
+  using W_ = ChunkWork<D, C, Dt::BF16, false, true>;
   using Cfg = typename W_::Cfg;
-  constexpr int PT = Cfg::PT, NT = Cfg::NT, DPW = Cfg::DPW, KB = Cfg::KB;
-  static_assert(PT == 2 && Cfg::Cp == C, "factored form: bf16 inputs, C >= 32");
+  constexpr int PT = Cfg::PT, NT = Cfg::NT, KB = Cfg::KB, TLP = Cfg::TL_PLANE;
+  static_assert(PT == 2 && Cfg::Cp == C && C == 64, "factors of the scan: bf16 inputs, C = 64");
   __shared__ __align__(16) unsigned char smem[Cfg::BYTES];
   // Chunks are produced last-first: the scan reads them first-first, so the
   // earliest chunks are the most recently written (and still cache-resident)
@@ -649,77 +733,54 @@ __global__ __launch_bounds__(256, 2) void chunk_factors_kernel(
     bf16x8 kf[NT][KB][1], qf[NT][KB][1];
     w.rows_frags(k, kf);
     w.rows_frags(q, qf);
-    w.load(k, v, g, beta);
+    float gv, bv;
+    w.read_gates(g, beta, gv, bv);
+    w.finish_gates(gv, bv);
     w.gram_kk(kf);
     w.gram_qk(qf, kf);
   }
   __syncthreads();
   w.invert_diagonal();
-
-  floatx4 Wacc[NT][DPW], Uacc[NT][DPW];
-  w.solve_wy(Wacc, Uacc);
+  w.solve_t();
 
   const size_t slot = static_cast<size_t>(cid) * H + h;
-  // Row chunk n8 (16 bytes) of a row in slot order is made of the 4-element
-  // groups starting at 32 (n8/4) + 4 (n8%4) and 16 elements later.
+  if (w.tid < C) {
+    float* gt = f.gate + slot * 4 * C;
+    gt[w.tid] = w.sgam[w.tid];
+    gt[C + w.tid] = w.sD[w.tid];
+    gt[2 * C + w.tid] = w.sb[w.tid];
+    gt[3 * C + w.tid] = 0.f;
+  }
+  // P planes, compact lower layout, each row in slot order: row chunk n8
+  // (16 bytes) is made of the 4-element groups starting at 32 (n8/4) + 4 (n8%4)
+  // and 16 elements later.
   auto slot_chunk = [](const uint16_t* row, int n8) {
     const int c0 = 32 * (n8 >> 2) + 4 * (n8 & 3);
     const uint2 lo = *reinterpret_cast<const uint2*>(row + c0);
     const uint2 hi = *reinterpret_cast<const uint2*>(row + c0 + 16);
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
   };
-  // Ut^T: row v holds the chunk's column v of Ut (one float4 per D-tile row group).
-  float* ut = f.ut + slot * D * C;
-#pragma unroll
-  for (int a = 0; a < NT; ++a)
-#pragma unroll
-    for (int bb = 0; bb < DPW; ++bb) {
-      const int vrow = 16 * (w.wave + 4 * bb) + w.c16;
-      *reinterpret_cast<floatx4*>(ut + static_cast<size_t>(vrow) * C + 16 * a + 4 * w.g4) =
-          Uacc[a][bb];
-    }
-  if (w.tid < C) {
-    f.gate[slot * 2 * C + w.tid] = w.sgam[w.tid];
-    f.gate[slot * 2 * C + C + w.tid] = w.sD[w.tid];
-  }
-  // P planes, in slot order.
-  uint16_t* pg = f.p + slot * PT * C * C;
-  for (int idx = w.tid; idx < PT * C * C / 8; idx += 256) {
-    const int pl = idx / (C * C / 8), r = idx % (C * C / 8);
-    const int t = r / (C / 8), n8 = r % (C / 8);
-    *reinterpret_cast<uint4*>(pg + (pl * C + t) * C + 8 * n8) =
+  uint16_t* pg = f.p + slot * PT * TLP;
+  for (int idx = w.tid; idx < PT * TLP / 8; idx += 256) {
+    const int pl = idx / (TLP / 8), r = idx % (TLP / 8);
+    constexpr int LO = (C / 2) * (C / 16);  // 16-byte chunks of the short rows
+    const int t = r < LO ? r / (C / 16) : C / 2 + (r - LO) / (C / 8);
+    const int n8 = r < LO ? r % (C / 16) : (r - LO) % (C / 8);
+    *reinterpret_cast<uint4*>(pg + pl * TLP + 8 * r) =
         slot_chunk(w.Pp() + pl * Cfg::P_PS + t * Cfg::LDP, n8);
   }
-  __syncthreads();  // K and V are consumed; W planes take their place
-#pragma unroll
-  for (int a = 0; a < NT; ++a)
-#pragma unroll
-    for (int bb = 0; bb < DPW; ++bb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * a + 4 * w.g4 + e, d = 16 * (w.wave + 4 * bb) + w.c16;
-        uint16_t sp[PT];
-        split_planes<PT>(Wacc[a][bb][e], sp);
-#pragma unroll
-        for (int p = 0; p < PT; ++p) w.Wp()[p * Cfg::W_PS + t * Cfg::LDD + d] = sp[p];
-      }
-  __syncthreads();
-  uint16_t* wg = f.w + slot * PT * C * D;
-  for (int idx = w.tid; idx < PT * C * D / 8; idx += 256) {
-    const int pl = idx / (C * D / 8), r = idx % (C * D / 8);
-    const int t = r / (D / 8), n8 = r % (D / 8);
-    *reinterpret_cast<uint4*>(wg + (pl * C + t) * D + 8 * n8) =
-        *reinterpret_cast<const uint4*>(w.Wp() + pl * Cfg::W_PS + t * Cfg::LDD + 8 * n8);
-  }
+  __syncthreads();  // T planes complete
+  uint16_t* tg = f.t + slot * PT * TLP;
+  for (int idx = w.tid; idx < PT * TLP / 8; idx += 256)
+    *reinterpret_cast<uint4*>(tg + 8 * idx) = *reinterpret_cast<const uint4*>(w.Tl() + 8 * idx);
 }
 
 template <int D, int C>
-hipError_t factors_t(const void* q, const void* k, const void* v, const float* g,
-                     const float* beta, const int32_t* cu, const int32_t* cidx,
-                     const ChunkFactors& f, int max_chunks, int T_total, int H,
-                     hipStream_t stream) {
+hipError_t factors_t(const void* q, const void* k, const float* g, const float* beta,
+                     const int32_t* cu, const int32_t* cidx, const ChunkFactors& f,
+                     int max_chunks, int T_total, int H, hipStream_t stream) {
   hipLaunchKernelGGL((chunk_factors_kernel<D, C>), dim3(max_chunks, H), dim3(256), 0, stream, q,
-                     k, v, g, beta, cu, cidx, f, H, T_total);
+                     k, g, beta, cu, cidx, f, H, T_total);
   return hipGetLastError();
 }
 
@@ -802,17 +863,16 @@ hipError_t launch_chunk_out(const void* q, const void* k, const void* v, const f
 #undef GDR_OUT
 }
 
-hipError_t launch_chunk_factors(const void* q, const void* k, const void* v, const float* g,
-                                const float* beta, const int32_t* cu_seqlens,
-                                const int32_t* chunk_indices, const ChunkFactors& f,
-                                int max_chunks, int T_total, int H, int d, int chunk,
-                                hipStream_t stream) {
+hipError_t launch_chunk_factors(const void* q, const void* k, const float* g, const float* beta,
+                                const int32_t* cu_seqlens, const int32_t* chunk_indices,
+                                const ChunkFactors& f, int max_chunks, int T_total, int H, int d,
+                                int chunk, hipStream_t stream) {
   if (max_chunks <= 0) return hipSuccess;
   if (chunk != 64) return hipErrorInvalidValue;
   if (d == 128)
-    return factors_t<128, 64>(q, k, v, g, beta, cu_seqlens, chunk_indices, f, max_chunks, T_total,
-                              H, stream);
-  return factors_t<64, 64>(q, k, v, g, beta, cu_seqlens, chunk_indices, f, max_chunks, T_total, H,
+    return factors_t<128, 64>(q, k, g, beta, cu_seqlens, chunk_indices, f, max_chunks, T_total, H,
+                              stream);
+  return factors_t<64, 64>(q, k, g, beta, cu_seqlens, chunk_indices, f, max_chunks, T_total, H,
                            stream);
 }
 

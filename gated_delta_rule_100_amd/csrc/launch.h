@@ -65,46 +65,43 @@ hipError_t launch_final_state(const float* state_in, const float* fixed,
                               int n_chunks, float* state_out, hipStream_t stream);
 
 // Per-chunk factors of the sequential schedule, one slot per (chunk slot,
-// head) (d = dk = dv, C = chunk); P rows store their contraction index in
-// operand-slot order (chunk.hip):
-//   w     [slots][H][2][C][d]  W = (I + A)^{-1} diag(beta gamma) K as bf16 hi/lo planes
-//   p     [slots][H][2][C][C]  P = (Q K^T) (.) Gamma (s <= t) as bf16 hi/lo planes
-//   ut    [slots][H][d][C]     Ut^T, Ut = (I + A)^{-1} diag(beta) V, fp32
-//   gate  [slots][H][2][C]     gamma_t and D_t, fp32
-//   sink  kScanSinkBytes       scratch that output rows past a chunk's end are
-//                              written to (never read)
-constexpr size_t kScanSinkBytes = 4096;
+// head) (C = chunk = 64).  T and P are lower triangular and stored compactly:
+// rows t < C/2 keep their first C/2 columns, rows t >= C/2 all C (TL = 3 C^2 / 4
+// elements per plane); P rows store their contraction index in operand-slot
+// order (chunk.hip):
+//   t     [slots][H][2][TL]   T = (I + A)^{-1} as bf16 hi/lo planes
+//   p     [slots][H][2][TL]   P = (Q K^T) (.) Gamma (s <= t) as bf16 hi/lo planes
+//   gate  [slots][H][4][C]    gamma_t, D_t, beta_t and zeros, fp32
 struct ChunkFactors {
-  uint16_t* w;
+  uint16_t* t;
   uint16_t* p;
-  float* ut;
   float* gate;
-  unsigned char* sink;
 };
 
 // Bytes of each ChunkFactors array for `slots` chunk slots (host helper).
 struct ChunkFactorSizes {
-  size_t w, p, ut, gate;
+  size_t t, p, gate;
 };
-inline ChunkFactorSizes chunk_factor_sizes(int slots, int H, int d, int chunk) {
+inline ChunkFactorSizes chunk_factor_sizes(int slots, int H, int chunk) {
   const size_t n = static_cast<size_t>(slots) * H;
-  const size_t c = static_cast<size_t>(chunk), dd = static_cast<size_t>(d);
-  return {n * 2 * c * dd * 2, n * 2 * c * c * 2, n * dd * c * 4, n * 2 * c * 4};
+  const size_t c = static_cast<size_t>(chunk);
+  const size_t tl = 3 * c * c / 4;
+  return {n * 2 * tl * 2, n * 2 * tl * 2, n * 4 * c * 4};
 }
 
 // Factors of every chunk slot < max_chunks (bf16 inputs, chunk 64).
-hipError_t launch_chunk_factors(const void* q, const void* k, const void* v, const float* g,
-                                const float* beta, const int32_t* cu_seqlens,
-                                const int32_t* chunk_indices, const ChunkFactors& f,
-                                int max_chunks, int T_total, int H, int d, int chunk,
-                                hipStream_t stream);
+hipError_t launch_chunk_factors(const void* q, const void* k, const float* g, const float* beta,
+                                const int32_t* cu_seqlens, const int32_t* chunk_indices,
+                                const ChunkFactors& f, int max_chunks, int T_total, int H, int d,
+                                int chunk, hipStream_t stream);
 
-// Sequential scan over the chunks of every sequence from the factors: outputs
-// o, final states, and (when fixed != NULL) the state at every chunk end.
-hipError_t launch_chunk_scan(const void* q, const void* k, const int32_t* cu_seqlens,
-                             const int32_t* chunk_offsets, const ChunkFactors& f,
-                             const float* state_in, float* state_out, float* fixed, void* o,
-                             int N, int H, int d, int chunk, int n_slots, int T_total,
-                             int out_dtype, hipStream_t stream);
+// Sequential scan over the chunks of every sequence from the factors and the
+// q, k, v inputs: outputs o, final states, and (when fixed != NULL) the state
+// at every chunk end.
+hipError_t launch_chunk_scan(const void* q, const void* k, const void* v,
+                             const int32_t* cu_seqlens, const int32_t* chunk_offsets,
+                             const ChunkFactors& f, const float* state_in, float* state_out,
+                             float* fixed, void* o, int N, int H, int d, int chunk, int n_slots,
+                             int T_total, int out_dtype, hipStream_t stream);
 
 }  // namespace gdr

@@ -52,18 +52,35 @@ __device__ __forceinline__ void mma16_planes(floatx4& acc, const shortx4 (&a)[PA
   }
 }
 
+// Two fp32 values as P planes of bf16 pairs (value a in the low half): one
+// v_cvt_pk_bf16_f32 (round to nearest even) per plane, and the residual taken
+// against the rounded pair read back as fp32 (a shift and a mask).  Equal bit
+// for bit to rounding each value on its own.
+template <int P>
+__device__ __forceinline__ void split2(float a, float b, uint32_t (&out)[P]) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2v));
+    out[p] = h;
+    if (p + 1 < P) {
+      a = a - __uint_as_float(h << 16);
+      b = b - __uint_as_float(h & 0xffff0000u);
+    }
+  }
+}
+
 // Split 4 fp32 values (a D tile's floatx4) into P planes of 4 bf16.
 template <int P>
 __device__ __forceinline__ void split4(const floatx4& x, shortx4 (&out)[P]) {
-  floatx4 r = x;
+  uint32_t lo[P], hi[P];
+  split2<P>(x[0], x[1], lo);
+  split2<P>(x[2], x[3], hi);
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const __bf16 hb = static_cast<__bf16>(r[e]);
-      out[p][e] = __builtin_bit_cast(short, hb);
-      r[e] = r[e] - static_cast<float>(hb);
-    }
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    out[p] = __builtin_bit_cast(shortx4, u32x2{lo[p], hi[p]});
   }
 }
 
@@ -128,16 +145,12 @@ __device__ __forceinline__ void split_planes(float x, uint16_t (&out)[P]) {
 // Split 8 fp32 values into P bf16x8 fragments.
 template <int P>
 __device__ __forceinline__ void split8(const float (&x)[8], bf16x8 (&out)[P]) {
-  ushort8 w[P];
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  uint32_t w[4][P];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    uint16_t sp[P];
-    split_planes<P>(x[e], sp);
+  for (int i = 0; i < 4; ++i) split2<P>(x[2 * i], x[2 * i + 1], w[i]);
 #pragma unroll
-    for (int p = 0; p < P; ++p) w[p][e] = sp[p];
-  }
-#pragma unroll
-  for (int p = 0; p < P; ++p) out[p] = __builtin_bit_cast(bf16x8, w[p]);
+  for (int p = 0; p < P; ++p) out[p] = __builtin_bit_cast(bf16x8, u32x4{w[0][p], w[1][p], w[2][p], w[3][p]});
 }
 
 // 8 consecutive bf16 of each plane from LDS (16-byte aligned).
