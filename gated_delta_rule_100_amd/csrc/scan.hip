@@ -18,7 +18,8 @@
 // come out of the same pass.  The re-association is derived from the
 // recurrence.
 //
-// Compute waves.  Four waves each own one 16-row tile of state rows, held as
+// Compute waves.  Four waves (one per SIMD) each own one 16-row tile of state
+// rows, held as
 // D tiles of S^T: lane (c, g) holds S[v = 16 vt + c][16 jt + 4 g + e], e = 0..3.
 // That is the accumulator layout of the state update (A = K^T, B = diag(D) U).
 // For the contractions over dk the state is split into bf16 hi/lo planes and
@@ -39,8 +40,7 @@
 // the rows one fragment read touches fall into distinct banks; the permutation
 // is applied on the global side of the copies (each lane of a global-to-LDS
 // load names its own source address), so every copy instruction fills a dense
-// 1 KiB block.  Workgroups of one (sequence, head) are placed on the same XCD
-// so that they share its L2.
+// 1 KiB block.
 #include "launch.h"
 #include "mfma_planes.h"
 
@@ -48,8 +48,8 @@ namespace gdr {
 namespace {
 
 constexpr int kXcds = 8;
-constexpr int kComputeWaves = 4;
 constexpr int kCopyWaves = 4;
+constexpr int kComputeWaves = 4;  // 16 state rows each
 constexpr int kThreads = 64 * (kComputeWaves + kCopyWaves);
 
 template <int D, int C>
@@ -61,7 +61,7 @@ struct ScanCfg {
   static constexpr int CHD = D / 8;    // 16-byte chunks per row of D bf16
   static constexpr int CHC = C / 8;    // 16-byte chunks per row of C bf16
   static constexpr int ROWS = 16 * kComputeWaves;  // state rows per workgroup
-  static constexpr int CHV = ROWS / 8;             // 16-byte chunks per staged v row
+  static constexpr int NVB = D / ROWS;              // workgroups per (sequence, head)
   // T and P planes: rows t < C/2 keep their first C/2 columns (the rest is
   // above the diagonal), rows t >= C/2 keep all C.
   static constexpr int TL_LO = (C / 2) * (C / 2);
@@ -152,22 +152,10 @@ __device__ __forceinline__ void copy16(const void* src, void* lds) {
                                    (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
 }
 
-// Scheduling pattern for a region of R LDS reads and M >= R matrix products:
-// one read, then its share of the products (sched_group_barrier masks: 0x100
-// LDS read, 0x008 matrix product).  A wave issues in order and a 16-byte LDS
-// read holds its issue for about as long as two products take.
-template <int R, int M, int I = 0>
-__device__ __forceinline__ void interleave() {
-  static_assert(M >= R, "pattern");
-  if constexpr (I < R) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, (I + 1) * M / R - I * M / R, 0);
-    interleave<R, M, I + 1>();
-  }
-}
-
-// L LDS reads first, then pairs of one read and one product, then the
-// remaining L products (R reads and R products in all).
+// Scheduling pattern for a region of R LDS reads and R matrix products (masks
+// of sched_group_barrier: 0x100 LDS read, 0x008 matrix product): L reads
+// first, then pairs of one read and one product, then the remaining L
+// products.  A wave issues in order, so the reads run L ahead of their use.
 template <int L, int R, int I = 0>
 __device__ __forceinline__ void lead_interleave() {
   if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(0x100, L, 0);
@@ -188,11 +176,12 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
     float* __restrict__ fixed, void* __restrict__ o, int N, int H, int n_slots, int T_total) {
   using Cfg = ScanCfg<D, C>;
   constexpr int NT = Cfg::NT, ND = Cfg::ND, KB = Cfg::KB, CB = Cfg::CB;
-  constexpr int CHD = Cfg::CHD, CHC = Cfg::CHC, CHV = Cfg::CHV, TL = Cfg::TL;
-  constexpr int NVB = D / Cfg::ROWS;  // workgroups per (sequence, head)
+  constexpr int CHD = Cfg::CHD, CHC = Cfg::CHC, TL = Cfg::TL, NVB = Cfg::NVB;
+  constexpr int CHV = Cfg::ROWS / 8;  // 16-byte chunks per staged v row
   __shared__ __align__(1024) unsigned char smem[Cfg::BYTES];
 
-  // XCD-aware placement: linear ids with the same residue mod 8 share an XCD.
+  // XCD-aware placement: linear ids with the same residue mod 8 share an XCD,
+  // so the workgroups of one (sequence, head) share its L2.
   const int lin = blockIdx.x;
   const int xcd = lin % kXcds, r = lin / kXcds;
   const int vb = r % NVB;
@@ -311,8 +300,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
   }
 
   // ---- compute waves ----
-  const int vl = 16 * wave + c16;               // local state row of this lane
-  const int vrow = Cfg::ROWS * vb + vl;         // state row held by this lane
+  const int vrow = Cfg::ROWS * vb + 16 * wave + c16;  // state row held by this lane
   const size_t sbase = (static_cast<size_t>(n) * H + h) * D * D + static_cast<size_t>(vrow) * D;
   floatx4 S[ND];
 #pragma unroll
@@ -336,36 +324,13 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
       const uint16_t* Vl = reinterpret_cast<const uint16_t*>(buf + Cfg::OFF_V);
       const float* Gl = reinterpret_cast<const float*>(buf + Cfg::OFF_G);
 
-      // Z = K S^T (rows: tokens) and Y^T = S Q^T (rows: state rows).  The K
-      // and Q fragments of 32-block kb + 1 are read while the products of
-      // block kb run (two register buffers).
-      bf16x8 ka[2][NT], qa[2][NT];
-      auto read_kq = [&](int kb, int bi) {
-#pragma unroll
-        for (int a = 0; a < NT; ++a) {
-          const int t = 16 * a + c16, n8 = 4 * kb + g4;
-          ka[bi][a] = *reinterpret_cast<const bf16x8*>(Kl + t * D + 8 * (n8 ^ swz_tr(t, CHD)));
-          qa[bi][a] = *reinterpret_cast<const bf16x8*>(Ql + t * D + 8 * (n8 ^ swz(t, CHD)));
-        }
-      };
-      read_kq(0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-
-      // S^T as operand planes, 32 state columns per block, in natural order
-      // (lane group g holds columns 32 kb + 8 g .. +7): split the two stacked D
-      // tiles, then regroup with permlane swaps.  The 16x16x32 A and B
-      // fragments have the same lane layout, so these registers serve as B
-      // (rows of S^T) in K S^T and as A (rows of S) in S Q^T.
-      bf16x8 sb[KB][2];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        float x[8];
-#pragma unroll
-        for (int e2 = 0; e2 < 8; ++e2) x[e2] = S[2 * kb + e2 / 4][e2 & 3];
-        split8<2>(x, sb[kb]);
-#pragma unroll
-        for (int p = 0; p < 2; ++p) sb[kb][p] = slot_to_natural(sb[kb][p]);
-      }
+      // Z = K S^T (rows: tokens) and Y^T = S Q^T (rows: state rows), one
+      // 32-deep block of state columns at a time.  S^T enters as operand
+      // planes in natural order (lane group g holds columns 32 kb + 8 g .. +7):
+      // the two stacked D tiles are split, then regrouped with permlane swaps.
+      // The 16x16x32 A and B fragments have the same lane layout, so these
+      // registers serve as B (rows of S^T) in K S^T and as A (rows of S) in
+      // S Q^T.
       floatx4 Z[NT], Yt[NT];
 #pragma unroll
       for (int a = 0; a < NT; ++a) {
@@ -374,67 +339,63 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
       }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const int cur = kb & 1;
-        if (kb + 1 < KB) read_kq(kb + 1, cur ^ 1);
+        bf16x8 sbk[2];
+        {
+          float x[8];
+#pragma unroll
+          for (int e2 = 0; e2 < 8; ++e2) x[e2] = S[2 * kb + e2 / 4][e2 & 3];
+          split8<2>(x, sbk);
+#pragma unroll
+          for (int p = 0; p < 2; ++p) sbk[p] = slot_to_natural(sbk[p]);
+        }
+        bf16x8 ka[NT], qa[NT];
+#pragma unroll
+        for (int a = 0; a < NT; ++a) {
+          const int t = 16 * a + c16, n8 = 4 * kb + g4;
+          ka[a] = *reinterpret_cast<const bf16x8*>(Kl + t * D + 8 * (n8 ^ swz_tr(t, CHD)));
+          qa[a] = *reinterpret_cast<const bf16x8*>(Ql + t * D + 8 * (n8 ^ swz(t, CHD)));
+        }
         // plane pairs, smallest terms first; the four token tiles are
         // interleaved so that consecutive products are independent
 #pragma unroll
-        for (int a = 0; a < NT; ++a) Z[a] = mfma16x16x32(ka[cur][a], sb[kb][1], Z[a]);
+        for (int a = 0; a < NT; ++a) Z[a] = mfma16x16x32(ka[a], sbk[1], Z[a]);
 #pragma unroll
-        for (int a = 0; a < NT; ++a) Z[a] = mfma16x16x32(ka[cur][a], sb[kb][0], Z[a]);
+        for (int a = 0; a < NT; ++a) Z[a] = mfma16x16x32(ka[a], sbk[0], Z[a]);
 #pragma unroll
-        for (int a = 0; a < NT; ++a) Yt[a] = mfma16x16x32(sb[kb][1], qa[cur][a], Yt[a]);
+        for (int a = 0; a < NT; ++a) Yt[a] = mfma16x16x32(sbk[1], qa[a], Yt[a]);
 #pragma unroll
-        for (int a = 0; a < NT; ++a) Yt[a] = mfma16x16x32(sb[kb][0], qa[cur][a], Yt[a]);
-        if (kb + 1 < KB) interleave<2 * NT, 4 * NT>();
-        __builtin_amdgcn_sched_barrier(0);
+        for (int a = 0; a < NT; ++a) Yt[a] = mfma16x16x32(sbk[0], qa[a], Yt[a]);
       }
 
-      // The chunk's gates, v and T, read before any of their uses.
-      floatx4 gam[NT], dg[NT], bet[NT];
-      float gt[NT];
-      shortx4 vv[NT];
-#pragma unroll
-      for (int a = 0; a < NT; ++a) {
-        gam[a] = *reinterpret_cast<const floatx4*>(Gl + 16 * a + 4 * g4);
-        dg[a] = *reinterpret_cast<const floatx4*>(Gl + C + 16 * a + 4 * g4);
-        bet[a] = *reinterpret_cast<const floatx4*>(Gl + 2 * C + 16 * a + 4 * g4);
-        gt[a] = Gl[16 * a + c16];
-        // v rows 16 a + 4 g + e at this lane's state row: a transpose read
-        vv[a] = read_tr4(Vl, Cfg::ROWS, CHV, 16 * a, 16 * wave, c16, g4);
-      }
-      // T block (i, j): lane (c, g) takes row 16 i + c, columns 16 j + 4 g .. +3
-      shortx4 tf[NT][NT][2];
-#pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        const int t = 16 * i + c16, ch = t < C / 2 ? CHC / 2 : CHC;
-#pragma unroll
-        for (int j = 0; j <= i; ++j) {
-          const int cchunk = 2 * j + (g4 >> 1);
-          const int off = tl_row<C>(t) + 8 * (cchunk ^ swz(t, ch)) + 4 * (g4 & 1);
-#pragma unroll
-          for (int p = 0; p < 2; ++p) tf[i][j][p] = *reinterpret_cast<const shortx4*>(Tl + p * TL + off);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-
-      // R = diag(beta) (V - diag(gamma) Z) as planes, then U = T R over the
-      // lower blocks (16x16x16 products: R's D tiles are their B operands).
+      // R = diag(beta) (V - diag(gamma) Z) as planes (v rows 16 a + 4 g + e at
+      // this lane's state row: a transpose read), then U = T R over the lower
+      // blocks with 16x16x16 products, R's D tiles being their B operands.  T
+      // block (i, j): lane (c, g) takes row 16 i + c, columns 16 j + 4 g .. +3.
       shortx4 rp[NT][2];
 #pragma unroll
       for (int a = 0; a < NT; ++a) {
+        const floatx4 gam = *reinterpret_cast<const floatx4*>(Gl + 16 * a + 4 * g4);
+        const floatx4 bet = *reinterpret_cast<const floatx4*>(Gl + 2 * C + 16 * a + 4 * g4);
+        const shortx4 vv = read_tr4(Vl, Cfg::ROWS, CHV, 16 * a, 16 * wave, c16, g4);
         floatx4 rr;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          rr[e] = bet[a][e] * (bf16_bits_to_f32(static_cast<uint16_t>(vv[a][e])) - gam[a][e] * Z[a][e]);
+          rr[e] = bet[e] * (bf16_bits_to_f32(static_cast<uint16_t>(vv[e])) - gam[e] * Z[a][e]);
         split4<2>(rr, rp[a]);
       }
       floatx4 U[NT];
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
+        const int t = 16 * i + c16, ch = t < C / 2 ? CHC / 2 : CHC;
         U[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j <= i; ++j) mma16_planes<2, 2>(U[i], tf[i][j], rp[j]);
+        for (int j = 0; j <= i; ++j) {
+          const int off = tl_row<C>(t) + 8 * ((2 * j + (g4 >> 1)) ^ swz(t, ch)) + 4 * (g4 & 1);
+          shortx4 tf[2];
+#pragma unroll
+          for (int p = 0; p < 2; ++p) tf[p] = *reinterpret_cast<const shortx4*>(Tl + p * TL + off);
+          mma16_planes<2, 2>(U[i], tf, rp[j]);
+        }
       }
 
       // U as operand planes (32 tokens per block, slot order), plain and
@@ -447,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
         for (int e2 = 0; e2 < 8; ++e2) {
           const int a0 = 2 * kb + e2 / 4, e = e2 & 3;
           x[e2] = U[a0][e];
-          xd[e2] = dg[a0][e] * U[a0][e];
+          xd[e2] = Gl[C + 16 * a0 + 4 * g4 + e] * U[a0][e];
         }
         split8<2>(x, ub[kb]);
         split8<2>(xd, udb[kb]);
@@ -456,28 +417,26 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
       // O^T = Y^T diag(gamma) + U^T P^T: lane (c, g) ends up with token
       // 16 a + c and state rows 4 g .. 4 g + 3 of its wave's tile.  P is zero
       // above the diagonal, so token tile a needs the 32-blocks kb <= a / 2.
-      bf16x8 pa[NT][CB][2];
-#pragma unroll
-      for (int a = 0; a < NT; ++a) {
-        const int t = 16 * a + c16, ch = t < C / 2 ? CHC / 2 : CHC;
-#pragma unroll
-        for (int kb = 0; kb <= a / 2; ++kb)
-#pragma unroll
-          for (int p = 0; p < 2; ++p)
-            pa[a][kb][p] = *reinterpret_cast<const bf16x8*>(
-                Pl + p * TL + tl_row<C>(t) + 8 * ((4 * kb + g4) ^ swz(t, ch)));
-      }
       floatx4 oa[NT];
 #pragma unroll
-      for (int a = 0; a < NT; ++a) oa[a] = Yt[a] * gt[a];
+      for (int a = 0; a < NT; ++a) oa[a] = Yt[a] * Gl[16 * a + c16];
 #pragma unroll
       for (int kb = 0; kb < CB; ++kb) {
+        bf16x8 pa[NT][2];
 #pragma unroll
-        for (int a = 2 * kb; a < NT; ++a) oa[a] = mfma16x16x32(ub[kb][1], pa[a][kb][0], oa[a]);
+        for (int a = 2 * kb; a < NT; ++a) {
+          const int t = 16 * a + c16, ch = t < C / 2 ? CHC / 2 : CHC;
 #pragma unroll
-        for (int a = 2 * kb; a < NT; ++a) oa[a] = mfma16x16x32(ub[kb][0], pa[a][kb][1], oa[a]);
+          for (int p = 0; p < 2; ++p)
+            pa[a][p] = *reinterpret_cast<const bf16x8*>(Pl + p * TL + tl_row<C>(t) +
+                                                        8 * ((4 * kb + g4) ^ swz(t, ch)));
+        }
 #pragma unroll
-        for (int a = 2 * kb; a < NT; ++a) oa[a] = mfma16x16x32(ub[kb][0], pa[a][kb][0], oa[a]);
+        for (int a = 2 * kb; a < NT; ++a) oa[a] = mfma16x16x32(ub[kb][1], pa[a][0], oa[a]);
+#pragma unroll
+        for (int a = 2 * kb; a < NT; ++a) oa[a] = mfma16x16x32(ub[kb][0], pa[a][1], oa[a]);
+#pragma unroll
+        for (int a = 2 * kb; a < NT; ++a) oa[a] = mfma16x16x32(ub[kb][0], pa[a][0], oa[a]);
       }
       {
         int tok0;
@@ -537,9 +496,8 @@ hipError_t scan_t(const void* q, const void* k, const void* v, const int32_t* cu
                   const int32_t* offs, const ChunkFactors& f, const float* state_in,
                   float* state_out, float* fixed, void* o, int N, int H, int n_slots, int T_total,
                   hipStream_t stream) {
-  constexpr int NVB = D / (16 * kComputeWaves);
   const int64_t pairs = static_cast<int64_t>(N) * H;
-  const int64_t groups = (pairs + kXcds - 1) / kXcds * kXcds * NVB;
+  const int64_t groups = (pairs + kXcds - 1) / kXcds * kXcds * ScanCfg<D, C>::NVB;
   if (groups > INT32_MAX) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((chunk_scan_kernel<D, C, OUTD>), dim3(static_cast<unsigned>(groups)),
                      dim3(kThreads), 0, stream, static_cast<const uint16_t*>(q),
