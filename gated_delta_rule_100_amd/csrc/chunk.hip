@@ -69,8 +69,8 @@ struct ChunkCfg {
   static constexpr int KVW_BYTES = TF ? TL_BYTES : OUT ? mx(KV_BYTES, W_BYTES) : KV_BYTES;
   static constexpr int AOFF_BYTES = r16(mx(NOFF, 1) * PT * BLK_PS * 2);
   static constexpr int DIAG_BLK = r16(mx(16 * 17 * 4, PT * BLK_PS * 2));  // A_ii fp32, then T_ii planes
-  static constexpr int P_BYTES = OUT || TF ? r16(PT * P_PS * 2) : 0;
-  static constexpr int GATE_BYTES = 6 * C * 4;
+  static constexpr int P_BYTES = TF ? r16(PT * TL_PLANE * 2) : OUT ? r16(PT * P_PS * 2) : 0;
+  static constexpr int GATE_BYTES = (6 * C + 4) * 4;  // six vectors and a spare slot
   static constexpr int OFF_KR = 0;
   static constexpr int OFF_VR = KT_BYTES;
   static constexpr int OFF_W = 0;                         // W planes overlay K/V (outputs)
@@ -225,23 +225,43 @@ struct ChunkWork {
     finish_gates(gv, bv);
   }
 
-  // g_t and beta_t of this chunk (zero past it), as load() reads them.
+  // g_t and beta_t of this thread's token (the chunk's last token past it), as
+  // load() reads them; finish_gates() zeroes the padding.  Every thread loads,
+  // with no branch, so the wait counts for these and later loads stay exact.
   __device__ void read_gates(const float* g, const float* beta, float& gv, float& bv) const {
-    gv = 0.f;
-    bv = 0.f;
-    if (tid < c && tid < C) {
-      gv = g[static_cast<size_t>(tok0 + tid) * H + h];
-      bv = beta[static_cast<size_t>(tok0 + tid) * H + h];
+    const size_t i = static_cast<size_t>(tok0 + (tid < c ? tid : c - 1)) * H + h;
+    gv = g[i];
+    bv = beta[i];
+  }
+
+  // Row fragments of every chunk row for the Gram products of the scan
+  // factors; rows past the chunk repeat its last token instead of being
+  // zeroed (their beta is zero, so they leave A alone, and the P rows they
+  // produce belong to outputs that are never stored), so every load is
+  // unconditional.
+  __device__ void rows_frags_clamped(const void* base, bf16x8 (&f)[NT][KB][PI]) const {
+    static_assert(IN == Dt::BF16, "bf16 rows");
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti) {
+      const int t = 16 * ti + c16 < c ? 16 * ti + c16 : c - 1;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        f[ti][kb][0] = *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(base) + tok_off(t) +
+                                                        32 * kb + 8 * g4);
     }
   }
 
-  // Gates into LDS and their prefix quantities G, gamma, D, beta gamma.
+  // Gates into LDS (zero past the chunk) and their prefix quantities G, gamma,
+  // D, beta gamma.  The padding is zeroed by a multiplication, not a select on
+  // the loaded value (which the compiler would turn back into a conditional
+  // load), and every thread writes (threads past C to the spare slot), so no
+  // branch sits between the loads of gv, bv and their use.
   __device__ void finish_gates(float gv, float bv) {
-    if (tid < C) {
-      sg[tid] = gv;
-      sb[tid] = bv;
-    }
-    __syncthreads();
+    const float keep = tid < c && tid < C ? 1.f : 0.f;
+    float* spare = sg + 6 * C;
+    *(tid < C ? sg + tid : spare) = gv * keep;
+    *(tid < C ? sb + tid : spare + 1) = bv * keep;
+    lds_barrier();  // row loads may stay in flight
     if (tid < C) {
       // Sequential prefix in a fixed order: every thread forms the same G_C.
       float G = 0.f, Gt = 0.f;
@@ -255,7 +275,7 @@ struct ChunkWork {
       sD[tid] = expf(G - Gt);
       sbg[tid] = sb[tid] * gam;
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // A_ts = beta_t Gamma_ts (k_t . k_s), s < t: diagonal blocks in fp32
@@ -315,6 +335,77 @@ struct ChunkWork {
         const int t = idx / (Cfg::Cp - C), s = C + idx % (Cfg::Cp - C);
 #pragma unroll
         for (int p = 0; p < PT; ++p) Pp()[p * Cfg::P_PS + t * Cfg::LDP + s] = 0;
+      }
+    }
+  }
+
+  // Both Gram products of the scan factors, with the operands swapped so that
+  // a lane holds four consecutive columns of one row (row 16 ti + c, columns
+  // 16 tj + 4 g .. +3), which go to LDS as one 8-byte write per plane:
+  //   A_ts = beta_t Gamma_ts (k_t . k_s), s < t: diagonal blocks fp32 (zero on
+  //     and above the diagonal), strictly lower blocks as planes;
+  //   P = (Q K^T) (.) Gamma (s <= t, zero elsewhere) as planes in the compact
+  //     lower layout (rows t < C/2 keep C/2 columns), each row in operand-slot
+  //     order: column 16 tj + c of 32-block tj/2 sits at slot
+  //     8 (c/4) + 4 (tj % 2) + c % 4.
+  __device__ void gram_t(const bf16x8 (&kf)[NT][KB][PI], const bf16x8 (&qf)[NT][KB][PI]) {
+    static_assert(TF, "factors layout");
+    int tcount = 0;
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti) {
+#pragma unroll
+      for (int tj = 0; tj <= ti; ++tj, ++tcount) {
+        if ((tcount & 3) != wave) continue;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) mma_planes<PI, PI>(acc, kf[tj][kb], kf[ti][kb]);
+        const int t = 16 * ti + c16;
+        float a[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s = 16 * tj + 4 * g4 + e;
+          a[e] = s < t ? sb[t] * expf(sG[t] - sG[s]) * acc[e] : 0.f;
+        }
+        if (ti == tj) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Adiag(ti)[c16 * 17 + 4 * g4 + e] = a[e];
+        } else {
+          uint32_t lo[PT], hi[PT];
+          split2<PT>(a[0], a[1], lo);
+          split2<PT>(a[2], a[3], hi);
+          uint16_t* blk = Aoff(ti * (ti - 1) / 2 + tj) + c16 * Cfg::LDB + 4 * g4;
+#pragma unroll
+          for (int p = 0; p < PT; ++p)
+            *reinterpret_cast<uint2*>(blk + p * Cfg::BLK_PS) = make_uint2(lo[p], hi[p]);
+        }
+      }
+    }
+    int pcount = 0;
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti) {
+#pragma unroll
+      for (int tj = 0; tj < NT; ++tj) {
+        if (ti < NT / 2 && tj >= NT / 2) continue;  // not stored
+        if ((pcount++ & 3) != wave) continue;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (tj <= ti) {
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) mma_planes<PI, PI>(acc, kf[tj][kb], qf[ti][kb]);
+        }
+        const int t = 16 * ti + c16;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s = 16 * tj + 4 * g4 + e;
+          x[e] = s <= t ? acc[e] * expf(sG[t] - sG[s]) : 0.f;
+        }
+        uint32_t lo[PT], hi[PT];
+        split2<PT>(x[0], x[1], lo);
+        split2<PT>(x[2], x[3], hi);
+        uint16_t* dst = Pp() + tl_row(t) + 32 * (tj >> 1) + 8 * g4 + 4 * (tj & 1);
+#pragma unroll
+        for (int p = 0; p < PT; ++p)
+          *reinterpret_cast<uint2*>(dst + p * Cfg::TL_PLANE) = make_uint2(lo[p], hi[p]);
       }
     }
   }
@@ -423,8 +514,9 @@ struct ChunkWork {
     return t < C / 2 ? t * (C / 2) : (C / 2) * (C / 2) + (t - C / 2) * C;
   }
 
-  // T = (I + A)^{-1}, lower triangular, into the compact planes at Tl(): wave
-  // j forms column block j by block forward substitution,
+  // T = (I + A)^{-1}, lower triangular, into the compact planes at Tl() (rows
+  // in operand-slot order, as P): wave j forms column block j by block
+  // forward substitution,
   //   T_jj from the diagonal inversion,  T_ij = -T_ii sum_{j <= m < i} A_im T_mj,
   // every block in D-tile layout, which is the B operand of the next product.
   // The blocks of the compact layout above the diagonal are zeroed.
@@ -460,6 +552,8 @@ struct ChunkWork {
         mma16_planes<PT, PT>(x, tii, ap);
         X[i] = -x;
       }
+      // column 16 j + c of 32-block j/2 sits at slot 8 (c/4) + 4 (j % 2) + c % 4
+      const int col = 32 * (j >> 1) + 8 * (c16 >> 2) + 4 * (j & 1) + (c16 & 3);
 #pragma unroll
       for (int i = j; i < NT; ++i)
 #pragma unroll
@@ -468,7 +562,7 @@ struct ChunkWork {
           split_planes<PT>(X[i][e], sp);
           const int t = 16 * i + 4 * g4 + e;
 #pragma unroll
-          for (int p = 0; p < PT; ++p) Tl()[p * Cfg::TL_PLANE + tl_row(t) + 16 * j + c16] = sp[p];
+          for (int p = 0; p < PT; ++p) Tl()[p * Cfg::TL_PLANE + tl_row(t) + col] = sp[p];
         }
       // blocks above the diagonal that the compact layout stores: zeros
 #pragma unroll
@@ -477,8 +571,7 @@ struct ChunkWork {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
-          for (int p = 0; p < PT; ++p)
-            Tl()[p * Cfg::TL_PLANE + tl_row(16 * i + 4 * g4 + e) + 16 * j + c16] = 0;
+          for (int p = 0; p < PT; ++p) Tl()[p * Cfg::TL_PLANE + tl_row(16 * i + 4 * g4 + e) + col] = 0;
       }
     }
   }
@@ -704,9 +797,8 @@ __global__ __launch_bounds__(256, 2) void chunk_out_kernel(
 // which is (I + A) U = diag(beta) V - diag(beta gamma) K S0^T solved with the
 // inverse instead of forming W and Ut here.
 //
-// T rows are stored as they are; P rows (the B operand of a product whose
-// other operand comes from D tiles) store their contraction index in
-// operand-slot order: inside every 32-wide block, lane group g's eight slots
+// T and P rows (operands of products whose other operand comes from D tiles)
+// store their contraction index in operand-slot order: inside every 32-wide block, lane group g's eight slots
 // (elements 4g..4g+3 and 16+4g..16+4g+3, the order in which D tiles stack,
 // mfma_planes.h) are adjacent, so that the scan reads each fragment with one
 // 16-byte load.
@@ -730,14 +822,16 @@ __global__ __launch_bounds__(256, 2) void chunk_factors_kernel(
   W_ w;
   w.init(smem, ct.tok0, ct.c, h, H);
   {
-    bf16x8 kf[NT][KB][1], qf[NT][KB][1];
-    w.rows_frags(k, kf);
-    w.rows_frags(q, qf);
+    // the gates first: loads complete in order, so their prefix overlaps the
+    // row loads
     float gv, bv;
     w.read_gates(g, beta, gv, bv);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 kf[NT][KB][1], qf[NT][KB][1];
+    w.rows_frags_clamped(k, kf);
+    w.rows_frags_clamped(q, qf);
     w.finish_gates(gv, bv);
-    w.gram_kk(kf);
-    w.gram_qk(qf, kf);
+    w.gram_t(kf, qf);
   }
   __syncthreads();
   w.invert_diagonal();
@@ -751,28 +845,13 @@ __global__ __launch_bounds__(256, 2) void chunk_factors_kernel(
     gt[2 * C + w.tid] = w.sb[w.tid];
     gt[3 * C + w.tid] = 0.f;
   }
-  // P planes, compact lower layout, each row in slot order: row chunk n8
-  // (16 bytes) is made of the 4-element groups starting at 32 (n8/4) + 4 (n8%4)
-  // and 16 elements later.
-  auto slot_chunk = [](const uint16_t* row, int n8) {
-    const int c0 = 32 * (n8 >> 2) + 4 * (n8 & 3);
-    const uint2 lo = *reinterpret_cast<const uint2*>(row + c0);
-    const uint2 hi = *reinterpret_cast<const uint2*>(row + c0 + 16);
-    return make_uint4(lo.x, lo.y, hi.x, hi.y);
-  };
+  __syncthreads();  // T and P planes complete
+  uint16_t* tg = f.t + slot * PT * TLP;
   uint16_t* pg = f.p + slot * PT * TLP;
   for (int idx = w.tid; idx < PT * TLP / 8; idx += 256) {
-    const int pl = idx / (TLP / 8), r = idx % (TLP / 8);
-    constexpr int LO = (C / 2) * (C / 16);  // 16-byte chunks of the short rows
-    const int t = r < LO ? r / (C / 16) : C / 2 + (r - LO) / (C / 8);
-    const int n8 = r < LO ? r % (C / 16) : (r - LO) % (C / 8);
-    *reinterpret_cast<uint4*>(pg + pl * TLP + 8 * r) =
-        slot_chunk(w.Pp() + pl * Cfg::P_PS + t * Cfg::LDP, n8);
-  }
-  __syncthreads();  // T planes complete
-  uint16_t* tg = f.t + slot * PT * TLP;
-  for (int idx = w.tid; idx < PT * TLP / 8; idx += 256)
     *reinterpret_cast<uint4*>(tg + 8 * idx) = *reinterpret_cast<const uint4*>(w.Tl() + 8 * idx);
+    *reinterpret_cast<uint4*>(pg + 8 * idx) = *reinterpret_cast<const uint4*>(w.Pp() + 8 * idx);
+  }
 }
 
 template <int D, int C>

@@ -23,6 +23,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
+// (lgkmcnt) but not for global loads still in flight, which __syncthreads()
+// also drains (its release fence covers global memory).  The s_waitcnt
+// immediate leaves vmcnt and expcnt at their maxima (no constraint) and sets
+// lgkmcnt to zero; the empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15); every lane of the
 // row receives the total.  quad_perm [1,0,3,2] and [2,3,0,1] fold each quad,
 // then row_ror:4 and row_ror:8 fold the four quads.

@@ -25,8 +25,9 @@
 // For the contractions over dk the state is split into bf16 hi/lo planes and
 // regrouped into natural fragments with permlane swaps, which serve as B (rows
 // of S^T) in K S^T and as A (rows of S) in S Q^T.  Z, R and U are D tiles with
-// tokens as rows, so R feeds the 16x16x16 products with T directly, and U
-// feeds the output and state products.  k, q, v are exact bf16; fp32 operands
+// tokens as rows; two of them stacked are an operand fragment in slot order,
+// which is how R meets T (whose rows are stored in slot order) and U meets P
+// and K^T.  k, q, v are exact bf16; fp32 operands
 // are hi/lo planes.  The compute waves read only LDS and write their outputs
 // and states straight to global memory.
 //
@@ -367,21 +368,28 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
         for (int a = 0; a < NT; ++a) Yt[a] = mfma16x16x32(sbk[0], qa[a], Yt[a]);
       }
 
-      // R = diag(beta) (V - diag(gamma) Z) as planes (v rows 16 a + 4 g + e at
-      // this lane's state row: a transpose read), then U = T R over the lower
-      // blocks with 16x16x16 products, R's D tiles being their B operands.  T
-      // block (i, j): lane (c, g) takes row 16 i + c, columns 16 j + 4 g .. +3.
-      shortx4 rp[NT][2];
+      // R = diag(beta) (V - diag(gamma) Z) (v rows 16 a + 4 g + e at this
+      // lane's state row: a transpose read), as operand planes of 32 tokens
+      // (two stacked D tiles, slot order), then U = T R over the lower blocks:
+      // T rows are stored in slot order, so the T fragment of row 16 i + c and
+      // 32-block m is one 16-byte read per plane.
+      floatx4 R[NT];
 #pragma unroll
       for (int a = 0; a < NT; ++a) {
         const floatx4 gam = *reinterpret_cast<const floatx4*>(Gl + 16 * a + 4 * g4);
         const floatx4 bet = *reinterpret_cast<const floatx4*>(Gl + 2 * C + 16 * a + 4 * g4);
         const shortx4 vv = read_tr4(Vl, Cfg::ROWS, CHV, 16 * a, 16 * wave, c16, g4);
-        floatx4 rr;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          rr[e] = bet[e] * (bf16_bits_to_f32(static_cast<uint16_t>(vv[e])) - gam[e] * Z[a][e]);
-        split4<2>(rr, rp[a]);
+          R[a][e] = bet[e] * (bf16_bits_to_f32(static_cast<uint16_t>(vv[e])) - gam[e] * Z[a][e]);
+      }
+      bf16x8 rb[CB][2];
+#pragma unroll
+      for (int m = 0; m < CB; ++m) {
+        float x[8];
+#pragma unroll
+        for (int e2 = 0; e2 < 8; ++e2) x[e2] = R[2 * m + e2 / 4][e2 & 3];
+        split8<2>(x, rb[m]);
       }
       floatx4 U[NT];
 #pragma unroll
@@ -389,12 +397,15 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
         const int t = 16 * i + c16, ch = t < C / 2 ? CHC / 2 : CHC;
         U[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j <= i; ++j) {
-          const int off = tl_row<C>(t) + 8 * ((2 * j + (g4 >> 1)) ^ swz(t, ch)) + 4 * (g4 & 1);
-          shortx4 tf[2];
+        for (int m = 0; m <= i / 2; ++m) {
+          bf16x8 tf[2];
 #pragma unroll
-          for (int p = 0; p < 2; ++p) tf[p] = *reinterpret_cast<const shortx4*>(Tl + p * TL + off);
-          mma16_planes<2, 2>(U[i], tf, rp[j]);
+          for (int p = 0; p < 2; ++p)
+            tf[p] = *reinterpret_cast<const bf16x8*>(Tl + p * TL + tl_row<C>(t) +
+                                                     8 * ((4 * m + g4) ^ swz(t, ch)));
+          U[i] = mfma16x16x32(tf[1], rb[m][0], U[i]);
+          U[i] = mfma16x16x32(tf[0], rb[m][1], U[i]);
+          U[i] = mfma16x16x32(tf[0], rb[m][0], U[i]);
         }
       }
 
