@@ -193,11 +193,12 @@ size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int 
  *     sequence (two-level for long sequences with few heads), chunk outputs,
  *     final states.  Taken when L_out or M_out is given, for fp32 inputs or
  *     chunk 16, and for long sequences at low parallelism;
- *   - sequential scan: layout, per-chunk factors, then one pass per (sequence,
- *     head, block of state rows) that applies the fixup in factored form
- *     (S M_c + L_c = gamma_C S - (S W^T) diag(D) K + L_c, without forming M)
- *     and writes the outputs, the final states and, when given, fixed_out.
- *     Taken otherwise.
+ *   - sequential scan: layout, per-chunk factors T = (I + A)^{-1} and
+ *     P = (Q K^T) (.) Gamma, then one pass per (sequence, head, block of state
+ *     rows) that applies the UT transform and the fixup in factored form
+ *     (S M_c + L_c = gamma_C S + (diag(D) T diag(beta) (V - diag(gamma) K S^T))^T K,
+ *     without forming M, L, W or Ut) and writes the outputs, the final states
+ *     and, when given, fixed_out.  Taken otherwise.
  */
 gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v,
                              const float* g, const float* beta,
