@@ -211,28 +211,36 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
     // ---- copy waves: each issues a quarter of every region's copies (the
     // gates are one copy, issued by the first wave).
     if (c1 <= c0) return;
-    const int cw = wave - kComputeWaves;
-    // per-lane source offsets of this wave's copies
-    int krow[Cfg::SK], qrow[Cfg::SQ], vrow[Cfg::SV];       // chunk row of k / q / v lanes
-    uint32_t kcol[Cfg::SK], qcol[Cfg::SQ], vcol[Cfg::SV];  // byte offset inside the row
-    uint32_t toff[Cfg::STL];                               // byte offset in a T or P slot
+    // wave-uniform, so that LDS destinations (and M0) stay scalar
+    const int cw = __builtin_amdgcn_readfirstlane(wave - kComputeWaves);
+    const uint32_t row_bytes = 2u * static_cast<uint32_t>(H) * D;  // one token row of q, k, v
+    // per-lane source offsets of this wave's copies: chunk row and byte offset
+    // inside the row (k, q, v), the two combined for a full chunk, and the
+    // byte offset in a T or P slot
+    int krow[Cfg::SK], qrow[Cfg::SQ], vrow[Cfg::SV];
+    uint32_t kcol[Cfg::SK], qcol[Cfg::SQ], vcol[Cfg::SV];
+    uint32_t kfull[Cfg::SK], qfull[Cfg::SQ], vfull[Cfg::SV];
+    uint32_t toff[Cfg::STL];
 #pragma unroll
     for (int x = 0; x < Cfg::SK; ++x) {
       const int p = 64 * (cw + kCopyWaves * x) + lane, t = p / CHD, pc = p % CHD;
       krow[x] = t;
       kcol[x] = 16u * (pc ^ swz_tr(t, CHD));
+      kfull[x] = static_cast<uint32_t>(t) * row_bytes + kcol[x];
     }
 #pragma unroll
     for (int x = 0; x < Cfg::SQ; ++x) {
       const int p = 64 * (cw + kCopyWaves * x) + lane, t = p / CHD, pc = p % CHD;
       qrow[x] = t;
       qcol[x] = 16u * (pc ^ swz(t, CHD));
+      qfull[x] = static_cast<uint32_t>(t) * row_bytes + qcol[x];
     }
 #pragma unroll
     for (int x = 0; x < Cfg::SV; ++x) {
       const int p = 64 * (cw + kCopyWaves * x) + lane, t = p / CHV, pc = p % CHV;
       vrow[x] = t;
       vcol[x] = 2u * (Cfg::ROWS * vb) + 16u * (pc ^ swz_tr(t, CHV));
+      vfull[x] = static_cast<uint32_t>(t) * row_bytes + vcol[x];
     }
 #pragma unroll
     for (int x = 0; x < Cfg::STL; ++x) {
@@ -250,10 +258,10 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
       }
       toff[x] = 2u * (pl * TL + tl_row<C>(t) + 8 * (pc ^ swz(t, ch)));
     }
-    const uint32_t row_bytes = 2u * static_cast<uint32_t>(H) * D;  // one token row of q, k, v
-    // Chunk s into buffer (s - c0) & 1.  Rows past the chunk repeat its last
-    // token (their beta is zero, so they leave U, O and the state alone), and
-    // every row read stays inside the inputs.
+    const uint32_t goff = 16u * lane;
+    // Chunk s into buffer (s - c0) & 1.  In a chunk shorter than C, rows past
+    // its end repeat its last token (their beta is zero, so they leave U, O
+    // and the state alone), and every row read stays inside the inputs.
     auto copy_chunk = [&](int s) {
       int tok;
       const int cl = chunk_range(s, tok);
@@ -268,25 +276,32 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
       const char* ts = reinterpret_cast<const char*>(f.t + slot * 2 * TL);
       const char* ps = reinterpret_cast<const char*>(f.p + slot * 2 * TL);
       unsigned char* buf = smem + ((s - c0) & 1) * Cfg::BUF;
+      if (last == C - 1) {
 #pragma unroll
-      for (int x = 0; x < Cfg::SK; ++x)
-        copy16(ks + static_cast<uint32_t>(krow[x] < last ? krow[x] : last) * row_bytes + kcol[x],
-               buf + Cfg::OFF_K + 1024 * (cw + kCopyWaves * x));
+        for (int x = 0; x < Cfg::SK; ++x) copy16(ks + kfull[x], buf + Cfg::OFF_K + 1024 * (cw + kCopyWaves * x));
 #pragma unroll
-      for (int x = 0; x < Cfg::SQ; ++x)
-        copy16(qs + static_cast<uint32_t>(qrow[x] < last ? qrow[x] : last) * row_bytes + qcol[x],
-               buf + Cfg::OFF_Q + 1024 * (cw + kCopyWaves * x));
+        for (int x = 0; x < Cfg::SQ; ++x) copy16(qs + qfull[x], buf + Cfg::OFF_Q + 1024 * (cw + kCopyWaves * x));
 #pragma unroll
-      for (int x = 0; x < Cfg::STL; ++x)
-        copy16(ts + toff[x], buf + Cfg::OFF_T + 1024 * (cw + kCopyWaves * x));
+        for (int x = 0; x < Cfg::SV; ++x) copy16(vs + vfull[x], buf + Cfg::OFF_V + 1024 * (cw + kCopyWaves * x));
+      } else {
 #pragma unroll
-      for (int x = 0; x < Cfg::STL; ++x)
-        copy16(ps + toff[x], buf + Cfg::OFF_P + 1024 * (cw + kCopyWaves * x));
+        for (int x = 0; x < Cfg::SK; ++x)
+          copy16(ks + static_cast<uint32_t>(krow[x] < last ? krow[x] : last) * row_bytes + kcol[x],
+                 buf + Cfg::OFF_K + 1024 * (cw + kCopyWaves * x));
 #pragma unroll
-      for (int x = 0; x < Cfg::SV; ++x)
-        copy16(vs + static_cast<uint32_t>(vrow[x] < last ? vrow[x] : last) * row_bytes + vcol[x],
-               buf + Cfg::OFF_V + 1024 * (cw + kCopyWaves * x));
-      if (cw == 0) copy16(f.gate + slot * 4 * C + 4 * lane, buf + Cfg::OFF_G);
+        for (int x = 0; x < Cfg::SQ; ++x)
+          copy16(qs + static_cast<uint32_t>(qrow[x] < last ? qrow[x] : last) * row_bytes + qcol[x],
+                 buf + Cfg::OFF_Q + 1024 * (cw + kCopyWaves * x));
+#pragma unroll
+        for (int x = 0; x < Cfg::SV; ++x)
+          copy16(vs + static_cast<uint32_t>(vrow[x] < last ? vrow[x] : last) * row_bytes + vcol[x],
+                 buf + Cfg::OFF_V + 1024 * (cw + kCopyWaves * x));
+      }
+#pragma unroll
+      for (int x = 0; x < Cfg::STL; ++x) copy16(ts + toff[x], buf + Cfg::OFF_T + 1024 * (cw + kCopyWaves * x));
+#pragma unroll
+      for (int x = 0; x < Cfg::STL; ++x) copy16(ps + toff[x], buf + Cfg::OFF_P + 1024 * (cw + kCopyWaves * x));
+      if (cw == 0) copy16(reinterpret_cast<const char*>(f.gate + slot * 4 * C) + goff, buf + Cfg::OFF_G);
     };
 
     copy_chunk(c0);
