@@ -68,7 +68,8 @@ struct ChunkCfg {
   static constexpr int TL_BYTES = TF ? r16(PT * TL_PLANE * 2) : 0;
   static constexpr int KVW_BYTES = TF ? TL_BYTES : OUT ? mx(KV_BYTES, W_BYTES) : KV_BYTES;
   static constexpr int AOFF_BYTES = r16(mx(NOFF, 1) * PT * BLK_PS * 2);
-  static constexpr int DIAG_BLK = r16(mx(16 * 17 * 4, PT * BLK_PS * 2));  // A_ii fp32, then T_ii planes
+  static constexpr int LDA = 20;                          // row stride of A_ii (16-byte rows)
+  static constexpr int DIAG_BLK = r16(mx(16 * LDA * 4, PT * BLK_PS * 2));  // A_ii fp32, then T_ii planes
   static constexpr int P_BYTES = TF ? r16(PT * TL_PLANE * 2) : OUT ? r16(PT * P_PS * 2) : 0;
   static constexpr int GATE_BYTES = (6 * C + 4) * 4;  // six vectors and a spare slot
   static constexpr int OFF_KR = 0;
@@ -296,7 +297,7 @@ struct ChunkWork {
           const int t = 16 * ti + r, s = 16 * tj + c16;
           const float a = s < t ? sb[t] * expf(sG[t] - sG[s]) * acc[e] : 0.f;
           if (ti == tj) {
-            Adiag(ti)[r * 17 + c16] = a;
+            Adiag(ti)[r * Cfg::LDA + c16] = a;
           } else {
             uint16_t sp[PT];
             split_planes<PT>(a, sp);
@@ -367,8 +368,7 @@ struct ChunkWork {
           a[e] = s < t ? sb[t] * expf(sG[t] - sG[s]) * acc[e] : 0.f;
         }
         if (ti == tj) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) Adiag(ti)[c16 * 17 + 4 * g4 + e] = a[e];
+          *reinterpret_cast<floatx4*>(Adiag(ti) + c16 * Cfg::LDA + 4 * g4) = floatx4{a[0], a[1], a[2], a[3]};
         } else {
           uint32_t lo[PT], hi[PT];
           split2<PT>(a[0], a[1], lo);
@@ -420,7 +420,12 @@ struct ChunkWork {
 #pragma unroll
       for (int t = 1; t < 16; ++t)
 #pragma unroll
-        for (int s = 0; s < t; ++s) a[t][s] = A[t * 17 + s];
+        for (int s4 = 0; s4 < t; s4 += 4) {
+          const floatx4 r = *reinterpret_cast<const floatx4*>(A + t * Cfg::LDA + s4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (s4 + e < t) a[t][s4 + e] = r[e];
+        }
       float x[16];
 #pragma unroll
       for (int t = 0; t < 16; ++t) x[t] = t == j ? 1.f : 0.f;
