@@ -3,14 +3,16 @@
 // Per (sequence, head) the fp32 state S (dv x dk, dk contiguous) is read once
 // and written once; that stream is the whole cost (64 KiB each way per head at
 // dk = dv = 128), so the kernel is an HBM stream:
-//   * one 256-thread workgroup per (sequence, head);
+//   * rows are independent, so each 256-thread workgroup takes 32 rows of one
+//     (sequence, head) (16 KiB): many small workgroups keep the stream
+//     smoother than one 64 KiB workgroup per head (measured 6.2 against
+//     5.8 TB/s on the decode shape, with bitwise-equal results);
 //   * 16 lanes per state row, each lane holding dk/16 columns as 16-byte
 //     vectors, so one wave-wide load covers four contiguous row segments of
 //     256 bytes -- fully used 128-byte lines;
-//   * every load of the state is issued before any arithmetic (64 KiB per
-//     workgroup in flight), non-temporal (the state is touched once), the
-//     rank-1 update happens in registers and the rows are stored back in
-//     place; no LDS (the state has no reuse -- the
+//   * every load of the state is issued before any arithmetic, non-temporal
+//     (the state is touched once), the rank-1 update happens in registers and
+//     the rows are stored back in place; no LDS (the state has no reuse -- the
 //     register-direct load of the FlashInfer PR #7156 page, code analysis 1);
 //   * the two row dot products (s.k before the update, s'.q after) are
 //     16-lane DPP reductions.
@@ -24,8 +26,40 @@ namespace gdr {
 namespace {
 
 constexpr int kDecodeThreads = 256;
+constexpr int kDecodeRowsPerThread = 2;  // 32 state rows per workgroup
+constexpr int kMtpThreads = 256;
 
-template <int DK, int DV, Dt IN, Dt OUT>
+// One state row of the decode step, shared by every decode-type kernel so that
+// their results agree bit for bit: a = s.k, u = beta (v - alpha a),
+// s' = alpha s + u k in place, returns s'.q (both dots reduced over the row's
+// 16 lanes).  Contraction into fused multiply-adds is switched off and the
+// fused operations are written out, so the instruction sequence does not
+// depend on how the compiler schedules the surrounding kernel.
+template <int VEC>
+__device__ __forceinline__ float update_row(floatx4 (&st)[VEC], const float (&kk)[VEC][4],
+                                            const float (&qq)[VEC][4], float alpha, float b,
+                                            float v) {
+#pragma clang fp contract(off)
+  float a = 0.f;
+#pragma unroll
+  for (int j = 0; j < VEC; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a = __builtin_fmaf(st[j][e], kk[j][e], a);
+  a = row16_sum(a);
+  const float u = b * __builtin_fmaf(-alpha, a, v);
+  float p = 0.f;
+#pragma unroll
+  for (int j = 0; j < VEC; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = __builtin_fmaf(alpha, st[j][e], u * kk[j][e]);
+      st[j][e] = x;
+      p = __builtin_fmaf(x, qq[j][e], p);
+    }
+  return row16_sum(p);
+}
+
+template <int DK, int DV, Dt IN, Dt OUT, int RPT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
@@ -34,10 +68,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   constexpr int CPL = DK / LPR;         // columns per lane (8 or 4)
   constexpr int VEC = CPL / 4;          // float4 per lane per row
   constexpr int RG = kDecodeThreads / LPR;  // row groups (16)
-  constexpr int RPT = DV / RG;          // rows per thread (8 or 4)
-  static_assert(CPL % 4 == 0 && DV % RG == 0, "shape");
+  constexpr int ROWS = RG * RPT;        // state rows per workgroup
+  constexpr int WPP = DV / ROWS;        // workgroups per (sequence, head)
+  static_assert(CPL % 4 == 0 && DV % ROWS == 0, "shape");
 
-  const int pair = blockIdx.x;
+  const int pair = blockIdx.x / WPP, r0 = (blockIdx.x % WPP) * ROWS;
   if (pair >= NH) return;
   const int lane16 = threadIdx.x & (LPR - 1);
   const int rg = threadIdx.x / LPR;
@@ -49,7 +84,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   floatx4 st[RPT][VEC];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int row = rg + RG * i;
+    const int row = r0 + rg + RG * i;
 #pragma unroll
     for (int j = 0; j < VEC; ++j)
       st[i][j] = __builtin_nontemporal_load(&S[(row * DK + 4 * lane16 + 64 * j) / 4]);
@@ -63,35 +98,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   }
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
-    vv[i] = load_scalar<IN>(v, static_cast<size_t>(pair) * DV + rg + RG * i);
+    vv[i] = load_scalar<IN>(v, static_cast<size_t>(pair) * DV + r0 + rg + RG * i);
   const float alpha = expf(g[pair]);
   const float b = beta[pair];
 
   float oi[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    float a = 0.f;
-#pragma unroll
-    for (int j = 0; j < VEC; ++j)
-      a += st[i][j][0] * kk[j][0] + st[i][j][1] * kk[j][1] + st[i][j][2] * kk[j][2] +
-           st[i][j][3] * kk[j][3];
-    a = row16_sum(a);
-    const float u = b * (vv[i] - alpha * a);
-    float p = 0.f;
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      floatx4 s = st[i][j];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s[e] = alpha * s[e] + u * kk[j][e];
-      st[i][j] = s;
-      p += s[0] * qq[j][0] + s[1] * qq[j][1] + s[2] * qq[j][2] + s[3] * qq[j][3];
-    }
-    oi[i] = row16_sum(p);
-  }
+  for (int i = 0; i < RPT; ++i) oi[i] = update_row<VEC>(st[i], kk, qq, alpha, b, vv[i]);
 
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int row = rg + RG * i;
+    const int row = r0 + rg + RG * i;
 #pragma unroll
     for (int j = 0; j < VEC; ++j)
       __builtin_nontemporal_store(st[i][j], &S[(row * DK + 4 * lane16 + 64 * j) / 4]);
@@ -99,7 +116,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   // lane i of each row group writes the output of its i-th row
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
-    if (lane16 == i) store_scalar<OUT>(o, static_cast<size_t>(pair) * DV + rg + RG * i, oi[i]);
+    if (lane16 == i) store_scalar<OUT>(o, static_cast<size_t>(pair) * DV + r0 + rg + RG * i, oi[i]);
 }
 
 // Multi-token decode: T tokens per (sequence, head) applied in order to a state
@@ -110,14 +127,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
 // final state to `state_out` (which may be the input state; NULL keeps the
 // input state as it is).  The per-token arithmetic is that of decode_kernel.
 template <int DK, int DV, Dt IN, Dt OUT>
-__global__ __launch_bounds__(kDecodeThreads) void mtp_kernel(
+__global__ __launch_bounds__(kMtpThreads) void mtp_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* state_in,
     float* state_out, void* __restrict__ o, float* __restrict__ inter, int NH, int H, int T) {
   constexpr int LPR = 16;
   constexpr int CPL = DK / LPR;
   constexpr int VEC = CPL / 4;
-  constexpr int RG = kDecodeThreads / LPR;
+  constexpr int RG = kMtpThreads / LPR;
   constexpr int RPT = DV / RG;
   static_assert(CPL % 4 == 0 && DV % RG == 0, "shape");
 
@@ -161,25 +178,7 @@ __global__ __launch_bounds__(kDecodeThreads) void mtp_kernel(
     const size_t orow = ((static_cast<size_t>(n) * T + t) * H + h) * DV;
     float oi[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      float a = 0.f;
-#pragma unroll
-      for (int j = 0; j < VEC; ++j)
-        a += st[i][j][0] * kk[j][0] + st[i][j][1] * kk[j][1] + st[i][j][2] * kk[j][2] +
-             st[i][j][3] * kk[j][3];
-      a = row16_sum(a);
-      const float u = bb * (vv[i] - alpha * a);
-      float p = 0.f;
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) {
-        floatx4 s = st[i][j];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[e] = alpha * s[e] + u * kk[j][e];
-        st[i][j] = s;
-        p += s[0] * qq[j][0] + s[1] * qq[j][1] + s[2] * qq[j][2] + s[3] * qq[j][3];
-      }
-      oi[i] = row16_sum(p);
-    }
+    for (int i = 0; i < RPT; ++i) oi[i] = update_row<VEC>(st[i], kk, qq, alpha, bb, vv[i]);
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
       if (lane16 == i) store_scalar<OUT>(o, orow + rg + RG * i, oi[i]);
@@ -221,7 +220,7 @@ template <int DK, int DV, Dt IN, Dt OUT>
 hipError_t launch_mtp_t(const void* q, const void* k, const void* v, const float* g,
                         const float* beta, const float* state_in, float* state_out, void* o,
                         float* inter, int NH, int H, int T, hipStream_t stream) {
-  hipLaunchKernelGGL((mtp_kernel<DK, DV, IN, OUT>), dim3(NH), dim3(kDecodeThreads), 0, stream, q,
+  hipLaunchKernelGGL((mtp_kernel<DK, DV, IN, OUT>), dim3(NH), dim3(kMtpThreads), 0, stream, q,
                      k, v, g, beta, state_in, state_out, o, inter, NH, H, T);
   return hipGetLastError();
 }
@@ -230,8 +229,13 @@ template <int DK, int DV, Dt IN, Dt OUT>
 hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* g,
                            const float* beta, float* state, void* o, int NH,
                            hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<DK, DV, IN, OUT>), dim3(NH), dim3(kDecodeThreads), 0, stream,
-                     q, k, v, g, beta, state, o, NH);
+  constexpr int RG = kDecodeThreads / 16;  // row groups
+  constexpr int RPT = kDecodeRowsPerThread < DV / RG ? kDecodeRowsPerThread : DV / RG;
+  constexpr int WPP = DV / (RPT * RG);
+  const int64_t groups = static_cast<int64_t>(NH) * WPP;
+  if (groups > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((decode_kernel<DK, DV, IN, OUT, RPT>), dim3(static_cast<unsigned>(groups)),
+                     dim3(kDecodeThreads), 0, stream, q, k, v, g, beta, state, o, NH);
   return hipGetLastError();
 }
 

@@ -37,15 +37,18 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15); every lane of the
-// row receives the total.  quad_perm [1,0,3,2] and [2,3,0,1] fold each quad,
-// then row_ror:4 and row_ror:8 fold the four quads.
+// row receives the same bits.  Each stage adds the value of a partner lane
+// whose partner is the lane itself (quad_perm [1,0,3,2] and [2,3,0,1] within
+// a quad, row_half_mirror between the two quads of a half row, row_ror:8
+// between the halves), so both lanes of a pair add the same two numbers and
+// the total does not depend on the lane that reads it.
 __device__ __forceinline__ float row16_sum(float x) {
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
            0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
            0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-           0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, true));
+           0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, true));
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
            0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, true));
   return x;
