@@ -296,7 +296,7 @@ def main():
             "cp_form_frac": round(PRE_CP_BYTES / pre_s / 1e9 / HBM_PEAK_GBS, 4),
         },
         "roofline": {
-            "bound": "hbm", "kernel": "decode_kernel<128,128,bf16,bf16>",
+            "bound": "hbm", "kernel": "decode_kernel<128,128,bf16,bf16,2> (32 state rows per workgroup)",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic("decode.hip", "decode_N64_H32_d128_traffic.json"),
