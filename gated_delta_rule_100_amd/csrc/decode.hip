@@ -27,7 +27,13 @@ namespace {
 
 constexpr int kDecodeThreads = 256;
 constexpr int kDecodeRowsPerThread = 2;  // 32 state rows per workgroup
-constexpr int kMtpThreads = 256;
+
+// Rows per thread at dv (at most dv / 16 row groups' worth).
+template <int DV>
+constexpr int decode_rows_per_thread() {
+  return kDecodeRowsPerThread < DV / (kDecodeThreads / 16) ? kDecodeRowsPerThread
+                                                           : DV / (kDecodeThreads / 16);
+}
 
 // One state row of the decode step, shared by every decode-type kernel so that
 // their results agree bit for bit: a = s.k, u = beta (v - alpha a),
@@ -126,19 +132,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
 // token is written to `inter` (for rolling back rejected draft tokens), and the
 // final state to `state_out` (which may be the input state; NULL keeps the
 // input state as it is).  The per-token arithmetic is that of decode_kernel.
-template <int DK, int DV, Dt IN, Dt OUT>
-__global__ __launch_bounds__(kMtpThreads) void mtp_kernel(
+template <int DK, int DV, Dt IN, Dt OUT, int RPT>
+__global__ __launch_bounds__(kDecodeThreads) void mtp_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* state_in,
     float* state_out, void* __restrict__ o, float* __restrict__ inter, int NH, int H, int T) {
   constexpr int LPR = 16;
   constexpr int CPL = DK / LPR;
   constexpr int VEC = CPL / 4;
-  constexpr int RG = kMtpThreads / LPR;
-  constexpr int RPT = DV / RG;
-  static_assert(CPL % 4 == 0 && DV % RG == 0, "shape");
+  constexpr int RG = kDecodeThreads / LPR;
+  constexpr int ROWS = RG * RPT;        // state rows per workgroup
+  constexpr int WPP = DV / ROWS;        // workgroups per (sequence, head)
+  static_assert(CPL % 4 == 0 && DV % ROWS == 0, "shape");
 
-  const int pair = blockIdx.x;
+  const int pair = blockIdx.x / WPP, r0 = (blockIdx.x % WPP) * ROWS;
   if (pair >= NH) return;
   const int n = pair / H, h = pair % H;
   const int lane16 = threadIdx.x & (LPR - 1);
@@ -148,7 +155,7 @@ __global__ __launch_bounds__(kMtpThreads) void mtp_kernel(
   floatx4 st[RPT][VEC];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int row = rg + RG * i;
+    const int row = r0 + rg + RG * i;
 #pragma unroll
     for (int j = 0; j < VEC; ++j)
       st[i][j] = __builtin_nontemporal_load(&Sin[(row * DK + 4 * lane16 + 64 * j) / 4]);
@@ -165,7 +172,7 @@ __global__ __launch_bounds__(kMtpThreads) void mtp_kernel(
       load_vec<IN, 4>(q, (row * H + h) * DK + 4 * lane16 + 64 * j, q_[j]);
     }
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) v_[i] = load_scalar<IN>(v, (row * H + h) * DV + rg + RG * i);
+    for (int i = 0; i < RPT; ++i) v_[i] = load_scalar<IN>(v, (row * H + h) * DV + r0 + rg + RG * i);
     g_ = g[row * H + h];
     b_ = beta[row * H + h];
   };
@@ -181,12 +188,12 @@ __global__ __launch_bounds__(kMtpThreads) void mtp_kernel(
     for (int i = 0; i < RPT; ++i) oi[i] = update_row<VEC>(st[i], kk, qq, alpha, bb, vv[i]);
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
-      if (lane16 == i) store_scalar<OUT>(o, orow + rg + RG * i, oi[i]);
+      if (lane16 == i) store_scalar<OUT>(o, orow + r0 + rg + RG * i, oi[i]);
     if (inter) {
       floatx4* I = reinterpret_cast<floatx4*>(inter + orow * DK);
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        const int row = rg + RG * i;
+        const int row = r0 + rg + RG * i;
 #pragma unroll
         for (int j = 0; j < VEC; ++j) I[(row * DK + 4 * lane16 + 64 * j) / 4] = st[i][j];
       }
@@ -208,7 +215,7 @@ __global__ __launch_bounds__(kMtpThreads) void mtp_kernel(
     floatx4* Sout = reinterpret_cast<floatx4*>(state_out + static_cast<size_t>(pair) * DV * DK);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int row = rg + RG * i;
+      const int row = r0 + rg + RG * i;
 #pragma unroll
       for (int j = 0; j < VEC; ++j)
         __builtin_nontemporal_store(st[i][j], &Sout[(row * DK + 4 * lane16 + 64 * j) / 4]);
@@ -220,8 +227,12 @@ template <int DK, int DV, Dt IN, Dt OUT>
 hipError_t launch_mtp_t(const void* q, const void* k, const void* v, const float* g,
                         const float* beta, const float* state_in, float* state_out, void* o,
                         float* inter, int NH, int H, int T, hipStream_t stream) {
-  hipLaunchKernelGGL((mtp_kernel<DK, DV, IN, OUT>), dim3(NH), dim3(kMtpThreads), 0, stream, q,
-                     k, v, g, beta, state_in, state_out, o, inter, NH, H, T);
+  constexpr int RPT = decode_rows_per_thread<DV>();
+  const int64_t groups = static_cast<int64_t>(NH) * (DV / (RPT * (kDecodeThreads / 16)));
+  if (groups > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((mtp_kernel<DK, DV, IN, OUT, RPT>), dim3(static_cast<unsigned>(groups)),
+                     dim3(kDecodeThreads), 0, stream, q, k, v, g, beta, state_in, state_out, o,
+                     inter, NH, H, T);
   return hipGetLastError();
 }
 
@@ -229,10 +240,8 @@ template <int DK, int DV, Dt IN, Dt OUT>
 hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* g,
                            const float* beta, float* state, void* o, int NH,
                            hipStream_t stream) {
-  constexpr int RG = kDecodeThreads / 16;  // row groups
-  constexpr int RPT = kDecodeRowsPerThread < DV / RG ? kDecodeRowsPerThread : DV / RG;
-  constexpr int WPP = DV / (RPT * RG);
-  const int64_t groups = static_cast<int64_t>(NH) * WPP;
+  constexpr int RPT = decode_rows_per_thread<DV>();
+  const int64_t groups = static_cast<int64_t>(NH) * (DV / (RPT * (kDecodeThreads / 16)));
   if (groups > INT32_MAX) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((decode_kernel<DK, DV, IN, OUT, RPT>), dim3(static_cast<unsigned>(groups)),
                      dim3(kDecodeThreads), 0, stream, q, k, v, g, beta, state, o, NH);
