@@ -123,15 +123,58 @@ size_t scan_workspace(int mc, int H, int chunk) {
 
 // Schedule of gdr_chunk_prefill.  The sequential scan (scan.hip) keeps every
 // state in registers for a whole sequence and forms neither L, M nor the
-// per-chunk states; it takes bf16 inputs and chunk 64.  The chunk-parallel
-// form (chunk-local L and M, fixup, chunk outputs) serves requests for L or M,
-// fp32 inputs, chunk 16, and long sequences at low parallelism, where one
-// dependent chain per (sequence, head) would leave the GPU idle (the case the
-// two-level fixup is for).
-bool use_scan(const float* L_out, const float* M_out, int T_total, int N, int H, int chunk,
-              int in_dtype) {
-  return !L_out && !M_out && in_dtype == GDR_BF16 && chunk == 64 &&
-         fixup_segment(T_total, N, H, chunk) == 0;
+// per-chunk states; it takes bf16 inputs and chunk 64.  For long sequences at
+// low parallelism, where one dependent chain per (sequence, head) would leave
+// the GPU idle, the segmented scan cuts every sequence into segments of whole
+// chunks and runs three scan passes over all segments at once -- local end
+// states from zero, transfer matrices (identity start, v = 0), and the final
+// pass from the true segment starts -- with the segment-level fixup of the
+// chunk-parallel form between them.  The chunk-parallel form (chunk-local L
+// and M, fixup, chunk outputs) serves requests for L or M, fp32 inputs and
+// chunk 16.
+enum Schedule { kChunkParallel = 0, kScan = 1, kSegmentedScan = 2 };
+
+Schedule schedule(const float* L_out, const float* M_out, int T_total, int N, int H, int chunk,
+                  int in_dtype) {
+  if (L_out || M_out || in_dtype != GDR_BF16 || chunk != 64) return kChunkParallel;
+  return fixup_segment(T_total, N, H, chunk) == 0 ? kScan : kSegmentedScan;
+}
+
+// Segment length (chunks) of the segmented scan: about 128 / (N H) segments
+// per sequence, so that a pass runs about 256 workgroups (two per (segment,
+// head)), and at least 16 chunks per segment.
+int scan_segment(int T_total, int N, int H, int chunk) {
+  const int64_t pairs = static_cast<int64_t>(N) * H;
+  const int64_t avg_chunks = (static_cast<int64_t>(T_total) + static_cast<int64_t>(N) * chunk - 1) /
+                             (static_cast<int64_t>(N) * chunk);
+  int64_t per_seq = 128 / (pairs > 0 ? pairs : 1);
+  if (per_seq < 2) per_seq = 2;
+  int64_t seg = (avg_chunks + per_seq - 1) / per_seq;
+  if (seg < 16) seg = 16;
+  return static_cast<int>(seg);
+}
+
+struct SegScanSizes {
+  int seg = 0, max_segs = 0;
+  size_t state_bytes = 0;  // bytes of one [max_segs, H, d, d] fp32 buffer
+};
+
+SegScanSizes segscan_sizes(int T_total, int N, int H, int d, int chunk, int max_chunks) {
+  SegScanSizes z;
+  if (fixup_segment(T_total, N, H, chunk) == 0) return z;
+  z.seg = scan_segment(T_total, N, H, chunk);
+  z.max_segs = max_chunks / z.seg + N;
+  z.state_bytes = static_cast<size_t>(z.max_segs) * H * d * d * sizeof(float);
+  return z;
+}
+
+// segment offsets | segment indices | cu_seg | offs_seg | L | M^T | end | start
+size_t segscan_workspace(const SegScanSizes& z, int N) {
+  if (z.seg == 0) return 0;
+  return align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1)) +
+         align_up(sizeof(int32_t) * 2 * static_cast<size_t>(z.max_segs)) +
+         2 * align_up(sizeof(int32_t) * (static_cast<size_t>(z.max_segs) + 1)) +
+         4 * align_up(z.state_bytes);
 }
 
 }  // namespace
@@ -225,7 +268,9 @@ size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int 
   cp += align_up(per * dk * dk);  // M
   cp += align_up(per * dv * dk);  // fixed
   cp += seg_workspace(seg_sizes(T_total, N, H, dk, chunk, mc), N);
-  const size_t sc = chunk == 64 ? scan_workspace(mc, H, chunk) : 0;
+  const size_t sc = chunk == 64 ? scan_workspace(mc, H, chunk) +
+                                      segscan_workspace(segscan_sizes(T_total, N, H, dk, chunk, mc), N)
+                                : 0;
   return layout_workspace(N, mc) + (cp > sc ? cp : sc);
 }
 
@@ -257,14 +302,21 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
   if (static_cast<int64_t>(T_total) * H > INT32_MAX || static_cast<int64_t>(mc) * H > INT32_MAX)
     return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: T_total*H too large");
 
-  // workspace carve-up: offsets | indices | factors (sequential scan), or
-  // offsets | indices | [L] | [M] | [fixed] | [segments] (chunk-parallel form)
-  const bool scan = use_scan(L_out, M_out, T_total, N, H, chunk, in_dtype);
+  // workspace carve-up: offsets | indices | factors [| segments] (sequential
+  // scan), or offsets | indices | [L] | [M] | [fixed] | [segments]
+  // (chunk-parallel form)
+  const Schedule sched = schedule(L_out, M_out, T_total, N, H, chunk, in_dtype);
+  const bool scan = sched != kChunkParallel;
   const size_t per = static_cast<size_t>(mc) * H * sizeof(float);
   size_t need = layout_workspace(N, mc);
   SegSizes segz;
+  SegScanSizes ssz;
   if (scan) {
     need += scan_workspace(mc, H, chunk);
+    if (sched == kSegmentedScan) {
+      ssz = segscan_sizes(T_total, N, H, dk, chunk, mc);
+      need += segscan_workspace(ssz, N);
+    }
   } else {
     if (!L_out) need += align_up(per * dv * dk);
     if (!M_out) need += align_up(per * dk * dk);
@@ -299,9 +351,55 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
                                     st);
       if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: chunk factors");
     }
-    e = gdr::launch_chunk_scan(q, k, v, cu_seqlens, offs, f, state_in, state_out, fixed_out, o, N,
-                               H, dk, chunk, mc, T_total, out_dtype, st);
-    return hip_status(e, "gdr_chunk_prefill: chunk scan");
+    ws += align_up(z.gate);
+    if (sched == kScan) {
+      e = gdr::launch_chunk_scan(q, k, v, cu_seqlens, offs, f, state_in, state_out, fixed_out, o,
+                                 N, H, dk, chunk, mc, T_total, out_dtype, 0, st);
+      return hip_status(e, "gdr_chunk_prefill: chunk scan");
+    }
+    // segmented scan
+    const int ms = ssz.max_segs;
+    int32_t* seg_offs = reinterpret_cast<int32_t*>(ws);
+    ws += align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1));
+    int32_t* seg_idx = reinterpret_cast<int32_t*>(ws);
+    ws += align_up(sizeof(int32_t) * 2 * static_cast<size_t>(ms));
+    int32_t* cu_seg = reinterpret_cast<int32_t*>(ws);
+    ws += align_up(sizeof(int32_t) * (static_cast<size_t>(ms) + 1));
+    int32_t* offs_seg = reinterpret_cast<int32_t*>(ws);
+    ws += align_up(sizeof(int32_t) * (static_cast<size_t>(ms) + 1));
+    float* seg_L = reinterpret_cast<float*>(ws);
+    ws += align_up(ssz.state_bytes);
+    float* seg_Mt = reinterpret_cast<float*>(ws);
+    ws += align_up(ssz.state_bytes);
+    float* seg_end = reinterpret_cast<float*>(ws);
+    ws += align_up(ssz.state_bytes);
+    float* seg_start = reinterpret_cast<float*>(ws);
+    e = gdr::launch_layout(offs, N, ssz.seg, seg_offs, seg_idx, ms, st);
+    if (e == hipSuccess)
+      e = gdr::launch_segment_ranges(cu_seqlens, offs, seg_idx, N, ssz.seg, chunk, ms, cu_seg,
+                                     offs_seg, st);
+    // local end state of every segment from zero
+    if (e == hipSuccess)
+      e = gdr::launch_chunk_scan(q, k, v, cu_seg, offs_seg, f, nullptr, seg_L, nullptr, nullptr,
+                                 ms, H, dk, chunk, mc, T_total, out_dtype, 0, st);
+    // transfer matrix of every segment, transposed: identity start, v = 0
+    if (e == hipSuccess)
+      e = gdr::launch_chunk_scan(q, k, nullptr, cu_seg, offs_seg, f, nullptr, seg_Mt, nullptr,
+                                 nullptr, ms, H, dk, chunk, mc, T_total, out_dtype,
+                                 gdr::kScanIdentityStart | gdr::kScanTransposedOut, st);
+    // segment-level fixup: the end state of every segment
+    if (e == hipSuccess)
+      e = gdr::launch_fixup_mode(0, seg_L, seg_Mt, state_in, seg_offs, nullptr, 0, nullptr,
+                                 seg_end, nullptr, ms, H, N, dk, 2, st);
+    if (e == hipSuccess)
+      e = gdr::launch_segment_starts(state_in, seg_end, seg_idx, ms, H, dk, seg_start, st);
+    // outputs (and chunk-end states) from the true segment starts
+    if (e == hipSuccess)
+      e = gdr::launch_chunk_scan(q, k, v, cu_seg, offs_seg, f, seg_start, nullptr, fixed_out, o,
+                                 ms, H, dk, chunk, mc, T_total, out_dtype, 0, st);
+    if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: segmented scan");
+    e = gdr::launch_final_state(state_in, seg_end, seg_offs, N, H, dk, dv, ms, state_out, st);
+    return hip_status(e, "gdr_chunk_prefill: final state");
   }
 
   float* L = L_out;

@@ -96,12 +96,32 @@ hipError_t launch_chunk_factors(const void* q, const void* k, const float* g, co
                                 int chunk, hipStream_t stream);
 
 // Sequential scan over the chunks of every sequence from the factors and the
-// q, k, v inputs: outputs o, final states, and (when fixed != NULL) the state
-// at every chunk end.
+// q, k, v inputs: outputs o (skipped when o is NULL), final states (skipped
+// when state_out is NULL), and (when fixed != NULL) the state at every chunk
+// end.  v == NULL takes v as zero.  flags: kScanIdentityStart starts every
+// (sequence, head) from the identity instead of state_in (dv = dk), which with
+// v == NULL makes the final state the sequence's transfer matrix;
+// kScanTransposedOut writes each final state transposed.
+constexpr int kScanIdentityStart = 1;
+constexpr int kScanTransposedOut = 2;
 hipError_t launch_chunk_scan(const void* q, const void* k, const void* v,
                              const int32_t* cu_seqlens, const int32_t* chunk_offsets,
                              const ChunkFactors& f, const float* state_in, float* state_out,
                              float* fixed, void* o, int N, int H, int d, int chunk, int n_slots,
-                             int T_total, int out_dtype, hipStream_t stream);
+                             int T_total, int out_dtype, int flags, hipStream_t stream);
+
+// Segments of a chunk-parallel layout as pseudo-sequences for the scan: for
+// every segment slot m < max_segs with seg_idx[m] = (n, j), tokens
+// [cu_seg[m], cu_seg[m+1]) and chunk slots [offs_seg[m], offs_seg[m+1]) are
+// chunks j*seg .. of sequence n; slots past the real count are empty.
+hipError_t launch_segment_ranges(const int32_t* cu_seqlens, const int32_t* chunk_offsets,
+                                 const int32_t* seg_idx, int N, int seg, int chunk, int max_segs,
+                                 int32_t* cu_seg, int32_t* offs_seg, hipStream_t stream);
+
+// Start state of every segment: the sequence's state_in (zero when NULL) for
+// its first segment, else the end state of the previous segment.
+hipError_t launch_segment_starts(const float* state_in, const float* seg_end,
+                                 const int32_t* seg_idx, int max_segs, int H, int d,
+                                 float* seg_start, hipStream_t stream);
 
 }  // namespace gdr

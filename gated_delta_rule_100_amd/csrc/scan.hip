@@ -174,7 +174,8 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ offs, ChunkFactors f, const float* state_in, float* state_out,
-    float* __restrict__ fixed, void* __restrict__ o, int N, int H, int n_slots, int T_total) {
+    float* __restrict__ fixed, void* __restrict__ o, int N, int H, int n_slots, int T_total,
+    int flags) {
   using Cfg = ScanCfg<D, C>;
   constexpr int NT = Cfg::NT, ND = Cfg::ND, KB = Cfg::KB, CB = Cfg::CB;
   constexpr int CHD = Cfg::CHD, CHC = Cfg::CHC, TL = Cfg::TL, NVB = Cfg::NVB;
@@ -281,8 +282,10 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
         for (int x = 0; x < Cfg::SK; ++x) copy16(ks + kfull[x], buf + Cfg::OFF_K + 1024 * (cw + kCopyWaves * x));
 #pragma unroll
         for (int x = 0; x < Cfg::SQ; ++x) copy16(qs + qfull[x], buf + Cfg::OFF_Q + 1024 * (cw + kCopyWaves * x));
+        if (v) {
 #pragma unroll
-        for (int x = 0; x < Cfg::SV; ++x) copy16(vs + vfull[x], buf + Cfg::OFF_V + 1024 * (cw + kCopyWaves * x));
+          for (int x = 0; x < Cfg::SV; ++x) copy16(vs + vfull[x], buf + Cfg::OFF_V + 1024 * (cw + kCopyWaves * x));
+        }
       } else {
 #pragma unroll
         for (int x = 0; x < Cfg::SK; ++x)
@@ -292,10 +295,12 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
         for (int x = 0; x < Cfg::SQ; ++x)
           copy16(qs + static_cast<uint32_t>(qrow[x] < last ? qrow[x] : last) * row_bytes + qcol[x],
                  buf + Cfg::OFF_Q + 1024 * (cw + kCopyWaves * x));
+        if (v) {
 #pragma unroll
-        for (int x = 0; x < Cfg::SV; ++x)
-          copy16(vs + static_cast<uint32_t>(vrow[x] < last ? vrow[x] : last) * row_bytes + vcol[x],
-                 buf + Cfg::OFF_V + 1024 * (cw + kCopyWaves * x));
+          for (int x = 0; x < Cfg::SV; ++x)
+            copy16(vs + static_cast<uint32_t>(vrow[x] < last ? vrow[x] : last) * row_bytes + vcol[x],
+                   buf + Cfg::OFF_V + 1024 * (cw + kCopyWaves * x));
+        }
       }
 #pragma unroll
       for (int x = 0; x < Cfg::STL; ++x) copy16(ts + toff[x], buf + Cfg::OFF_T + 1024 * (cw + kCopyWaves * x));
@@ -320,9 +325,15 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
   const size_t sbase = (static_cast<size_t>(n) * H + h) * D * D + static_cast<size_t>(vrow) * D;
   floatx4 S[ND];
 #pragma unroll
-  for (int jt = 0; jt < ND; ++jt)
-    S[jt] = state_in ? *reinterpret_cast<const floatx4*>(state_in + sbase + 16 * jt + 4 * g4)
-                     : floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int jt = 0; jt < ND; ++jt) {
+    if (flags & kScanIdentityStart) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[jt][e] = vrow == 16 * jt + 4 * g4 + e ? 1.f : 0.f;
+    } else {
+      S[jt] = state_in ? *reinterpret_cast<const floatx4*>(state_in + sbase + 16 * jt + 4 * g4)
+                       : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
 
   if (c1 > c0) {
     // The state registers are carried through the loop: drain their loads
@@ -393,7 +404,8 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
       for (int a = 0; a < NT; ++a) {
         const floatx4 gam = *reinterpret_cast<const floatx4*>(Gl + 16 * a + 4 * g4);
         const floatx4 bet = *reinterpret_cast<const floatx4*>(Gl + 2 * C + 16 * a + 4 * g4);
-        const shortx4 vv = read_tr4(Vl, Cfg::ROWS, CHV, 16 * a, 16 * wave, c16, g4);
+        const shortx4 vv = v ? read_tr4(Vl, Cfg::ROWS, CHV, 16 * a, 16 * wave, c16, g4)
+                             : shortx4{0, 0, 0, 0};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           R[a][e] = bet[e] * (bf16_bits_to_f32(static_cast<uint16_t>(vv[e])) - gam[e] * Z[a][e]);
@@ -464,7 +476,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
 #pragma unroll
         for (int a = 2 * kb; a < NT; ++a) oa[a] = mfma16x16x32(ub[kb][0], pa[a][0], oa[a]);
       }
-      {
+      if (o) {
         int tok0;
         const int cl = chunk_range(s, tok0);
 #pragma unroll
@@ -512,37 +524,105 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
     }
   }
 
+  if (state_out && (flags & kScanTransposedOut)) {
+    // column vrow of the (sequence, head)'s matrix: element (j, vrow) = S[vrow][j]
+    float* so = state_out + (static_cast<size_t>(n) * H + h) * D * D;
 #pragma unroll
-  for (int jt = 0; jt < ND; ++jt)
-    *reinterpret_cast<floatx4*>(state_out + sbase + 16 * jt + 4 * g4) = S[jt];
+    for (int jt = 0; jt < ND; ++jt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) so[static_cast<size_t>(16 * jt + 4 * g4 + e) * D + vrow] = S[jt][e];
+  } else if (state_out) {
+#pragma unroll
+    for (int jt = 0; jt < ND; ++jt)
+      *reinterpret_cast<floatx4*>(state_out + sbase + 16 * jt + 4 * g4) = S[jt];
+  }
 }
 
 template <int D, int C, Dt OUTD>
 hipError_t scan_t(const void* q, const void* k, const void* v, const int32_t* cu,
                   const int32_t* offs, const ChunkFactors& f, const float* state_in,
                   float* state_out, float* fixed, void* o, int N, int H, int n_slots, int T_total,
-                  hipStream_t stream) {
+                  int flags, hipStream_t stream) {
   const int64_t pairs = static_cast<int64_t>(N) * H;
   const int64_t groups = (pairs + kXcds - 1) / kXcds * kXcds * ScanCfg<D, C>::NVB;
   if (groups > INT32_MAX) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((chunk_scan_kernel<D, C, OUTD>), dim3(static_cast<unsigned>(groups)),
                      dim3(kThreads), 0, stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), cu, offs, f,
-                     state_in, state_out, fixed, o, N, H, n_slots, T_total);
+                     state_in, state_out, fixed, o, N, H, n_slots, T_total, flags);
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void segment_ranges_kernel(
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ offs,
+    const int32_t* __restrict__ seg_idx, int N, int seg, int chunk, int max_segs,
+    int32_t* __restrict__ cu_seg, int32_t* __restrict__ offs_seg) {
+  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m > max_segs) return;
+  int tok = cu[N], c = offs[N];  // end sentinel and slots past the real count
+  if (m < max_segs) {
+    const int n = seg_idx[2 * m], j = seg_idx[2 * m + 1];
+    if (n >= 0 && n < N && j >= 0) {
+      const int64_t t = cu[n] + static_cast<int64_t>(j) * seg * chunk;
+      const int64_t cc = offs[n] + static_cast<int64_t>(j) * seg;
+      tok = static_cast<int>(t < cu[n + 1] ? t : cu[n + 1]);
+      c = static_cast<int>(cc < offs[n + 1] ? cc : offs[n + 1]);
+    }
+  }
+  cu_seg[m] = tok;
+  offs_seg[m] = c;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void segment_starts_kernel(const float* state_in,
+                                                             const float* __restrict__ seg_end,
+                                                             const int32_t* __restrict__ seg_idx,
+                                                             int H, float* __restrict__ seg_start) {
+  const int m = blockIdx.x, h = blockIdx.y;
+  const int n = seg_idx[2 * m], j = seg_idx[2 * m + 1];
+  if (n < 0 || j < 0) return;  // no segment: the scan never reads this slot
+  const floatx4* src = nullptr;
+  if (j > 0)
+    src = reinterpret_cast<const floatx4*>(seg_end + (static_cast<size_t>(m - 1) * H + h) * D * D);
+  else if (state_in)
+    src = reinterpret_cast<const floatx4*>(state_in + (static_cast<size_t>(n) * H + h) * D * D);
+  floatx4* dst = reinterpret_cast<floatx4*>(seg_start + (static_cast<size_t>(m) * H + h) * D * D);
+  for (int i = threadIdx.x; i < D * D / 4; i += blockDim.x)
+    dst[i] = src ? src[i] : floatx4{0.f, 0.f, 0.f, 0.f};
+}
+
 }  // namespace
+
+hipError_t launch_segment_ranges(const int32_t* cu_seqlens, const int32_t* chunk_offsets,
+                                 const int32_t* seg_idx, int N, int seg, int chunk, int max_segs,
+                                 int32_t* cu_seg, int32_t* offs_seg, hipStream_t stream) {
+  hipLaunchKernelGGL(segment_ranges_kernel, dim3((max_segs + 1 + 255) / 256), dim3(256), 0, stream,
+                     cu_seqlens, chunk_offsets, seg_idx, N, seg, chunk, max_segs, cu_seg, offs_seg);
+  return hipGetLastError();
+}
+
+hipError_t launch_segment_starts(const float* state_in, const float* seg_end,
+                                 const int32_t* seg_idx, int max_segs, int H, int d,
+                                 float* seg_start, hipStream_t stream) {
+  if (max_segs <= 0) return hipSuccess;
+  if (d == 128)
+    hipLaunchKernelGGL(segment_starts_kernel<128>, dim3(max_segs, H), dim3(256), 0, stream,
+                       state_in, seg_end, seg_idx, H, seg_start);
+  else
+    hipLaunchKernelGGL(segment_starts_kernel<64>, dim3(max_segs, H), dim3(256), 0, stream,
+                       state_in, seg_end, seg_idx, H, seg_start);
+  return hipGetLastError();
+}
 
 hipError_t launch_chunk_scan(const void* q, const void* k, const void* v,
                              const int32_t* cu_seqlens, const int32_t* chunk_offsets,
                              const ChunkFactors& f, const float* state_in, float* state_out,
                              float* fixed, void* o, int N, int H, int d, int chunk, int n_slots,
-                             int T_total, int out_dtype, hipStream_t stream) {
+                             int T_total, int out_dtype, int flags, hipStream_t stream) {
   if (chunk != 64) return hipErrorInvalidValue;
 #define GDR_SCAN(D_, OUT_)                                                                         \
   return scan_t<D_, 64, OUT_>(q, k, v, cu_seqlens, chunk_offsets, f, state_in, state_out, fixed, o, \
-                              N, H, n_slots, T_total, stream)
+                              N, H, n_slots, T_total, flags, stream)
   if (d == 128) {
     if (out_dtype == 0) GDR_SCAN(128, Dt::BF16);
     GDR_SCAN(128, Dt::F32);

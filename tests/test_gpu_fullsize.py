@@ -77,6 +77,13 @@ def test_full_varlen_32768_tokens_H32():
 
 def test_full_long_T131072_H4():
     d = workload(4)
-    say("full long sequence B=1 T=131072 H=4 (two-level fixup)")
+    say("full long sequence B=1 T=131072 H=4 (segmented scan)")
     o, sout, F = run_full(d, keep_fixed=True)
     check_pairs(d, o, sout, [(0, 2)], fixed=F)
+
+
+def test_full_long_T131072_H4_chunk_parallel():
+    d = workload(4)
+    say("full long sequence B=1 T=131072 H=4 (chunk-parallel form, two-level fixup)")
+    o, sout, F = run_full(d, keep_fixed=True, keep_lm=True)
+    check_pairs(d, o, sout, [(0, 1)], fixed=F)

@@ -241,8 +241,11 @@ def test_split_prefill_resumes():
     assert rel_err(state.astype(np.float64), host64(full["state_out"])) <= 1e-3
 
 
-# Long sequences with few heads take the two-level (segmented) fixup: fold
-# segments of chunks, scan the segments, then apply the scanned starts.
+# Long sequences with few heads: with L and M requested ("cp") they take the
+# two-level fixup of the chunk-parallel form (fold segments of chunks, scan the
+# segments, apply the scanned starts); otherwise ("scan": with the chunk-end
+# states, "none": without) the segmented scan (local segment states, segment
+# transfer matrices, segment fixup, final pass from the true starts).
 LONG_CASES = {
     "long-T32768-H1-slow": (4, dict(seqlens=[32768], H=1, gate="slow")),
     "long-T32768-H1-unit-state": (4, dict(seqlens=[32768], H=1, gate="unit", state0=True)),
@@ -252,10 +255,11 @@ LONG_CASES = {
 }
 
 
+@pytest.mark.parametrize("schedule", ["cp", "scan", "none"])
 @pytest.mark.parametrize("name", list(LONG_CASES))
-def test_prefill_long_two_level(name):
+def test_prefill_long_two_level(name, schedule):
     idx, ov = LONG_CASES[name]
     d = workload(idx, seed=120, **ov)
-    say(f"prefill two-level {name}: T={d['T']} N={d['N']} H={d['H']}")
-    res = run_prefill(d)
+    say(f"prefill long {name} ({schedule}): T={d['T']} N={d['N']} H={d['H']}")
+    res = run_prefill(d, schedule=schedule)
     check_against_oracle(d, res, d["chunk"], check_locals=False)
