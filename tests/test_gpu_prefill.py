@@ -181,6 +181,24 @@ def test_prefill_in_place_state():
     assert torch.equal(st, ref["state_out"])
 
 
+def test_prefill_in_place_state_segmented():
+    """The segmented scan reads the initial state for the segment fixup and the
+    segment starts, and writes the final state last: in place gives the same
+    bits as a separate output."""
+    d = workload(4, seed=118, seqlens=[30000, 0, 19500], H=1, gate="slow", state0=True)
+    say("prefill in-place state, segmented scan")
+    import gated_delta_rule_100_amd as gdr
+    di = dev_inputs(d)
+    ref = run_prefill(d, schedule="none")
+    st = di["state0"].clone()
+    o = torch.empty_like(ref["o"])
+    gdr.gdr_chunk_prefill(di["q"], di["k"], di["v"], di["g"], di["beta"], di["cu"], st, st, o,
+                          chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref["o"])
+    assert torch.equal(st, ref["state_out"])
+
+
 def test_prefill_guard_bands():
     import gated_delta_rule_100_amd as gdr
     d = workload(3, seed=114, seqlens=[65, 1, 130], H=2)
