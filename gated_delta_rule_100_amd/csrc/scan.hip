@@ -53,16 +53,22 @@ constexpr int kCopyWaves = 4;
 constexpr int kComputeWaves = 4;  // 16 state rows each
 constexpr int kThreads = 64 * (kComputeWaves + kCopyWaves);
 
-template <int D, int C>
+template <int D, int C, int NH>
 struct ScanCfg {
   static constexpr int NT = C / 16;    // 16-token tiles
   static constexpr int ND = D / 16;    // 16-wide tiles of state columns
   static constexpr int KB = D / 32;    // 32-deep blocks over state columns
+  static constexpr int KH = KB / 2;    // blocks per column half
   static constexpr int CB = C / 32;    // 32-deep blocks over tokens
   static constexpr int CHD = D / 8;    // 16-byte chunks per row of D bf16
   static constexpr int CHC = C / 8;    // 16-byte chunks per row of C bf16
-  static constexpr int ROWS = 16 * kComputeWaves;  // state rows per workgroup
-  static constexpr int NVB = D / ROWS;              // workgroups per (sequence, head)
+  // NH compute waves share one 16-row state tile, each holding 1/NH of its
+  // columns (NH = 2: the column halves sit on two SIMDs and exchange their
+  // partial contractions over dk through LDS once per chunk).
+  static constexpr int ROWS = 16 * kComputeWaves / NH;  // state rows per workgroup
+  static constexpr int NVB = D / ROWS;                  // workgroups per (sequence, head)
+  static constexpr int JT = ND / NH;                    // 16-wide column tiles per wave
+  static constexpr int NO = NT / NH;                    // output token tiles per wave
   // T and P planes: rows t < C/2 keep their first C/2 columns (the rest is
   // above the diagonal), rows t >= C/2 keep all C.
   static constexpr int TL_LO = (C / 2) * (C / 2);
@@ -81,13 +87,17 @@ struct ScanCfg {
   static constexpr int OFF_V = OFF_P + P_BYTES;
   static constexpr int OFF_G = OFF_V + V_BYTES;
   static constexpr int BUF = OFF_G + G_BYTES;
-  static constexpr int BYTES = 2 * BUF;
+  // exchange region (NH = 2): per compute wave and lane, its partial K S^T
+  // (NT tiles) and its partial S Q^T for the partner's output tiles (NO)
+  static constexpr int X_SLOTS = NH > 1 ? NT + NO : 0;
+  static constexpr int OFF_X = 2 * BUF;
+  static constexpr int BYTES = 2 * BUF + X_SLOTS * kComputeWaves * 64 * 16;
   // copy instructions (1 KiB each) per region, and each copy wave's share
   static constexpr int NK = K_BYTES / 1024, NQ = Q_BYTES / 1024, NTL = T_BYTES / 1024;
   static constexpr int NV = V_BYTES / 1024;
   static constexpr int SK = NK / kCopyWaves, SQ = NQ / kCopyWaves, STL = NTL / kCopyWaves;
   static constexpr int SV = NV / kCopyWaves;
-  static_assert(C == 64 && (D == 64 || D == 128), "shape");
+  static_assert(C == 64 && (D == 64 || D == 128) && (NH == 1 || NH == 2), "shape");
   static_assert(K_BYTES % (1024 * kCopyWaves) == 0 && T_BYTES % (1024 * kCopyWaves) == 0 &&
                     V_BYTES % (1024 * kCopyWaves) == 0 && G_BYTES == 1024,
                 "copy tiling");
@@ -169,15 +179,16 @@ __device__ __forceinline__ void lead_interleave() {
   }
 }
 
-template <int D, int C, Dt OUTD>
+template <int D, int C, Dt OUTD, bool OUT, int NH>
 __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ offs, ChunkFactors f, const float* state_in, float* state_out,
     float* __restrict__ fixed, void* __restrict__ o, int N, int H, int n_slots, int T_total,
     int flags) {
-  using Cfg = ScanCfg<D, C>;
-  constexpr int NT = Cfg::NT, ND = Cfg::ND, KB = Cfg::KB, CB = Cfg::CB;
+  using Cfg = ScanCfg<D, C, NH>;
+  constexpr int NT = Cfg::NT, KB = Cfg::KB, KH = Cfg::KH, CB = Cfg::CB, JT = Cfg::JT;
+  constexpr int NO = Cfg::NO;
   constexpr int CHD = Cfg::CHD, CHC = Cfg::CHC, TL = Cfg::TL, NVB = Cfg::NVB;
   constexpr int CHV = Cfg::ROWS / 8;  // 16-byte chunks per staged v row
   __shared__ __align__(1024) unsigned char smem[Cfg::BYTES];
@@ -210,7 +221,8 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
 
   if (wave >= kComputeWaves) {
     // ---- copy waves: each issues a quarter of every region's copies (the
-    // gates are one copy, issued by the first wave).
+    // gates are one copy, issued by the first wave).  Without outputs, q and
+    // P are not needed.
     if (c1 <= c0) return;
     // wave-uniform, so that LDS destinations (and M0) stay scalar
     const int cw = __builtin_amdgcn_readfirstlane(wave - kComputeWaves);
@@ -280,8 +292,10 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
       if (last == C - 1) {
 #pragma unroll
         for (int x = 0; x < Cfg::SK; ++x) copy16(ks + kfull[x], buf + Cfg::OFF_K + 1024 * (cw + kCopyWaves * x));
+        if constexpr (OUT) {
 #pragma unroll
-        for (int x = 0; x < Cfg::SQ; ++x) copy16(qs + qfull[x], buf + Cfg::OFF_Q + 1024 * (cw + kCopyWaves * x));
+          for (int x = 0; x < Cfg::SQ; ++x) copy16(qs + qfull[x], buf + Cfg::OFF_Q + 1024 * (cw + kCopyWaves * x));
+        }
         if (v) {
 #pragma unroll
           for (int x = 0; x < Cfg::SV; ++x) copy16(vs + vfull[x], buf + Cfg::OFF_V + 1024 * (cw + kCopyWaves * x));
@@ -291,10 +305,12 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
         for (int x = 0; x < Cfg::SK; ++x)
           copy16(ks + static_cast<uint32_t>(krow[x] < last ? krow[x] : last) * row_bytes + kcol[x],
                  buf + Cfg::OFF_K + 1024 * (cw + kCopyWaves * x));
+        if constexpr (OUT) {
 #pragma unroll
-        for (int x = 0; x < Cfg::SQ; ++x)
-          copy16(qs + static_cast<uint32_t>(qrow[x] < last ? qrow[x] : last) * row_bytes + qcol[x],
-                 buf + Cfg::OFF_Q + 1024 * (cw + kCopyWaves * x));
+          for (int x = 0; x < Cfg::SQ; ++x)
+            copy16(qs + static_cast<uint32_t>(qrow[x] < last ? qrow[x] : last) * row_bytes + qcol[x],
+                   buf + Cfg::OFF_Q + 1024 * (cw + kCopyWaves * x));
+        }
         if (v) {
 #pragma unroll
           for (int x = 0; x < Cfg::SV; ++x)
@@ -304,8 +320,10 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
       }
 #pragma unroll
       for (int x = 0; x < Cfg::STL; ++x) copy16(ts + toff[x], buf + Cfg::OFF_T + 1024 * (cw + kCopyWaves * x));
+      if constexpr (OUT) {
 #pragma unroll
-      for (int x = 0; x < Cfg::STL; ++x) copy16(ps + toff[x], buf + Cfg::OFF_P + 1024 * (cw + kCopyWaves * x));
+        for (int x = 0; x < Cfg::STL; ++x) copy16(ps + toff[x], buf + Cfg::OFF_P + 1024 * (cw + kCopyWaves * x));
+      }
       if (cw == 0) copy16(reinterpret_cast<const char*>(f.gate + slot * 4 * C) + goff, buf + Cfg::OFF_G);
     };
 
@@ -314,6 +332,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
     bare_barrier();                 // B0: chunk c0 is in LDS
     for (int s = c0; s < c1; ++s) {
       if (s + 1 < c1) copy_chunk(s + 1);  // into the buffer chunk s - 1 released
+      if constexpr (NH > 1) bare_barrier();  // the compute waves' exchange barrier
       __builtin_amdgcn_s_waitcnt(0);
       bare_barrier();  // chunk s is done; chunk s + 1 is in LDS
     }
@@ -321,19 +340,33 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
   }
 
   // ---- compute waves ----
-  const int vrow = Cfg::ROWS * vb + 16 * wave + c16;  // state row held by this lane
+  // Wave (rt, hp): state rows 16 rt .. 16 rt + 15 of this workgroup's block,
+  // column tiles hp JT .. hp JT + JT - 1.
+  const int rt = wave / NH, hp = wave % NH;
+  const int vrow = Cfg::ROWS * vb + 16 * rt + c16;  // state row held by this lane
+  const int jt0 = hp * JT;                          // first column tile held
   const size_t sbase = (static_cast<size_t>(n) * H + h) * D * D + static_cast<size_t>(vrow) * D;
-  floatx4 S[ND];
+  floatx4 S[JT];
 #pragma unroll
-  for (int jt = 0; jt < ND; ++jt) {
+  for (int jl = 0; jl < JT; ++jl) {
+    const int jt = jt0 + jl;
     if (flags & kScanIdentityStart) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[jt][e] = vrow == 16 * jt + 4 * g4 + e ? 1.f : 0.f;
+      for (int e = 0; e < 4; ++e) S[jl][e] = vrow == 16 * jt + 4 * g4 + e ? 1.f : 0.f;
     } else {
-      S[jt] = state_in ? *reinterpret_cast<const floatx4*>(state_in + sbase + 16 * jt + 4 * g4)
+      S[jl] = state_in ? *reinterpret_cast<const floatx4*>(state_in + sbase + 16 * jt + 4 * g4)
                        : floatx4{0.f, 0.f, 0.f, 0.f};
     }
   }
+  // Output token tiles of this wave: all of them when NH = 1; with NH = 2 the
+  // column halves split them so that each does three 32-deep blocks of
+  // U^T P^T: half 0 takes tiles 0 and 3, half 1 tiles 1 and 2 (tile a needs
+  // blocks kb <= a / 2).  Tile u of half x (NH = 2):
+  auto otile = [](int x, int u) { return u == 0 ? x : 3 - x; };
+  float* xch = reinterpret_cast<float*>(smem + Cfg::OFF_X);
+  auto xslot = [&](int w, int x) {
+    return reinterpret_cast<floatx4*>(xch) + (x * kComputeWaves + w) * 64 + lane;
+  };
 
   if (c1 > c0) {
     // The state registers are carried through the loop: drain their loads
@@ -351,60 +384,109 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
       const uint16_t* Vl = reinterpret_cast<const uint16_t*>(buf + Cfg::OFF_V);
       const float* Gl = reinterpret_cast<const float*>(buf + Cfg::OFF_G);
 
-      // Z = K S^T (rows: tokens) and Y^T = S Q^T (rows: state rows), one
-      // 32-deep block of state columns at a time.  S^T enters as operand
-      // planes in natural order (lane group g holds columns 32 kb + 8 g .. +7):
-      // the two stacked D tiles are split, then regrouped with permlane swaps.
-      // The 16x16x32 A and B fragments have the same lane layout, so these
-      // registers serve as B (rows of S^T) in K S^T and as A (rows of S) in
-      // S Q^T.
-      floatx4 Z[NT], Yt[NT];
+      // Z = K S^T (rows: tokens) and Y^T = S Q^T (rows: state rows), as the
+      // sum of two partial contractions over the column halves of S (the
+      // 32-deep blocks kb < KH, then kb >= KH), which are added last.  S^T
+      // enters as operand planes in natural order (lane group g holds columns
+      // 32 kb + 8 g .. +7): the two stacked D tiles are split, then regrouped
+      // with permlane swaps.  The 16x16x32 A and B fragments have the same
+      // lane layout, so these registers serve as B (rows of S^T) in K S^T and
+      // as A (rows of S) in S Q^T.
+      constexpr int NCH = 2 / NH;  // column halves contracted by this wave
+      floatx4 Zh[NCH][NT], Yh[NCH][NT];
 #pragma unroll
-      for (int a = 0; a < NT; ++a) {
-        Z[a] = floatx4{0.f, 0.f, 0.f, 0.f};
-        Yt[a] = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        bf16x8 sbk[2];
-        {
-          float x[8];
-#pragma unroll
-          for (int e2 = 0; e2 < 8; ++e2) x[e2] = S[2 * kb + e2 / 4][e2 & 3];
-          split8<2>(x, sbk);
-#pragma unroll
-          for (int p = 0; p < 2; ++p) sbk[p] = slot_to_natural(sbk[p]);
-        }
-        bf16x8 ka[NT], qa[NT];
+      for (int hc = 0; hc < NCH; ++hc) {
 #pragma unroll
         for (int a = 0; a < NT; ++a) {
-          const int t = 16 * a + c16, n8 = 4 * kb + g4;
-          ka[a] = *reinterpret_cast<const bf16x8*>(Kl + t * D + 8 * (n8 ^ swz_tr(t, CHD)));
-          qa[a] = *reinterpret_cast<const bf16x8*>(Ql + t * D + 8 * (n8 ^ swz(t, CHD)));
+          Zh[hc][a] = floatx4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (OUT) Yh[hc][a] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
-        // plane pairs, smallest terms first; the four token tiles are
-        // interleaved so that consecutive products are independent
 #pragma unroll
-        for (int a = 0; a < NT; ++a) Z[a] = mfma16x16x32(ka[a], sbk[1], Z[a]);
+        for (int kl = 0; kl < KH; ++kl) {
+          const int kbl = hc * KH + kl;  // block among this wave's columns
+          const int kb = hp * (KB / NH) + kbl;
+          bf16x8 sbk[2];
+          {
+            float x[8];
 #pragma unroll
-        for (int a = 0; a < NT; ++a) Z[a] = mfma16x16x32(ka[a], sbk[0], Z[a]);
+            for (int e2 = 0; e2 < 8; ++e2) x[e2] = S[2 * kbl + e2 / 4][e2 & 3];
+            split8<2>(x, sbk);
 #pragma unroll
-        for (int a = 0; a < NT; ++a) Yt[a] = mfma16x16x32(sbk[1], qa[a], Yt[a]);
+            for (int p = 0; p < 2; ++p) sbk[p] = slot_to_natural(sbk[p]);
+          }
+          bf16x8 ka[NT], qa[NT];
 #pragma unroll
-        for (int a = 0; a < NT; ++a) Yt[a] = mfma16x16x32(sbk[0], qa[a], Yt[a]);
+          for (int a = 0; a < NT; ++a) {
+            const int t = 16 * a + c16, n8 = 4 * kb + g4;
+            ka[a] = *reinterpret_cast<const bf16x8*>(Kl + t * D + 8 * (n8 ^ swz_tr(t, CHD)));
+            if constexpr (OUT)
+              qa[a] = *reinterpret_cast<const bf16x8*>(Ql + t * D + 8 * (n8 ^ swz(t, CHD)));
+          }
+          // plane pairs, smallest terms first; the four token tiles are
+          // interleaved so that consecutive products are independent
+#pragma unroll
+          for (int a = 0; a < NT; ++a) Zh[hc][a] = mfma16x16x32(ka[a], sbk[1], Zh[hc][a]);
+#pragma unroll
+          for (int a = 0; a < NT; ++a) Zh[hc][a] = mfma16x16x32(ka[a], sbk[0], Zh[hc][a]);
+          if constexpr (OUT) {
+#pragma unroll
+            for (int a = 0; a < NT; ++a) Yh[hc][a] = mfma16x16x32(sbk[1], qa[a], Yh[hc][a]);
+#pragma unroll
+            for (int a = 0; a < NT; ++a) Yh[hc][a] = mfma16x16x32(sbk[0], qa[a], Yh[hc][a]);
+          }
+        }
+      }
+      floatx4 Z[NT], Yo[NO];  // Yo: Y^T of this wave's output tiles
+      if constexpr (NH == 1) {
+#pragma unroll
+        for (int a = 0; a < NT; ++a) {
+          Z[a] = Zh[0][a] + Zh[1][a];
+          if constexpr (OUT) Yo[a] = Yh[0][a] + Yh[1][a];
+        }
+      } else {
+        // exchange with the wave holding the other column half (wave ^ 1):
+        // all of its partial Z, and its partial Y^T of this wave's tiles
+#pragma unroll
+        for (int a = 0; a < NT; ++a) *xslot(wave, a) = Zh[0][a];
+        if constexpr (OUT) {
+#pragma unroll
+          for (int u = 0; u < NO; ++u) {
+            const int ap = otile(1 - hp, u);  // the partner's tile u
+            floatx4 y = Yh[0][0];
+#pragma unroll
+            for (int a = 1; a < NT; ++a) y = ap == a ? Yh[0][a] : y;
+            *xslot(wave, NT + u) = y;
+          }
+        }
+        // the LDS writes above must be complete before the barrier (gfx950
+        // does not wait for them at s_barrier)
+        lds_barrier();  // exchange written
+#pragma unroll
+        for (int a = 0; a < NT; ++a) Z[a] = Zh[0][a] + *xslot(wave ^ 1, a);
+        if constexpr (OUT) {
+#pragma unroll
+          for (int u = 0; u < NO; ++u) {
+            const int am = otile(hp, u);
+            floatx4 y = Yh[0][0];
+#pragma unroll
+            for (int a = 1; a < NT; ++a) y = am == a ? Yh[0][a] : y;
+            Yo[u] = y + *xslot(wave ^ 1, NT + u);
+          }
+        }
       }
 
       // R = diag(beta) (V - diag(gamma) Z) (v rows 16 a + 4 g + e at this
       // lane's state row: a transpose read), as operand planes of 32 tokens
       // (two stacked D tiles, slot order), then U = T R over the lower blocks:
       // T rows are stored in slot order, so the T fragment of row 16 i + c and
-      // 32-block m is one 16-byte read per plane.
+      // 32-block m is one 16-byte read per plane.  Both column halves form
+      // the same R and U.
       floatx4 R[NT];
 #pragma unroll
       for (int a = 0; a < NT; ++a) {
         const floatx4 gam = *reinterpret_cast<const floatx4*>(Gl + 16 * a + 4 * g4);
         const floatx4 bet = *reinterpret_cast<const floatx4*>(Gl + 2 * C + 16 * a + 4 * g4);
-        const shortx4 vv = v ? read_tr4(Vl, Cfg::ROWS, CHV, 16 * a, 16 * wave, c16, g4)
+        const shortx4 vv = v ? read_tr4(Vl, Cfg::ROWS, CHV, 16 * a, 16 * rt, c16, g4)
                              : shortx4{0, 0, 0, 0};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -448,77 +530,90 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
           x[e2] = U[a0][e];
           xd[e2] = Gl[C + 16 * a0 + 4 * g4 + e] * U[a0][e];
         }
-        split8<2>(x, ub[kb]);
+        if constexpr (OUT) split8<2>(x, ub[kb]);
         split8<2>(xd, udb[kb]);
       }
 
-      // O^T = Y^T diag(gamma) + U^T P^T: lane (c, g) ends up with token
-      // 16 a + c and state rows 4 g .. 4 g + 3 of its wave's tile.  P is zero
-      // above the diagonal, so token tile a needs the 32-blocks kb <= a / 2.
-      floatx4 oa[NT];
+      if constexpr (OUT) {
+        // O^T = Y^T diag(gamma) + U^T P^T for this wave's token tiles: lane
+        // (c, g) ends up with token 16 a + c and state rows 4 g .. 4 g + 3 of
+        // its row tile.  P is zero above the diagonal, so token tile a needs
+        // the 32-blocks kb <= a / 2.
+        floatx4 oa[NO];
+        int at[NO];
 #pragma unroll
-      for (int a = 0; a < NT; ++a) oa[a] = Yt[a] * Gl[16 * a + c16];
-#pragma unroll
-      for (int kb = 0; kb < CB; ++kb) {
-        bf16x8 pa[NT][2];
-#pragma unroll
-        for (int a = 2 * kb; a < NT; ++a) {
-          const int t = 16 * a + c16, ch = t < C / 2 ? CHC / 2 : CHC;
-#pragma unroll
-          for (int p = 0; p < 2; ++p)
-            pa[a][p] = *reinterpret_cast<const bf16x8*>(Pl + p * TL + tl_row<C>(t) +
-                                                        8 * ((4 * kb + g4) ^ swz(t, ch)));
+        for (int u = 0; u < NO; ++u) {
+          at[u] = NH == 1 ? u : otile(hp, u);
+          oa[u] = Yo[u] * Gl[16 * at[u] + c16];
         }
 #pragma unroll
-        for (int a = 2 * kb; a < NT; ++a) oa[a] = mfma16x16x32(ub[kb][1], pa[a][0], oa[a]);
+        for (int kb = 0; kb < CB; ++kb) {
+          // tiles with a / 2 >= kb: NH = 1: a >= 2 kb; NH = 2: u >= kb
+          constexpr int UB0 = 0;
+          bf16x8 pa[NO][2];
 #pragma unroll
-        for (int a = 2 * kb; a < NT; ++a) oa[a] = mfma16x16x32(ub[kb][0], pa[a][1], oa[a]);
+          for (int u = UB0; u < NO; ++u) {
+            if (NH == 1 ? u < 2 * kb : u < kb) continue;
+            const int t = 16 * at[u] + c16;
+            const int ch = (NH == 1 ? u < NT / 2 : u == 0) ? CHC / 2 : CHC;
 #pragma unroll
-        for (int a = 2 * kb; a < NT; ++a) oa[a] = mfma16x16x32(ub[kb][0], pa[a][0], oa[a]);
-      }
-      if (o) {
+            for (int p = 0; p < 2; ++p)
+              pa[u][p] = *reinterpret_cast<const bf16x8*>(Pl + p * TL + tl_row<C>(t) +
+                                                          8 * ((4 * kb + g4) ^ swz(t, ch)));
+          }
+#pragma unroll
+          for (int u = 0; u < NO; ++u)
+            if (NH == 1 ? u >= 2 * kb : u >= kb) oa[u] = mfma16x16x32(ub[kb][1], pa[u][0], oa[u]);
+#pragma unroll
+          for (int u = 0; u < NO; ++u)
+            if (NH == 1 ? u >= 2 * kb : u >= kb) oa[u] = mfma16x16x32(ub[kb][0], pa[u][1], oa[u]);
+#pragma unroll
+          for (int u = 0; u < NO; ++u)
+            if (NH == 1 ? u >= 2 * kb : u >= kb) oa[u] = mfma16x16x32(ub[kb][0], pa[u][0], oa[u]);
+        }
         int tok0;
         const int cl = chunk_range(s, tok0);
 #pragma unroll
-        for (int a = 0; a < NT; ++a) {
-          const int t = 16 * a + c16;
+        for (int u = 0; u < NO; ++u) {
+          const int t = 16 * at[u] + c16;
           if (t < cl)
-            store4<OUTD>(o, (static_cast<size_t>(tok0 + t) * H + h) * D + Cfg::ROWS * vb + 16 * wave + 4 * g4,
-                         oa[a]);
+            store4<OUTD>(o, (static_cast<size_t>(tok0 + t) * H + h) * D + Cfg::ROWS * vb + 16 * rt + 4 * g4,
+                         oa[u]);
         }
       }
 
       __builtin_amdgcn_sched_barrier(0);
-      // S <- gamma_C S + (diag(D) U)^T K, as S^T = gamma_C S^T + K^T diag(D) U.
-      // K^T fragments (features 16 jt + c16; slots = tokens 32 kb + 4 g4 + e
-      // and 32 kb + 16 + 4 g4 + e) come from transpose reads of the K rows,
-      // running ahead of the products that consume them.
-      bf16x8 kt[CB][ND];
+      // S <- gamma_C S + (diag(D) U)^T K, as S^T = gamma_C S^T + K^T diag(D) U,
+      // on this wave's column tiles.  K^T fragments (features 16 jt + c16;
+      // slots = tokens 32 kb + 4 g4 + e and 32 kb + 16 + 4 g4 + e) come from
+      // transpose reads of the K rows, running ahead of the products that
+      // consume them.
+      bf16x8 kt[CB][JT];
 #pragma unroll
       for (int kb = 0; kb < CB; ++kb)
 #pragma unroll
-        for (int jt = 0; jt < ND; ++jt) {
-          const shortx4 lo = read_tr4(Kl, D, CHD, 32 * kb, 16 * jt, c16, g4);
-          const shortx4 hi = read_tr4(Kl, D, CHD, 32 * kb + 16, 16 * jt, c16, g4);
-          kt[kb][jt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        for (int jl = 0; jl < JT; ++jl) {
+          const shortx4 lo = read_tr4(Kl, D, CHD, 32 * kb, 16 * (jt0 + jl), c16, g4);
+          const shortx4 hi = read_tr4(Kl, D, CHD, 32 * kb + 16, 16 * (jt0 + jl), c16, g4);
+          kt[kb][jl] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
       const float gam_end = Gl[C - 1];
 #pragma unroll
-      for (int jt = 0; jt < ND; ++jt) S[jt] *= gam_end;
+      for (int jl = 0; jl < JT; ++jl) S[jl] *= gam_end;
 #pragma unroll
       for (int kb = 0; kb < CB; ++kb)
 #pragma unroll
-        for (int jt = 0; jt < ND; ++jt) {
-          bf16x8 kk[1] = {kt[kb][jt]};
-          mma_planes<1, 2>(S[jt], kk, udb[kb]);
+        for (int jl = 0; jl < JT; ++jl) {
+          bf16x8 kk[1] = {kt[kb][jl]};
+          mma_planes<1, 2>(S[jl], kk, udb[kb]);
         }
-      lead_interleave<8, 2 * CB * ND>();
+      lead_interleave<8, 2 * CB * JT>();
       __builtin_amdgcn_sched_barrier(0);
       if (fixed) {
         float* fx = fixed + (static_cast<size_t>(s) * H + h) * D * D + static_cast<size_t>(vrow) * D;
 #pragma unroll
-        for (int jt = 0; jt < ND; ++jt)
-          *reinterpret_cast<floatx4*>(fx + 16 * jt + 4 * g4) = S[jt];
+        for (int jl = 0; jl < JT; ++jl)
+          *reinterpret_cast<floatx4*>(fx + 16 * (jt0 + jl) + 4 * g4) = S[jl];
       }
       bare_barrier();  // chunk s is done with its buffer; chunk s + 1 is in LDS
     }
@@ -528,29 +623,61 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
     // column vrow of the (sequence, head)'s matrix: element (j, vrow) = S[vrow][j]
     float* so = state_out + (static_cast<size_t>(n) * H + h) * D * D;
 #pragma unroll
-    for (int jt = 0; jt < ND; ++jt)
+    for (int jl = 0; jl < JT; ++jl)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) so[static_cast<size_t>(16 * jt + 4 * g4 + e) * D + vrow] = S[jt][e];
+      for (int e = 0; e < 4; ++e)
+        so[static_cast<size_t>(16 * (jt0 + jl) + 4 * g4 + e) * D + vrow] = S[jl][e];
   } else if (state_out) {
 #pragma unroll
-    for (int jt = 0; jt < ND; ++jt)
-      *reinterpret_cast<floatx4*>(state_out + sbase + 16 * jt + 4 * g4) = S[jt];
+    for (int jl = 0; jl < JT; ++jl)
+      *reinterpret_cast<floatx4*>(state_out + sbase + 16 * (jt0 + jl) + 4 * g4) = S[jl];
   }
 }
 
+// Workgroups of the column-split form (NH = 2) that fit the GPU at once: MI355X
+// has 256 compute units and one scan workgroup fills one (its LDS).
+constexpr int64_t kSplitMaxGroups = 256;
+
+template <int D, int C, Dt OUTD, bool OUT, int NH>
+hipError_t scan_launch(const void* q, const void* k, const void* v, const int32_t* cu,
+                       const int32_t* offs, const ChunkFactors& f, const float* state_in,
+                       float* state_out, float* fixed, void* o, int N, int H, int n_slots,
+                       int T_total, int flags, hipStream_t stream) {
+  const int64_t pairs = static_cast<int64_t>(N) * H;
+  const int64_t groups = (pairs + kXcds - 1) / kXcds * kXcds * ScanCfg<D, C, NH>::NVB;
+  if (groups > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((chunk_scan_kernel<D, C, OUTD, OUT, NH>), dim3(static_cast<unsigned>(groups)),
+                     dim3(kThreads), 0, stream, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), cu, offs, f,
+                     state_in, state_out, fixed, o, N, H, n_slots, T_total, flags);
+  return hipGetLastError();
+}
+
+// The scan is a chain of dependent chunk steps per (sequence, head), so its
+// time is the step latency times the chunks of the longest sequence as long
+// as the workgroups fit the GPU at once.  Splitting every 16-row state tile
+// over two SIMDs (NH = 2) cuts a step's matrix products per wave from 132 to
+// 75 for twice the workgroups; it is taken when those still fit at once.
+// Both forms add the two column halves' contractions in the same order, so
+// their results are identical bit for bit.
 template <int D, int C, Dt OUTD>
 hipError_t scan_t(const void* q, const void* k, const void* v, const int32_t* cu,
                   const int32_t* offs, const ChunkFactors& f, const float* state_in,
                   float* state_out, float* fixed, void* o, int N, int H, int n_slots, int T_total,
                   int flags, hipStream_t stream) {
-  const int64_t pairs = static_cast<int64_t>(N) * H;
-  const int64_t groups = (pairs + kXcds - 1) / kXcds * kXcds * ScanCfg<D, C>::NVB;
-  if (groups > INT32_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((chunk_scan_kernel<D, C, OUTD>), dim3(static_cast<unsigned>(groups)),
-                     dim3(kThreads), 0, stream, static_cast<const uint16_t*>(q),
-                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), cu, offs, f,
-                     state_in, state_out, fixed, o, N, H, n_slots, T_total, flags);
-  return hipGetLastError();
+  const int64_t split_groups = (static_cast<int64_t>(N) * H + kXcds - 1) / kXcds * kXcds *
+                               ScanCfg<D, C, 2>::NVB;
+  const bool split = split_groups <= kSplitMaxGroups;
+#define GDR_SCAN_L(OUT_, NH_)                                                                      \
+  return scan_launch<D, C, OUTD, OUT_, NH_>(q, k, v, cu, offs, f, state_in, state_out, fixed, o,  \
+                                            N, H, n_slots, T_total, flags, stream)
+  if (o) {
+    if (split) GDR_SCAN_L(true, 2);
+    GDR_SCAN_L(true, 1);
+  }
+  if (split) GDR_SCAN_L(false, 2);
+  GDR_SCAN_L(false, 1);
+#undef GDR_SCAN_L
 }
 
 __global__ __launch_bounds__(256) void segment_ranges_kernel(

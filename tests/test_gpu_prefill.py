@@ -149,6 +149,36 @@ def test_prefill_packing_invariance(schedule):
         assert torch.equal(single["state_out"][0], packed["state_out"][n])
 
 
+def test_prefill_scan_forms_agree_bitwise():
+    # The sequential scan splits each 16-row state tile over two SIMDs when the
+    # workgroups of a batch fit the GPU at once (few (sequence, head) pairs)
+    # and keeps whole tiles per wave otherwise; both add the two column
+    # halves' contractions in the same order, so a packed batch of many pairs
+    # (whole tiles) and its sequences run alone (split tiles) agree bit for bit.
+    rng = np.random.default_rng(113)
+    lens = [int(x) for x in rng.integers(1, 200, size=33)]
+    lens[3], lens[10] = 0, 64
+    d = workload(3, seed=113, seqlens=lens, H=8)
+    say(f"prefill scan forms: N={len(lens)} H=8 T={d['T']} (packed: whole tiles; alone: split)")
+    packed = run_prefill(d, schedule="scan")
+    check_against_oracle(d, packed, d["chunk"], check_locals=False)
+    cu = d["cu_seqlens"]
+    for n in (0, 3, 10, 32):
+        a, b = int(cu[n]), int(cu[n + 1])
+        sub = dict(d)
+        for key in ("q", "k", "v", "g", "beta"):
+            sub[key] = np.ascontiguousarray(d[key][a:b])
+        sub["state0"] = np.ascontiguousarray(d["state0"][n:n + 1])
+        sub["cu_seqlens"] = np.array([0, b - a], dtype=np.int32)
+        sub["N"], sub["T"] = 1, b - a
+        single = run_prefill(sub, schedule="scan")
+        assert torch.equal(single["o"], packed["o"][a:b])
+        assert torch.equal(single["state_out"][0], packed["state_out"][n])
+        c0 = int(np.sum((np.array(lens[:n]) + 63) // 64))
+        nc = (b - a + 63) // 64
+        assert torch.equal(single["fixed"][:nc], packed["fixed"][c0:c0 + nc])
+
+
 def test_prefill_all_sequences_empty():
     import gated_delta_rule_100_amd as gdr
     say("prefill with T_total = 0")
