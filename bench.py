@@ -7,7 +7,10 @@ One step = one pass over both forms of the path on synthetic inputs:
   * prefill: chunked prefill of 4 sequences x 4096 tokens, 16 heads,
              dk = dv = 128, chunk 64, bf16 q/k/v, fp32 gates and states.
 The headline `value` is the decode state bandwidth (state bytes read + written
-per step / decode time); the prefill throughput is reported beside it.
+per step / decode time); the prefill throughput is reported beside it.  The
+other prefill workloads (varlen: 8 sequences, 32768 tokens, 32 heads; long:
+one 131072-token sequence, 4 heads) are timed after the step, outside it, and
+reported as `prefill_varlen` and `prefill_long`.
 
 Decode is measured cold: four state buffers (512 MiB, more than the 256 MB
 Infinity Cache) are used in rotation.  Prefill writes a 1 GiB scrub buffer
@@ -16,6 +19,7 @@ HBM before timing starts.  Kernel times come from HIP events recorded on the
 stream the kernels are launched on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--no-other-prefill] [--prefill-only IDX]
 """
 from __future__ import annotations
 
@@ -52,12 +56,27 @@ PRE_FACTOR_R = PRE_FACTOR_W + 2 * 16384
 PRE_SCAN_BYTES = PRE_IO_BYTES + PRE_CHUNK_HEADS * (PRE_FACTOR_W + PRE_FACTOR_R)
 
 
+def io_min_bytes(idx):
+    """Bytes any implementation must move for prefill workload idx: q, k, v, o
+    (bf16), g and beta (fp32) per token and head, and the fp32 states in and
+    out (the long workload has no initial state)."""
+    from gdr_synth import WORKLOADS
+    spec = WORKLOADS[idx]
+    tokens = {2: PRE_TOKENS, 3: 32768, 4: 131072}[idx]
+    n_seq = {2: PRE_B, 3: 8, 4: 1}[idx]
+    H, D = spec["H"], spec["dk"]
+    states = (2 if spec["state0"] else 1) * n_seq * H * D * D * 4
+    return tokens * H * (3 * D * 2 + D * 2 + 8) + states
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-prefill", action="store_true",
+                    help="skip timing the varlen and long-sequence prefill workloads")
     ap.add_argument("--cpu-seconds", type=float, default=16.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--prefill-only", type=int, default=None, metavar="IDX",
@@ -256,6 +275,16 @@ def main():
     print(f"[bench] decode {dec}", file=sys.stderr, flush=True)
     pre = bench_prefill(torch, gdr, args.steps, args.warmup)
     print(f"[bench] prefill {pre}", file=sys.stderr, flush=True)
+    # the other prefill workloads, reported beside the step (not part of it)
+    others = {}
+    if not args.no_other_prefill:
+        for idx, key in ((3, "prefill_varlen"), (4, "prefill_long")):
+            r = bench_prefill(torch, gdr, max(3, min(args.steps, 10)), min(args.warmup, 2), idx)
+            print(f"[bench] {key} {r}", file=sys.stderr, flush=True)
+            t = r["ms_mean"] / 1e3
+            others[key] = {"workload": r["workload"], "value": round(r["tokens"] / t, 1),
+                           "unit": "tokens/s", "ms": round(r["ms_mean"], 4),
+                           "io_min_frac": round(io_min_bytes(idx) / t / 1e9 / HBM_PEAK_GBS, 4)}
     copy_gbs = copy_bandwidth(torch)
     print(f"[bench] device copy {copy_gbs:.1f} GB/s", file=sys.stderr, flush=True)
     cpu = None
@@ -303,6 +332,7 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    out.update(others)
     print(json.dumps(out))
 
 

@@ -9,8 +9,10 @@ Recipe (numpy PCG64, seed = workload index unless stated):
     g_pre, beta_pre, [S0 (only when the workload has an initial state)];
   * q and k are L2-normalised per (token, head) over dk, in float64;
   * g = -softplus(g_pre) (so alpha = exp(g) lies in (0, 1)), beta = sigmoid(beta_pre);
-    the "slow" gate variant uses g = -0.01 * softplus(g_pre) and the "unit"
-    variant g = 0 (alpha = 1), beta unchanged;
+    the "slow" gate variant uses g = -0.01 * softplus(g_pre), the "steep"
+    variant g = -4 * softplus(g_pre) (in-chunk decays far below e^-87, so
+    that decay factors underflow) and the "unit" variant g = 0 (alpha = 1),
+    beta unchanged;
   * S0 = 0.02 * N(0, 1) (standard deviation 0.02);
   * everything is cast to float32; q, k, v are then rounded to bfloat16 with
     round-to-nearest-even where the workload is bf16.  Gates and states stay
@@ -103,7 +105,7 @@ def generate(seqlens, H: int, dk: int, dv: int, dtype: str = "bf16",
     seqlens: list of per-sequence token counts (zeros allowed), or None when
         `lengths_from_rng` = (n_seq, total, cap) asks for the varlen recipe.
     dtype: "bf16" or "f32" for q, k, v.
-    gate: "std" | "slow" | "unit".
+    gate: "std" | "slow" | "steep" | "unit".
     keys: "gauss" (the default recipe) or "orthonormal": per sequence and head
         the keys are the rows of an orthonormal set (QR of a Gaussian draw),
         which needs each sequence no longer than dk.
@@ -146,6 +148,8 @@ def generate(seqlens, H: int, dk: int, dv: int, dtype: str = "bf16",
         g = -_softplus(g_pre)
     elif gate == "slow":
         g = -0.01 * _softplus(g_pre)
+    elif gate == "steep":
+        g = -4.0 * _softplus(g_pre)
     elif gate == "unit":
         g = np.zeros_like(g_pre)
     else:

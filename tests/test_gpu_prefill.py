@@ -78,6 +78,8 @@ CASES = {
     "varlen-ragged-H2-d128-C64": (3, dict(seqlens=[1, 63, 64, 65, 0, 200, 130, 7], H=2)),
     "varlen-ragged-slow": (3, dict(seqlens=[129, 0, 1, 77], H=2, gate="slow")),
     "long-T8192-H4-slow-gates": (4, dict(seqlens=[8192], H=4, gate="slow")),
+    # in-chunk decays far below e^-87: decay factors and gamma underflow
+    "steep-gates-ragged": (2, dict(seqlens=[200, 130, 64, 5], H=2, gate="steep")),
     "d64-C64-bf16": (2, dict(seqlens=[150, 64, 3], H=3, dk=64, dv=64, gate="slow")),
     "d128-C16-bf16": (2, dict(seqlens=[70, 33], H=2, chunk=16, gate="slow")),
     "d128-C16-f32": (0, dict(seqlens=[40, 17, 0], H=2, dk=128, dv=128, gate="slow", state0=True)),
