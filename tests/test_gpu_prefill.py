@@ -78,6 +78,11 @@ CASES = {
     "varlen-ragged-H2-d128-C64": (3, dict(seqlens=[1, 63, 64, 65, 0, 200, 130, 7], H=2)),
     "varlen-ragged-slow": (3, dict(seqlens=[129, 0, 1, 77], H=2, gate="slow")),
     "long-T8192-H4-slow-gates": (4, dict(seqlens=[8192], H=4, gate="slow")),
+    # skewed lengths with enough (sequence, head) pairs to fill the GPU: more
+    # scan workgroups than compute units, whole-tile form
+    "varlen-skewed-H32": (3, dict(seqlens=[4000, 50, 300, 64, 1, 0, 700, 129], H=32)),
+    "varlen-skewed-H32-slow": (3, dict(seqlens=[70, 3100, 0, 1100, 64, 640, 1, 9], H=32,
+                                       gate="slow")),
     # in-chunk decays far below e^-87: decay factors and gamma underflow
     "steep-gates-ragged": (2, dict(seqlens=[200, 130, 64, 5], H=2, gate="steep")),
     "d64-C64-bf16": (2, dict(seqlens=[150, 64, 3], H=3, dk=64, dv=64, gate="slow")),
