@@ -223,6 +223,248 @@ __global__ __launch_bounds__(kDecodeThreads) void mtp_kernel(
   }
 }
 
+// Multi-token decode on the matrix cores (6 <= T <= 8 tokens, no per-token
+// states; the kernel itself takes any 1 <= T <= 8).  The T tokens of a (sequence, head) are one chunk of the chunked
+// form of the recurrence (derived from it: G_t = g_1 + ... + g_t,
+// gamma_t = e^{G_t}, D_t = e^{G_T - G_t}, A_ts = beta_t e^{G_t - G_s} k_t.k_s for
+// s < t, Tinv = (I + A)^{-1}, P_ts = e^{G_t - G_s} q_t.k_s for s <= t):
+//   Z = S K^T, Y = S Q^T                         (one product: [K; Q] stacked)
+//   U = (diag(beta) (V - diag(gamma) Z)) Tinv^T  per state row
+//   O = diag(gamma) Y + U P^T                    (o_t = S_t q_t for every t)
+//   S <- gamma_T S + U diag(D) K
+// all in fp32 on v_mfma_f32_16x16x4_f32.  A workgroup holds 64 state rows, a
+// wave 16: lane (c, g) holds S[row c][16 kt + 4 g + e], which is at once the A
+// operand of S K^T (the contraction index permuted the same way in both
+// operands) and the accumulator layout of S^T <- gamma_T S^T + K^T diag(D) U^T,
+// so the state is never moved between lanes.  The T x T factors are formed by
+// every workgroup of a head (they are small).
+constexpr int kMtpWaves = 4;               // 16 state rows each
+constexpr int kMtpMaxT = 8;
+// Below this many tokens the token-by-token kernel is faster: the chunked one
+// costs about the same for any T <= 8 (on 64 sequences x 32 heads, d = 128,
+// cold: 59 us at T = 2, 61 at T = 4, 65 at T = 8, against 49.5, 57 and 78
+// token by token).
+constexpr int kMtpChunkMinT = 6;
+
+// Waves (16 state rows each) of a workgroup at dv.
+template <int DV>
+constexpr int mtp_waves() {
+  return DV / 16 < kMtpWaves ? DV / 16 : kMtpWaves;
+}
+
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int DK, int DV, Dt IN, Dt OUT>
+__global__ __launch_bounds__(64 * kMtpWaves) void mtp_chunk_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const float* state_in,
+    float* state_out, void* __restrict__ o, int NH, int H, int T) {
+  constexpr int NW = mtp_waves<DV>(), kMtpThreads = 64 * NW, kMtpRows = 16 * NW;
+  constexpr int WPP = DV / kMtpRows;  // workgroups per (sequence, head)
+  constexpr int KT = DK / 16;         // 16-column tiles of the state
+  constexpr int LDK = DK + 4;         // padded row of the token matrix (floats)
+  constexpr int TPT = 16 * DK / kMtpThreads;  // token-matrix elements per thread
+  constexpr int XLD = 9;              // row stride of the per-wave R / U exchange
+  // factor region offsets (floats)
+  constexpr int F_GRAW = 0, F_B = 8, F_G = 16, F_GAM = 24, F_D = 32, F_TINV = 40, F_P = 104,
+                F_DOT = 168, F_A = 296, F_N = 360;
+  static_assert(DV % kMtpRows == 0 && DK % 16 == 0, "shape");
+  static_assert(kMtpThreads >= 128, "the factor step gives one thread to each of the 2 x 64 dots");
+  __shared__ __align__(16) float sKQ[16 * LDK];  // rows 0-7: k_t, rows 8-15: q_t (zero past T)
+  __shared__ __align__(16) float sF[F_N];
+  __shared__ __align__(16) float sX[NW][16 * XLD];
+
+  const int pair = blockIdx.x / WPP, r0 = (blockIdx.x % WPP) * kMtpRows;
+  if (pair >= NH) return;
+  const int n = pair / H, h = pair % H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c = lane & 15, gq = lane >> 4;
+  const int rbase = r0 + 16 * wave;  // first state row of this wave
+  const size_t tok0 = static_cast<size_t>(n) * T;
+
+  // Token inputs first (a wait for them then does not wait for the state).
+  float tk[TPT];
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    const int idx = tid + kMtpThreads * i, rr = idx / DK, col = idx % DK, t = rr & 7;
+    tk[i] = t < T ? load_scalar<IN>(rr < 8 ? k : q, ((tok0 + t) * H + h) * DK + col) : 0.f;
+  }
+  float gv = 0.f, bv = 0.f;
+  if (tid < kMtpMaxT && tid < T) {
+    gv = g[(tok0 + tid) * H + h];
+    bv = beta[(tok0 + tid) * H + h];
+  }
+  // v of this lane's four rows at token c (lanes c < T of the first 8)
+  float vv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (c < T) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      vv[e] = load_scalar<IN>(v, ((tok0 + c) * H + h) * DV + rbase + 4 * gq + e);
+  }
+  // this lane's state row, 16-column tiles: S[row c][16 kt + 4 gq + e]
+  const floatx4* Sin = reinterpret_cast<const floatx4*>(state_in + static_cast<size_t>(pair) * DV * DK);
+  floatx4 st[KT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+    st[kt] = __builtin_nontemporal_load(&Sin[((rbase + c) * DK + 16 * kt + 4 * gq) / 4]);
+
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    const int idx = tid + kMtpThreads * i;
+    sKQ[(idx / DK) * LDK + idx % DK] = tk[i];
+  }
+  if (tid < kMtpMaxT) {
+    sF[F_GRAW + tid] = gv;
+    sF[F_B + tid] = bv;
+  }
+  lds_barrier();  // the state loads stay in flight
+
+  // Gate prefix (fixed order; padding adds g = 0, so G_7 = G_T) and the dot
+  // products k_t.k_s (threads 0-63) and q_t.k_s (64-127), t, s < 8.
+  if (tid < kMtpMaxT) {
+    float G = 0.f, Gt = 0.f;
+    for (int s = 0; s < kMtpMaxT; ++s) {
+      G += sF[F_GRAW + s];
+      if (s == tid) Gt = G;
+    }
+    sF[F_G + tid] = Gt;
+    sF[F_GAM + tid] = expf(Gt);
+    sF[F_D + tid] = tid < T ? expf(G - Gt) : 0.f;
+  }
+  if (tid < 128) {
+    const int t = (tid >> 3) & 7, s = tid & 7;
+    const float* a = sKQ + ((tid >> 6) ? 8 + t : t) * LDK;
+    const float* b = sKQ + s * LDK;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependent chains
+#pragma unroll 8
+    for (int j = 0; j < DK; j += 4) {
+      const floatx4 x = *reinterpret_cast<const floatx4*>(a + j);
+      const floatx4 y = *reinterpret_cast<const floatx4*>(b + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(x[e], y[e], acc[e]);
+    }
+    sF[F_DOT + tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  }
+  lds_barrier();
+  // A (threads 0-63) and P (64-127), one element each
+  if (tid < 128) {
+    const int t = (tid >> 3) & 7, s = tid & 7;
+    const float decay = expf(sF[F_G + t] - sF[F_G + s]);
+    if (tid < 64)
+      sF[F_A + 8 * t + s] = s < t ? sF[F_B + t] * decay * sF[F_DOT + tid] : 0.f;
+    else
+      sF[F_P + 8 * t + s] = s <= t ? decay * sF[F_DOT + tid] : 0.f;
+  }
+  lds_barrier();
+  // Tinv = (I + A)^{-1} by forward substitution (thread j: column j)
+  if (tid < kMtpMaxT) {
+    const int j = tid;
+    float x[kMtpMaxT];
+#pragma unroll
+    for (int t = 0; t < kMtpMaxT; ++t) {
+      float acc = t == j ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < t; ++s) acc = fmaf(-sF[F_A + 8 * t + s], x[s], acc);
+      x[t] = acc;
+    }
+#pragma unroll
+    for (int t = 0; t < kMtpMaxT; ++t) sF[F_TINV + 8 * t + j] = x[t];
+  }
+  lds_barrier();
+
+  // [Z | Y] = S [K; Q]^T: lane (c, gq) ends with row 4 gq + e of the wave and
+  // column c (token c of Z for c < 8, token c - 8 of Y for c >= 8).
+  floatx4 zy0 = {0.f, 0.f, 0.f, 0.f}, zy1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    const floatx4 kc = *reinterpret_cast<const floatx4*>(sKQ + c * LDK + 16 * kt + 4 * gq);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (kt & 1) zy1 = mfma4(st[kt][e], kc[e], zy1);
+      else zy0 = mfma4(st[kt][e], kc[e], zy0);
+    }
+  }
+  const floatx4 zy = zy0 + zy1;
+
+  // R = beta (v - gamma Z) on lanes c < 8, exchanged through LDS as [row][t]
+  float* X = sX[wave];
+  if (c < kMtpMaxT) {
+    const float bt = sF[F_B + c], gt = sF[F_GAM + c];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) X[(4 * gq + e) * XLD + c] = bt * (vv[e] - gt * zy[e]);
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  // U = R Tinv^T: A[row c][t] = R, B[t][t' = c] = Tinv[c][t]
+  floatx4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int t = 4 * ks + gq;
+    const float a = X[c * XLD + t];
+    const float b = c < kMtpMaxT ? sF[F_TINV + 8 * c + t] : 0.f;
+    u = mfma4(a, b, u);
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  if (c < kMtpMaxT) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) X[(4 * gq + e) * XLD + c] = u[e];
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  // U in the A layout (row c, token 4 ks + gq), for O and (scaled by D) the update
+  float ua[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) ua[ks] = X[c * XLD + 4 * ks + gq];
+
+  // O = gamma Y + U P^T on lanes c >= 8 (token c - 8, rows 4 gq + e)
+  floatx4 pu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const float b = c >= kMtpMaxT ? sF[F_P + 8 * (c - kMtpMaxT) + 4 * ks + gq] : 0.f;
+    pu = mfma4(ua[ks], b, pu);
+  }
+  if (c >= kMtpMaxT && c - kMtpMaxT < T) {
+    const int t = c - kMtpMaxT;
+    const float gt = sF[F_GAM + t];
+    const size_t ob = ((tok0 + t) * H + h) * DV + rbase + 4 * gq;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_scalar<OUT>(o, ob + e, fmaf(gt, zy[e], pu[e]));
+  }
+
+  // S^T <- gamma_T S^T + K^T diag(D) U^T, tile by tile: A[j][t] = K[t][16 kt + j],
+  // B[t][row c] = D_t U[c][t]; the output lands on lane (c, gq), element e =
+  // S[row c][16 kt + 4 gq + e], where the state already is.
+  const float gam_end = sF[F_GAM + kMtpMaxT - 1];
+  float ub[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) ub[ks] = sF[F_D + 4 * ks + gq] * ua[ks];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    floatx4 acc = st[kt] * gam_end;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) acc = mfma4(sKQ[(4 * ks + gq) * LDK + 16 * kt + c], ub[ks], acc);
+    st[kt] = acc;
+  }
+  if (state_out) {
+    floatx4* Sout = reinterpret_cast<floatx4*>(state_out + static_cast<size_t>(pair) * DV * DK);
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+      __builtin_nontemporal_store(st[kt], &Sout[((rbase + c) * DK + 16 * kt + 4 * gq) / 4]);
+  }
+}
+
+template <int DK, int DV, Dt IN, Dt OUT>
+hipError_t launch_mtp_chunk_t(const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, const float* state_in, float* state_out, void* o,
+                              int NH, int H, int T, hipStream_t stream) {
+  const int64_t groups = static_cast<int64_t>(NH) * (DV / (16 * mtp_waves<DV>()));
+  if (groups > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((mtp_chunk_kernel<DK, DV, IN, OUT>), dim3(static_cast<unsigned>(groups)),
+                     dim3(64 * mtp_waves<DV>()), 0, stream, q, k, v, g, beta, state_in, state_out, o,
+                     NH, H, T);
+  return hipGetLastError();
+}
+
 template <int DK, int DV, Dt IN, Dt OUT>
 hipError_t launch_mtp_t(const void* q, const void* k, const void* v, const float* g,
                         const float* beta, const float* state_in, float* state_out, void* o,
@@ -277,9 +519,15 @@ hipError_t launch_mtp(const void* q, const void* k, const void* v, const float* 
                       int out_dtype, hipStream_t stream) {
   (void)dv;
   const int NH = N * H;
+  // 6..8 tokens without per-token states: the chunked form on the matrix
+  // cores; otherwise (and for T = 1, which then equals the decode step bit for
+  // bit) the token-by-token kernel.
+  const bool chunked = inter == nullptr && T >= kMtpChunkMinT && T <= kMtpMaxT;
 #define GDR_MTP(D_, IN_, OUT_)                                                                \
-  return launch_mtp_t<D_, D_, IN_, OUT_>(q, k, v, g, beta, state_in, state_out, o, inter, NH, H, \
-                                         T, stream)
+  return chunked ? launch_mtp_chunk_t<D_, D_, IN_, OUT_>(q, k, v, g, beta, state_in, state_out, \
+                                                         o, NH, H, T, stream)                    \
+                 : launch_mtp_t<D_, D_, IN_, OUT_>(q, k, v, g, beta, state_in, state_out, o,     \
+                                                   inter, NH, H, T, stream)
   if (dk == 128) {
     if (in_dtype == 0 && out_dtype == 0) GDR_MTP(128, Dt::BF16, Dt::BF16);
     if (in_dtype == 0) GDR_MTP(128, Dt::BF16, Dt::F32);

@@ -85,8 +85,36 @@ def test_mtp_T1_equals_decode_step_bitwise():
         assert torch.equal(s1, s2)
 
 
+# Without per-token states, 6 <= T <= 8 tokens take the chunked kernel (the T
+# tokens as one chunk of the chunked form, on fp32 matrix products).
+CHUNKED_CASES = {
+    "N3-T6-H2-d128-bf16": (3, 6, 2, 128, "bf16", "std"),
+    "N2-T8-H3-d64-f32": (2, 8, 3, 64, "f32", "std"),
+    "N4-T7-H2-d128-f32": (4, 7, 2, 128, "f32", "std"),
+    "N3-T7-H2-d128-bf16-slow": (3, 7, 2, 128, "bf16", "slow"),
+    "N2-T6-H2-d64-bf16-steep": (2, 6, 2, 64, "bf16", "steep"),
+    "N2-T8-H2-d128-f32-unit": (2, 8, 2, 128, "f32", "unit"),
+}
+
+
+@pytest.mark.parametrize("name", list(CHUNKED_CASES))
+def test_mtp_chunked_matches_oracle(name):
+    N, T, H, d, dtype, gate = CHUNKED_CASES[name]
+    say(f"mtp chunked {name}")
+    data, _, x = mtp_inputs(N, T, H, d, dtype, seed=320 + T, gate=gate)
+    o, so, _ = run_mtp(x, inter=False)
+    o_ref, s_ref, _ = oracle.recurrent(data["q"], data["k"], data["v"], data["g"], data["beta"],
+                                       data["cu_seqlens"], data["state0"])
+    tol = tol_for(data)
+    errs = {"o": rel_err(host64(o).reshape(o_ref.shape), o_ref),
+            "state_out": rel_err(host64(so), s_ref)}
+    say(f"  errors: {errs}")
+    for key, e in errs.items():
+        assert e <= tol, (key, e)
+
+
 def test_mtp_in_place_and_uncommitted():
-    N, T, H, d = 3, 5, 2, 128
+    N, T, H, d = 3, 6, 2, 128
     say("mtp in place / no final state")
     _, _, x = mtp_inputs(N, T, H, d, "bf16", seed=311)
     ref_o, ref_s, ref_i = run_mtp(x)
@@ -96,9 +124,14 @@ def test_mtp_in_place_and_uncommitted():
     assert so is None and torch.equal(x["state0"], before)
     assert torch.equal(o, ref_o) and torch.equal(I, ref_i)
     assert torch.equal(I[:, -1], ref_s)
-    # in place, without intermediates
+    # without intermediates (6 <= T <= 8: the chunked kernel): a new final state
+    # and in place give the same bits, and both agree with the token-by-token
+    # kernel to rounding
+    o2, so2, _ = run_mtp(x, inter=False)
     o, so, _ = run_mtp(x, state_out="inplace", inter=False)
-    assert torch.equal(o, ref_o) and torch.equal(x["state0"], ref_s)
+    assert torch.equal(o, o2) and torch.equal(x["state0"], so2)
+    assert rel_err(host64(o), host64(ref_o)) <= 1e-5
+    assert rel_err(host64(so2), host64(ref_s)) <= 1e-5
 
 
 def test_mtp_bf16_output_is_rne_and_deterministic():
@@ -145,4 +178,24 @@ def test_mtp_full_size_sampled():
         e = (rel_err(oh[rows, h], o_ref[rows, h]), rel_err(sh[n, h], s_ref[n, h]),
              rel_err(Ih[rows, h], cs_ref[rows, h]))
         say(f"  pair ({n},{h}): o {e[0]:.2e} state {e[1]:.2e} inter {e[2]:.2e}")
+        assert max(e) <= 1e-3
+
+
+def test_mtp_chunked_full_size_sampled():
+    # the decode workload's shape with 8 draft tokens, without per-token states
+    N, T, H, d = 64, 8, 32, 128
+    say("mtp chunked full size N=64 T=8 H=32 d=128 bf16")
+    data, _, x = mtp_inputs(N, T, H, d, "bf16", seed=315)
+    o, so, _ = run_mtp(x, torch.bfloat16, inter=False)
+    o32, so32, _ = run_mtp(x, inter=False)
+    assert torch.equal(o, o32.to(torch.bfloat16)) and torch.equal(so, so32)
+    pairs = [(0, 0), (17, 5), (63, 31), (40, 16)]
+    o_ref, s_ref, _ = oracle.recurrent(data["q"], data["k"], data["v"], data["g"], data["beta"],
+                                       data["cu_seqlens"], data["state0"], pairs=pairs)
+    oh = host64(o32).reshape(N * T, H, d)
+    sh = host64(so32)
+    for n, h in pairs:
+        rows = slice(n * T, (n + 1) * T)
+        e = (rel_err(oh[rows, h], o_ref[rows, h]), rel_err(sh[n, h], s_ref[n, h]))
+        say(f"  pair ({n},{h}): o {e[0]:.2e} state {e[1]:.2e}")
         assert max(e) <= 1e-3
