@@ -10,7 +10,8 @@ The headline `value` is the decode state bandwidth (state bytes read + written
 per step / decode time); the prefill throughput is reported beside it.  The
 other prefill workloads (varlen: 8 sequences, 32768 tokens, 32 heads; long:
 one 131072-token sequence, 4 heads) are timed after the step, outside it, and
-reported as `prefill_varlen` and `prefill_long`.
+reported as `prefill_varlen` and `prefill_long`, and multi-token decode (8
+draft tokens per sequence on the decode workload's shape) as `decode_mtp`.
 
 Decode is measured cold: four state buffers (512 MiB, more than the 256 MB
 Infinity Cache) are used in rotation.  Prefill writes a 1 GiB scrub buffer
@@ -76,7 +77,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-prefill", action="store_true",
-                    help="skip timing the varlen and long-sequence prefill workloads")
+                    help="skip timing the varlen and long-sequence prefill workloads and "
+                         "multi-token decode")
     ap.add_argument("--cpu-seconds", type=float, default=16.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--prefill-only", type=int, default=None, metavar="IDX",
@@ -127,6 +129,36 @@ def bench_decode(torch, gdr, steps, warmup):
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
     return dict(ms_mean=float(ms), wall_s=wall)
+
+
+def bench_mtp(torch, gdr, steps, warmup, T=8):
+    """Multi-token decode on the decode workload's shape (64 sequences x 32
+    heads, d = 128, bf16) with T draft tokens each and no per-token states,
+    cold (4 rotating state buffers, each updated in place)."""
+    from gdr_synth import generate
+    d = generate([T] * DEC_N, DEC_H, DEC_D, DEC_D, dtype="bf16", state0=True, seed=1)
+    di = to_dev(d, torch)
+    x = {key: di[key].view(DEC_N, T, DEC_H, -1) for key in ("q", "k", "v")}
+    g, b = di["g"].view(DEC_N, T, DEC_H), di["beta"].view(DEC_N, T, DEC_H)
+    bufs = [di["state0"].clone() for _ in range(4)]
+    o = torch.empty(DEC_N, T, DEC_H, DEC_D, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def launch(i):
+        gdr.gdr_decode_mtp(x["q"], x["k"], x["v"], g, b, bufs[i % 4], bufs[i % 4], o, None,
+                           stream=stream)
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        launch(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return dict(ms_mean=float(ms), T=T)
 
 
 def copy_bandwidth(torch, reps=10):
@@ -285,6 +317,14 @@ def main():
             others[key] = {"workload": r["workload"], "value": round(r["tokens"] / t, 1),
                            "unit": "tokens/s", "ms": round(r["ms_mean"], 4),
                            "io_min_frac": round(io_min_bytes(idx) / t / 1e9 / HBM_PEAK_GBS, 4)}
+        m = bench_mtp(torch, gdr, args.steps, args.warmup)
+        print(f"[bench] decode_mtp {m}", file=sys.stderr, flush=True)
+        t = m["ms_mean"] / 1e3
+        others["decode_mtp"] = {
+            "workload": f"multi-token decode N=64 T={m['T']} H=32 dk=dv=128 bf16, no per-token states",
+            "value": round(DEC_STATE_BYTES / t / 1e9, 2), "unit": "state GB/s",
+            "us": round(m["ms_mean"] * 1e3, 2),
+            "tokens_per_s": round(DEC_N * m["T"] / t, 1)}
     copy_gbs = copy_bandwidth(torch)
     print(f"[bench] device copy {copy_gbs:.1f} GB/s", file=sys.stderr, flush=True)
     cpu = None
