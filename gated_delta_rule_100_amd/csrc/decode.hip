@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kDecodeThreads) void mtp_kernel(
   }
 }
 
-// Multi-token decode on the matrix cores (6 <= T <= 8 tokens, no per-token
+// Multi-token decode on the matrix cores (5 <= T <= 8 tokens, no per-token
 // states; the kernel itself takes any 1 <= T <= 8).  The T tokens of a (sequence, head) are one chunk of the chunked
 // form of the recurrence (derived from it: G_t = g_1 + ... + g_t,
 // gamma_t = e^{G_t}, D_t = e^{G_T - G_t}, A_ts = beta_t e^{G_t - G_s} k_t.k_s for
@@ -242,9 +242,9 @@ constexpr int kMtpWaves = 4;               // 16 state rows each
 constexpr int kMtpMaxT = 8;
 // Below this many tokens the token-by-token kernel is faster: the chunked one
 // costs about the same for any T <= 8 (on 64 sequences x 32 heads, d = 128,
-// cold: 59 us at T = 2, 61 at T = 4, 65 at T = 8, against 49.5, 57 and 78
-// token by token).
-constexpr int kMtpChunkMinT = 6;
+// cold: about 59 us at T = 2 and 4, 60 at T = 6, 62 at T = 8, against 48, 58,
+// about 68 and 78 token by token).
+constexpr int kMtpChunkMinT = 5;
 
 // Waves (16 state rows each) of a workgroup at dv.
 template <int DV>
@@ -257,7 +257,9 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
 }
 
 template <int DK, int DV, Dt IN, Dt OUT>
-__global__ __launch_bounds__(64 * kMtpWaves) void mtp_chunk_kernel(
+// (at least 5 waves per SIMD: 84 VGPRs and no accumulation registers, against
+// 4 waves and a 32-register accumulator copy by default; 62 against 66 us)
+__global__ __launch_bounds__(64 * kMtpWaves, 5) void mtp_chunk_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* state_in,
     float* state_out, void* __restrict__ o, int NH, int H, int T) {
@@ -519,7 +521,7 @@ hipError_t launch_mtp(const void* q, const void* k, const void* v, const float* 
                       int out_dtype, hipStream_t stream) {
   (void)dv;
   const int NH = N * H;
-  // 6..8 tokens without per-token states: the chunked form on the matrix
+  // 5..8 tokens without per-token states: the chunked form on the matrix
   // cores; otherwise (and for T = 1, which then equals the decode step bit for
   // bit) the token-by-token kernel.
   const bool chunked = inter == nullptr && T >= kMtpChunkMinT && T <= kMtpMaxT;

@@ -104,7 +104,7 @@ gdr_status gdr_decode_step(const void* q, const void* k, const void* v,
  * (state_in for t = 0), and its output uses the updated state.  The result is
  * that of gdr_chunk_prefill over N packed sequences of T tokens, and T = 1 is
  * gdr_decode_step (bit for bit).  The state is read once and written once
- * whatever T is.  Without `inter`, 6 <= T <= 8 tokens are applied as one chunk
+ * whatever T is.  Without `inter`, 5 <= T <= 8 tokens are applied as one chunk
  * of the chunked form (fp32 matrix products), other T token by token; the two
  * agree to fp32 rounding, and each is deterministic.
  *

@@ -85,14 +85,14 @@ def test_mtp_T1_equals_decode_step_bitwise():
         assert torch.equal(s1, s2)
 
 
-# Without per-token states, 6 <= T <= 8 tokens take the chunked kernel (the T
+# Without per-token states, 5 <= T <= 8 tokens take the chunked kernel (the T
 # tokens as one chunk of the chunked form, on fp32 matrix products).
 CHUNKED_CASES = {
     "N3-T6-H2-d128-bf16": (3, 6, 2, 128, "bf16", "std"),
     "N2-T8-H3-d64-f32": (2, 8, 3, 64, "f32", "std"),
     "N4-T7-H2-d128-f32": (4, 7, 2, 128, "f32", "std"),
     "N3-T7-H2-d128-bf16-slow": (3, 7, 2, 128, "bf16", "slow"),
-    "N2-T6-H2-d64-bf16-steep": (2, 6, 2, 64, "bf16", "steep"),
+    "N2-T5-H2-d64-bf16-steep": (2, 5, 2, 64, "bf16", "steep"),
     "N2-T8-H2-d128-f32-unit": (2, 8, 2, 128, "f32", "unit"),
 }
 
@@ -124,7 +124,7 @@ def test_mtp_in_place_and_uncommitted():
     assert so is None and torch.equal(x["state0"], before)
     assert torch.equal(o, ref_o) and torch.equal(I, ref_i)
     assert torch.equal(I[:, -1], ref_s)
-    # without intermediates (6 <= T <= 8: the chunked kernel): a new final state
+    # without intermediates (5 <= T <= 8: the chunked kernel): a new final state
     # and in place give the same bits, and both agree with the token-by-token
     # kernel to rounding
     o2, so2, _ = run_mtp(x, inter=False)
