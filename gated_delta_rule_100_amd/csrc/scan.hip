@@ -361,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
   // Output token tiles of this wave: all of them when NH = 1; with NH = 2 the
   // column halves split them so that each does three 32-deep blocks of
   // U^T P^T: half 0 takes tiles 0 and 3, half 1 tiles 1 and 2 (tile a needs
-  // blocks kb <= a / 2).  Tile u of half x (NH = 2):
+  // blocks kb <= a / 2; four token tiles, C = 64).  Tile u of half x (NH = 2):
   auto otile = [](int x, int u) { return u == 0 ? x : 3 - x; };
   float* xch = reinterpret_cast<float*>(smem + Cfg::OFF_X);
   auto xslot = [&](int w, int x) {
@@ -549,10 +549,9 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
 #pragma unroll
         for (int kb = 0; kb < CB; ++kb) {
           // tiles with a / 2 >= kb: NH = 1: a >= 2 kb; NH = 2: u >= kb
-          constexpr int UB0 = 0;
           bf16x8 pa[NO][2];
 #pragma unroll
-          for (int u = UB0; u < NO; ++u) {
+          for (int u = 0; u < NO; ++u) {
             if (NH == 1 ? u < 2 * kb : u < kb) continue;
             const int t = 16 * at[u] + c16;
             const int ch = (NH == 1 ? u < NT / 2 : u == 0) ? CHC / 2 : CHC;
