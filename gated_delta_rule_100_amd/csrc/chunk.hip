@@ -235,23 +235,6 @@ struct ChunkWork {
     bv = beta[i];
   }
 
-  // Row fragments of every chunk row for the Gram products of the scan
-  // factors; rows past the chunk repeat its last token instead of being
-  // zeroed (their beta is zero, so they leave A alone, and the P rows they
-  // produce belong to outputs that are never stored), so every load is
-  // unconditional.
-  __device__ void rows_frags_clamped(const void* base, bf16x8 (&f)[NT][KB][PI]) const {
-    static_assert(IN == Dt::BF16, "bf16 rows");
-#pragma unroll
-    for (int ti = 0; ti < NT; ++ti) {
-      const int t = 16 * ti + c16 < c ? 16 * ti + c16 : c - 1;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        f[ti][kb][0] = *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(base) + tok_off(t) +
-                                                        32 * kb + 8 * g4);
-    }
-  }
-
   // Gates into LDS (zero past the chunk) and their prefix quantities G, gamma,
   // D, beta gamma.  The padding is zeroed by a multiplication, not a select on
   // the loaded value (which the compiler would turn back into a conditional
@@ -823,20 +806,43 @@ __global__ __launch_bounds__(256, 2) void chunk_out_kernel(
 // (elements 4g..4g+3 and 16+4g..16+4g+3, the order in which D tiles stack,
 // mfma_planes.h) are adjacent, so that the scan reads each fragment with one
 // 16-byte load.
+// Chunk rows of q and k staged in LDS for the factors kernel: dense rows of D
+// bf16 whose 16-byte chunks are permuted by row (physical chunk = logical
+// chunk XOR rows_swz(row)), so that the 16 rows one fragment read touches fall
+// into distinct banks.
+template <int CH>
+__device__ __forceinline__ int rows_swz(int row) { return (row * CH / 16) & (CH - 1); }
+
+// One 16-byte lane of a global-to-LDS copy: the 64 lanes of the wave fill the
+// 1 KiB at `lds` in lane order (the LDS address must be wave-uniform).
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                   (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
+}
+
 template <int D, int C>
 __global__ __launch_bounds__(256, 2) void chunk_factors_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, const int32_t* __restrict__ cu, const int32_t* __restrict__ cidx,
-    ChunkFactors f, int H, int T_total) {
+    ChunkFactors f, int H, int T_total, int max_chunks) {
   using W_ = ChunkWork<D, C, Dt::BF16, false, true>;
   using Cfg = typename W_::Cfg;
-  constexpr int PT = Cfg::PT, NT = Cfg::NT, KB = Cfg::KB, TLP = Cfg::TL_PLANE;
+  constexpr int PT = Cfg::PT, NT = Cfg::NT, KB = Cfg::KB, TLP = Cfg::TL_PLANE, CHD = Cfg::CHD;
   static_assert(PT == 2 && Cfg::Cp == C && C == 64, "factors of the scan: bf16 inputs, C = 64");
-  __shared__ __align__(16) unsigned char smem[Cfg::BYTES];
-  // Chunks are produced last-first: the scan reads them first-first, so the
-  // earliest chunks are the most recently written (and still cache-resident)
-  // when it starts.
-  const int cid = gridDim.x - 1 - blockIdx.x, h = blockIdx.y;
+  // The chunk's k rows then q rows are copied into LDS with whole-row copies
+  // (each 1 KiB copy instruction reads 1024 / (2 D) rows in full) and read
+  // back as MFMA fragments.  They occupy the start of LDS, which the T, A and
+  // P planes reuse once the fragments are in registers.
+  constexpr int RB_BYTES = 2 * C * D * 2;
+  constexpr int NCP = RB_BYTES / 1024, CPW = NCP / 4;
+  static_assert(RB_BYTES <= Cfg::OFF_GATE && NCP % 8 == 0, "row staging");
+  __shared__ __align__(1024) unsigned char smem[Cfg::BYTES];
+  // Heads vary fastest in dispatch order, so the workgroups in flight at once
+  // read whole token rows of q and k (all heads of a chunk) rather than one
+  // head's 256-byte slice of rows H * 256 bytes apart.  Chunks are produced
+  // last-first: the scan reads them first-first, so the earliest chunks are
+  // the most recently written (and still cache-resident) when it starts.
+  const int h = blockIdx.x % H, cid = max_chunks - 1 - static_cast<int>(blockIdx.x / H);
   const ChunkTokens ct = chunk_tokens(cu, cidx, cid, C, T_total);
   if (ct.c <= 0) return;
 
@@ -844,14 +850,39 @@ __global__ __launch_bounds__(256, 2) void chunk_factors_kernel(
   w.init(smem, ct.tok0, ct.c, h, H);
   {
     // the gates first: loads complete in order, so their prefix overlaps the
-    // row loads
+    // row copies
     float gv, bv;
     w.read_gates(g, beta, gv, bv);
     __builtin_amdgcn_sched_barrier(0);
+    // Rows past the chunk repeat its last token (their beta is zero, so they
+    // leave A alone, and the P rows they produce belong to outputs that are
+    // never stored).
+    const int wave = __builtin_amdgcn_readfirstlane(w.wave), lane = w.tid & 63;
+#pragma unroll
+    for (int x = 0; x < CPW; ++x) {
+      const int i = wave + 4 * x;  // copy index: k rows first, then q rows
+      const int p = 64 * (i % (NCP / 2)) + lane, t = p / CHD, pc = p % CHD;
+      const int tt = t < ct.c ? t : ct.c - 1;
+      const uint16_t* src = static_cast<const uint16_t*>(x < CPW / 2 ? k : q) + w.tok_off(tt) +
+                            8 * (pc ^ rows_swz<CHD>(t));
+      dma16(src, smem + 1024 * i);
+    }
+    w.finish_gates(gv, bv);  // LDS-only barriers: the copies stay in flight
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies (vmcnt) and LDS ops
+    lds_barrier();                  // every wave's copies have landed
+    const uint16_t* rows = reinterpret_cast<const uint16_t*>(smem);
     bf16x8 kf[NT][KB][1], qf[NT][KB][1];
-    w.rows_frags_clamped(k, kf);
-    w.rows_frags_clamped(q, qf);
-    w.finish_gates(gv, bv);
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti) {
+      const int t = 16 * ti + w.c16;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int off = t * D + 8 * ((4 * kb + w.g4) ^ rows_swz<CHD>(t));
+        kf[ti][kb][0] = *reinterpret_cast<const bf16x8*>(rows + off);
+        qf[ti][kb][0] = *reinterpret_cast<const bf16x8*>(rows + C * D + off);
+      }
+    }
+    lds_barrier();  // the staged rows are in registers: the planes may overwrite them
     w.gram_t(kf, qf);
   }
   __syncthreads();
@@ -879,8 +910,10 @@ template <int D, int C>
 hipError_t factors_t(const void* q, const void* k, const float* g, const float* beta,
                      const int32_t* cu, const int32_t* cidx, const ChunkFactors& f,
                      int max_chunks, int T_total, int H, hipStream_t stream) {
-  hipLaunchKernelGGL((chunk_factors_kernel<D, C>), dim3(max_chunks, H), dim3(256), 0, stream, q,
-                     k, g, beta, cu, cidx, f, H, T_total);
+  const int64_t groups = static_cast<int64_t>(max_chunks) * H;
+  if (groups > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((chunk_factors_kernel<D, C>), dim3(static_cast<unsigned>(groups)), dim3(256), 0,
+                     stream, q, k, g, beta, cu, cidx, f, H, T_total, max_chunks);
   return hipGetLastError();
 }
 
