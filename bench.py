@@ -10,8 +10,10 @@ The headline `value` is the decode state bandwidth (state bytes read + written
 per step / decode time); the prefill throughput is reported beside it.  The
 other prefill workloads (varlen: 8 sequences, 32768 tokens, 32 heads; long:
 one 131072-token sequence, 4 heads) are timed after the step, outside it, and
-reported as `prefill_varlen` and `prefill_long`, and multi-token decode (8
-draft tokens per sequence on the decode workload's shape) as `decode_mtp`.
+reported as `prefill_varlen` and `prefill_long`, the prefill workload in the
+chunk-parallel form (the caller asks for every chunk's L and M) as
+`prefill_cp`, and multi-token decode (8 draft tokens per sequence on the decode
+workload's shape) as `decode_mtp`.
 
 Decode is measured cold: four state buffers (512 MiB, more than the 256 MB
 Infinity Cache) are used in rotation.  Prefill writes a 1 GiB scrub buffer
@@ -195,7 +197,7 @@ def recorded_traffic(kernel_file, record):
     return rec.get("hbm_bytes_per_launch")
 
 
-def bench_prefill(torch, gdr, steps, warmup, idx=2):
+def bench_prefill(torch, gdr, steps, warmup, idx=2, cp_form=False):
     from gdr_synth import workload
     d = workload(idx)
     di = to_dev(d, torch)
@@ -206,10 +208,16 @@ def bench_prefill(torch, gdr, steps, warmup, idx=2):
                      dtype=torch.uint8, device="cuda")
     scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
     stream = torch.cuda.current_stream()
+    L = M = None
+    if cp_form:  # asking for L and M takes the chunk-parallel form
+        mc = gdr.gdr_max_chunks(T, N, C)
+        L = torch.empty(mc, H, D, D, device="cuda")
+        M = torch.empty(mc, H, D, D, device="cuda")
 
     def launch():
         gdr.gdr_chunk_prefill(di["q"], di["k"], di["v"], di["g"], di["beta"], di["cu"],
-                              di["state0"], sout, o, chunk=C, workspace=ws, stream=stream)
+                              di["state0"], sout, o, chunk=C, L_out=L, M_out=M, workspace=ws,
+                              stream=stream)
 
     for _ in range(warmup):
         launch()
@@ -317,6 +325,14 @@ def main():
             others[key] = {"workload": r["workload"], "value": round(r["tokens"] / t, 1),
                            "unit": "tokens/s", "ms": round(r["ms_mean"], 4),
                            "io_min_frac": round(io_min_bytes(idx) / t / 1e9 / HBM_PEAK_GBS, 4)}
+        r = bench_prefill(torch, gdr, max(3, min(args.steps, 10)), min(args.warmup, 2), 2,
+                          cp_form=True)
+        print(f"[bench] prefill_cp {r}", file=sys.stderr, flush=True)
+        t = r["ms_mean"] / 1e3
+        others["prefill_cp"] = {
+            "workload": r["workload"] + " (chunk-parallel form: L and M requested)",
+            "value": round(r["tokens"] / t, 1), "unit": "tokens/s", "ms": round(r["ms_mean"], 4),
+            "cp_form_frac": round(PRE_CP_BYTES / t / 1e9 / HBM_PEAK_GBS, 4)}
         m = bench_mtp(torch, gdr, args.steps, args.warmup)
         print(f"[bench] decode_mtp {m}", file=sys.stderr, flush=True)
         t = m["ms_mean"] / 1e3

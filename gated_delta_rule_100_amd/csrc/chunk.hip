@@ -170,6 +170,23 @@ struct ChunkWork {
     }
   }
 
+  // Row fragments of K for the Gram products from the planes load() staged in
+  // LDS (the same values rows_frags would load, without a second, scattered
+  // read of K from global memory).  Call after load().
+  __device__ void k_frags_lds(bf16x8 (&f)[NT][KB][PI]) const {
+#pragma unroll
+    for (int ti = 0; ti < NT; ++ti) {
+      const int t = 16 * ti + c16;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int off = t * D + 8 * ((4 * kb + g4) ^ swz_tr(t, Cfg::CHD));
+#pragma unroll
+        for (int p = 0; p < PI; ++p)
+          f[ti][kb][p] = *reinterpret_cast<const bf16x8*>(Kr() + p * Cfg::KR_PS + off);
+      }
+    }
+  }
+
   // K and V rows as planes (row-major, zero for t >= c, 16-byte chunks
   // permuted by swz_tr for the transpose reads), gates and their prefix
   // quantities.  Every global load is issued before the first LDS write; a
@@ -617,9 +634,9 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
   W_ w;
   w.init(smem, ct.tok0, ct.c, h, H);
   {
-    bf16x8 kf[Cfg::NT][Cfg::KB][Cfg::PI];
-    w.rows_frags(k, kf);
     w.load(k, v, g, beta);
+    bf16x8 kf[Cfg::NT][Cfg::KB][Cfg::PI];
+    w.k_frags_lds(kf);
     w.gram_kk(kf);
   }
   __syncthreads();
@@ -680,9 +697,9 @@ __global__ __launch_bounds__(256, 2) void chunk_out_kernel(
   w.init(smem, ct.tok0, ct.c, h, H);
   {
     bf16x8 kf[NT][KB][PI], qf[NT][KB][PI];
-    w.rows_frags(k, kf);
     w.rows_frags(q, qf);
     w.load(k, v, g, beta);
+    w.k_frags_lds(kf);
     w.gram_kk(kf);
     w.gram_qk(qf, kf);
   }
