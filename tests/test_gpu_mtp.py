@@ -86,7 +86,8 @@ def test_mtp_T1_equals_decode_step_bitwise():
 
 
 # Without per-token states, 5 <= T <= 8 tokens take the chunked kernel (the T
-# tokens as one chunk of the chunked form, on fp32 matrix products).
+# tokens as one chunk of the chunked form, on fp32 matrix products); the last
+# two cases take the token-by-token kernel without per-token states.
 CHUNKED_CASES = {
     "N3-T6-H2-d128-bf16": (3, 6, 2, 128, "bf16", "std"),
     "N2-T8-H3-d64-f32": (2, 8, 3, 64, "f32", "std"),
@@ -94,6 +95,9 @@ CHUNKED_CASES = {
     "N3-T7-H2-d128-bf16-slow": (3, 7, 2, 128, "bf16", "slow"),
     "N2-T5-H2-d64-bf16-steep": (2, 5, 2, 64, "bf16", "steep"),
     "N2-T8-H2-d128-f32-unit": (2, 8, 2, 128, "f32", "unit"),
+    # outside 5..8 the token-by-token kernel runs without per-token states
+    "N3-T3-H2-d128-bf16-token": (3, 3, 2, 128, "bf16", "std"),
+    "N2-T12-H2-d64-bf16-token": (2, 12, 2, 64, "bf16", "slow"),
 }
 
 
