@@ -295,7 +295,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards with no exchange across sequences/heads; see DESIGN.md)",
+              "(the path shards by sequence and head with no exchange)",
               file=sys.stderr)
         sys.exit(2)
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
