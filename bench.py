@@ -294,7 +294,7 @@ def _cpu_model():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by sequence and head with no exchange)",
               file=sys.stderr)
         sys.exit(2)
