@@ -42,6 +42,8 @@
 // is applied on the global side of the copies (each lane of a global-to-LDS
 // load names its own source address), so every copy instruction fills a dense
 // 1 KiB block.
+#include <type_traits>
+
 #include "launch.h"
 #include "mfma_planes.h"
 
@@ -375,8 +377,12 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     bare_barrier();  // B0: chunk c0 is in LDS
 
-    for (int s = c0; s < c1; ++s) {
-      const unsigned char* buf = smem + ((s - c0) & 1) * Cfg::BUF;
+    // One chunk step; the chunk buffer is a compile-time constant (chunk s of
+    // the sequence sits in buffer (s - c0) & 1), so that each of the two
+    // copies of the step below reads LDS at loop-invariant addresses.
+    auto step = [&](int s, auto bsel) {
+      using B = decltype(bsel);
+      const unsigned char* buf = smem + B::value * Cfg::BUF;
       const uint16_t* Kl = reinterpret_cast<const uint16_t*>(buf + Cfg::OFF_K);
       const uint16_t* Ql = reinterpret_cast<const uint16_t*>(buf + Cfg::OFF_Q);
       const uint16_t* Tl = reinterpret_cast<const uint16_t*>(buf + Cfg::OFF_T);
@@ -615,6 +621,10 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
           *reinterpret_cast<floatx4*>(fx + 16 * (jt0 + jl) + 4 * g4) = S[jl];
       }
       bare_barrier();  // chunk s is done with its buffer; chunk s + 1 is in LDS
+    };
+    for (int s = c0; s < c1; s += 2) {
+      step(s, std::integral_constant<int, 0>{});
+      if (s + 1 < c1) step(s + 1, std::integral_constant<int, 1>{});
     }
   }
 
