@@ -61,6 +61,7 @@ def _load():
     lib.gdr_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P]
     lib.gdr_decode_mtp.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
     lib.gdr_decode_step.restype = I
+    lib.gdr_decode_mtp.restype = I
     lib.gdr_max_chunks.argtypes = [I, I, I]
     lib.gdr_max_chunks.restype = I
     lib.gdr_chunk_layout.argtypes = [P, I, I, P, P, I, P]
