@@ -1,0 +1,98 @@
+"""Batches whose state tensor holds more than 2^31 elements (more than 131072
+(sequence, head) pairs at d = 128, 9.1 GB of fp32 state), so that every offset
+past the first 131072 pairs needs 64-bit arithmetic.  Decode, chunked
+multi-token decode and prefill run on such a batch; sampled pairs on both
+sides of the 2^31-element boundary are checked against the oracle, run on
+that pair alone (bf16 inputs: max|gpu - ref| / max|ref| <= 1e-3).
+
+The state is drawn on the device from a seeded generator (N(0, 0.02)); the
+host keeps copies of the sampled pairs only."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gdr_synth import generate
+from gpu_util import BF16_TOL, dev_inputs, host64, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+N, H, D = 4352, 32, 128          # 139264 pairs: 2.28e9 state elements
+PAIRS = [(0, 0), (2048, 17), (4095, 31), (4096, 1), (4200, 9), (N - 1, H - 1)]
+
+
+def big_state(seed):
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    s = torch.randn(N, H, D, D, generator=gen, device="cuda", dtype=torch.float32)
+    return s.mul_(0.02)
+
+
+def pair_problem(d, n, h, tokens, s0):
+    """The inputs of one (sequence, head) pair as a one-sequence, one-head batch."""
+    a, b = int(d["cu_seqlens"][n]), int(d["cu_seqlens"][n + 1])
+    assert b - a == tokens
+    sub = {key: np.ascontiguousarray(d[key][a:b, h:h + 1]) for key in ("q", "k", "v", "g", "beta")}
+    return oracle.recurrent(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"],
+                            np.array([0, tokens]), s0[None, None])
+
+
+def check(d, tokens, s0_host, o, s_new, label):
+    for (n, h) in PAIRS:
+        o_ref, s_ref, _ = pair_problem(d, n, h, tokens, s0_host[(n, h)])
+        a = int(d["cu_seqlens"][n])
+        e_o = rel_err(host64(o[a:a + tokens, h]), o_ref[:, 0])
+        e_s = rel_err(host64(s_new[n, h]), s_ref[0, 0])
+        say(f"  {label} pair ({n},{h}) offset {(n * H + h) * D * D:.3e}: o {e_o:.2e} state {e_s:.2e}")
+        assert e_o <= BF16_TOL and e_s <= BF16_TOL, (label, n, h, e_o, e_s)
+
+
+def test_decode_state_past_2_31_elements():
+    import gated_delta_rule_100_amd as gdr
+    say(f"decode N={N} H={H} d={D}: state of {N * H * D * D:.3e} elements")
+    d = generate([1] * N, H, D, D, dtype="bf16", state0=False, seed=700)
+    di = dev_inputs(d)
+    state = big_state(701)
+    s0 = {p: host64(state[p[0], p[1]]) for p in PAIRS}
+    o = torch.empty(N, H, D, dtype=torch.float32, device="cuda")
+    gdr.gdr_decode_step(di["q"], di["k"], di["v"], di["g"], di["beta"], state, o)
+    torch.cuda.synchronize()
+    check(d, 1, s0, o, state, "decode")
+    del state
+    torch.cuda.empty_cache()
+
+
+def test_mtp_chunked_state_past_2_31_elements():
+    import gated_delta_rule_100_amd as gdr
+    T = 5
+    say(f"multi-token decode (chunked) N={N} T={T} H={H} d={D}, in place")
+    d = generate([T] * N, H, D, D, dtype="bf16", state0=False, seed=710)
+    di = dev_inputs(d)
+    x = {key: di[key].view(N, T, H, -1) for key in ("q", "k", "v")}
+    state = big_state(711)
+    s0 = {p: host64(state[p[0], p[1]]) for p in PAIRS}
+    o = torch.empty(N, T, H, D, dtype=torch.float32, device="cuda")
+    gdr.gdr_decode_mtp(x["q"], x["k"], x["v"], di["g"].view(N, T, H), di["beta"].view(N, T, H),
+                       state, state, o, None)
+    torch.cuda.synchronize()
+    check(d, T, s0, o.view(N * T, H, D), state, "mtp")
+    del state
+    torch.cuda.empty_cache()
+
+
+def test_prefill_state_past_2_31_elements():
+    import gated_delta_rule_100_amd as gdr
+    T = 2
+    say(f"prefill N={N} sequences of {T} tokens, H={H} d={D}: states of {N * H * D * D:.3e} elements")
+    d = generate([T] * N, H, D, D, dtype="bf16", state0=False, seed=720)
+    di = dev_inputs(d)
+    state_in = big_state(721)
+    s0 = {p: host64(state_in[p[0], p[1]]) for p in PAIRS}
+    state_out = torch.empty_like(state_in)
+    o = torch.empty(N * T, H, D, dtype=torch.float32, device="cuda")
+    gdr.gdr_chunk_prefill(di["q"], di["k"], di["v"], di["g"], di["beta"], di["cu"], state_in,
+                          state_out, o, chunk=64)
+    torch.cuda.synchronize()
+    check(d, T, s0, o, state_out, "prefill")
+    del state_in, state_out
+    torch.cuda.empty_cache()
