@@ -1,12 +1,13 @@
-"""Batches whose state tensor holds more than 2^31 elements (more than 131072
-(sequence, head) pairs at d = 128, 9.1 GB of fp32 state), so that every offset
-past the first 131072 pairs needs 64-bit arithmetic.  Decode, chunked
-multi-token decode and prefill run on such a batch; sampled pairs on both
-sides of the 2^31-element boundary are checked against the oracle, run on
-that pair alone (bf16 inputs: max|gpu - ref| / max|ref| <= 1e-3).
-
-The state is drawn on the device from a seeded generator (N(0, 0.02)); the
-host keeps copies of the sampled pairs only."""
+"""Batches with tensors of more than 2^31 elements, so that offsets past the
+boundary need 64-bit arithmetic:
+  - a state of more than 131072 (sequence, head) pairs at d = 128 (9.1 GB of
+    fp32 state) under decode, chunked multi-token decode and prefill;
+  - a prefill whose q, k, v and o hold more than 2^31 elements (token rows past
+    524288 at 32 heads).
+Sampled pairs on both sides of the boundary are checked against the oracle,
+run on that pair alone (bf16 inputs: max|gpu - ref| / max|ref| <= 1e-3).
+The large tensors are drawn on the device from seeded generators; the host
+keeps copies of the sampled pairs only."""
 import numpy as np
 import pytest
 import torch
@@ -95,4 +96,49 @@ def test_prefill_state_past_2_31_elements():
     torch.cuda.synchronize()
     check(d, T, s0, o, state_out, "prefill")
     del state_in, state_out
+    torch.cuda.empty_cache()
+
+
+def test_prefill_tokens_past_2_31_elements():
+    # 560 sequences of 1000 tokens, 32 heads: q, k, v and o hold 2.29e9 elements,
+    # so token rows past 524288 sit beyond 2^31 elements.  Inputs are drawn on
+    # the device from a seeded generator (q, k L2-normalised per token, v
+    # N(0,1), g = -softplus(N(0,1)), beta = sigmoid(N(0,1)), S0 = 0); the host
+    # copies the sampled pairs' tokens only.
+    import gated_delta_rule_100_amd as gdr
+    Nn, L, Hh = 560, 1000, 32
+    T = Nn * L
+    say(f"prefill {Nn} sequences of {L} tokens, H={Hh} d={D}: q/k/v/o of {T * Hh * D:.3e} elements")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(730)
+
+    def unit_rows():
+        x = torch.randn(T, Hh, D, generator=gen, device="cuda")
+        x /= x.norm(dim=-1, keepdim=True)
+        return x.to(torch.bfloat16)
+
+    q, k = unit_rows(), unit_rows()
+    v = torch.randn(T, Hh, D, generator=gen, device="cuda").to(torch.bfloat16)
+    g = -torch.nn.functional.softplus(torch.randn(T, Hh, generator=gen, device="cuda"))
+    beta = torch.sigmoid(torch.randn(T, Hh, generator=gen, device="cuda"))
+    cu = torch.arange(0, T + 1, L, dtype=torch.int32, device="cuda")
+    state_out = torch.empty(Nn, Hh, D, D, device="cuda")
+    o = torch.empty(T, Hh, D, dtype=torch.float32, device="cuda")
+    gdr.gdr_chunk_prefill(q, k, v, g, beta, cu, None, state_out, o, chunk=64)
+    torch.cuda.synchronize()
+
+    def bits(t):
+        return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    for n, h in [(0, 0), (300, 5), (524, 31), (540, 16), (Nn - 1, Hh - 1)]:
+        a, b = n * L, (n + 1) * L
+        sl = (slice(a, b), slice(h, h + 1))
+        o_ref, s_ref, _ = oracle.recurrent(
+            bits(q[sl]), bits(k[sl]), bits(v[sl]), g[sl].contiguous().cpu().numpy(),
+            beta[sl].contiguous().cpu().numpy(), np.array([0, L]))
+        e_o = rel_err(host64(o[a:b, h]), o_ref[:, 0])
+        e_s = rel_err(host64(state_out[n, h]), s_ref[0, 0])
+        say(f"  pair ({n},{h}) last token offset {((b - 1) * Hh + h) * D:.3e}: o {e_o:.2e} state {e_s:.2e}")
+        assert e_o <= BF16_TOL and e_s <= BF16_TOL, (n, h, e_o, e_s)
+    del q, k, v, o, state_out
     torch.cuda.empty_cache()
