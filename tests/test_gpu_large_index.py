@@ -142,3 +142,62 @@ def test_prefill_tokens_past_2_31_elements():
         assert e_o <= BF16_TOL and e_s <= BF16_TOL, (n, h, e_o, e_s)
     del q, k, v, o, state_out
     torch.cuda.empty_cache()
+
+
+def test_chunk_parallel_states_past_2_31_elements():
+    # The chunk-parallel schedule (L and M requested) on 4 sequences of 67200
+    # tokens at 32 heads: L, M and the fixed states hold 4204 chunk slots x 32
+    # heads x 128 x 128 = 2.2e9 elements each, so the chunks past slot 4096
+    # sit beyond 2^31.  Inputs drawn on the device from a seeded generator
+    # (the recipe of the token test above, S0 = 0).  The last sequence is
+    # checked against the oracle run on two of its heads: outputs, final
+    # state and the fixed state of its last chunks (slots past 4096).
+    import gated_delta_rule_100_amd as gdr
+    Nn, L, Hh, C = 4, 67200, 32, 64
+    T = Nn * L
+    mc = gdr.gdr_max_chunks(T, Nn, C)
+    say(f"chunk-parallel prefill {Nn} x {L} tokens, H={Hh}: L/M/fixed of {mc * Hh * D * D:.3e} elements")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(740)
+
+    def unit_rows():
+        x = torch.randn(T, Hh, D, generator=gen, device="cuda")
+        x /= x.norm(dim=-1, keepdim=True)
+        return x.to(torch.bfloat16)
+
+    q, k = unit_rows(), unit_rows()
+    v = torch.randn(T, Hh, D, generator=gen, device="cuda").to(torch.bfloat16)
+    g = -torch.nn.functional.softplus(torch.randn(T, Hh, generator=gen, device="cuda"))
+    beta = torch.sigmoid(torch.randn(T, Hh, generator=gen, device="cuda"))
+    cu = torch.arange(0, T + 1, L, dtype=torch.int32, device="cuda")
+    state_out = torch.empty(Nn, Hh, D, D, device="cuda")
+    o = torch.empty(T, Hh, D, dtype=torch.float32, device="cuda")
+    Lo = torch.empty(mc, Hh, D, D, device="cuda")
+    Mo = torch.empty(mc, Hh, D, D, device="cuda")
+    F = torch.empty(mc, Hh, D, D, device="cuda")
+    gdr.gdr_chunk_prefill(q, k, v, g, beta, cu, None, state_out, o, chunk=C, L_out=Lo, M_out=Mo,
+                          fixed_out=F)
+    torch.cuda.synchronize()
+    del Lo, Mo
+
+    def bits(t):
+        return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    n = Nn - 1
+    a, b = n * L, (n + 1) * L
+    c0 = n * (L // C)                     # the sequence's first chunk slot
+    nch = L // C
+    for h in (0, Hh - 1):
+        sl = (slice(a, b), slice(h, h + 1))
+        o_ref, s_ref, cs_ref = oracle.recurrent(
+            bits(q[sl]), bits(k[sl]), bits(v[sl]), g[sl].contiguous().cpu().numpy(),
+            beta[sl].contiguous().cpu().numpy(), np.array([0, L]), chunk=C)
+        e_o = rel_err(host64(o[a:b, h]), o_ref[:, 0])
+        e_s = rel_err(host64(state_out[n, h]), s_ref[0, 0])
+        last = slice(c0 + nch - 8, c0 + nch)
+        e_f = rel_err(host64(F[last, h]), cs_ref[nch - 8:nch, 0])
+        say(f"  pair ({n},{h}) last slot offset {((c0 + nch - 1) * Hh + h) * D * D:.3e}: "
+            f"o {e_o:.2e} state {e_s:.2e} fixed {e_f:.2e}")
+        assert max(e_o, e_s, e_f) <= BF16_TOL, (h, e_o, e_s, e_f)
+    del q, k, v, o, state_out, F
+    torch.cuda.empty_cache()
