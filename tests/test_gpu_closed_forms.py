@@ -6,7 +6,9 @@ from the inputs (not by the oracle):
     erase term S_{t-1} k_t vanishes, so with G the running sum of g
         S_T = sum_s beta_s e^{G_T - G_s} v_s k_s^T,
         o_t = sum_{s<=t} beta_s e^{G_t - G_s} (k_s . q_t) v_s.
-Keys for the second case are signed one-hot rows under a random permutation
+  - beta = 0 with any gates (pure decay): S_t = e^{G_t} S_0 and
+    o_t = e^{G_t} S_0 q_t.
+Keys for the orthogonal case are signed one-hot rows under a random permutation
 per (sequence, head): orthonormal and exact in bf16.  Every entry point runs
 both cases: decode (token by token), multi-token decode (chunked and token by
 token), and prefill under both schedules.  Outputs are fp32;
@@ -78,6 +80,24 @@ def identity_outputs(d):
     return o
 
 
+def decay_closed_form(d):
+    """beta = 0: o_t = e^{G_t} S_0 q_t and S_T = e^{G_T} S_0 per sequence."""
+    q = f64(d["q"])
+    g = d["g"].astype(np.float64)
+    cu = d["cu_seqlens"]
+    o = np.zeros((d["T"], d["H"], d["dv"]))
+    S = d["state0"].astype(np.float64).copy()
+    for n in range(d["N"]):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if b == a:
+            continue
+        G = np.cumsum(g[a:b], axis=0)                       # [t, h]
+        s0 = d["state0"][n].astype(np.float64)
+        o[a:b] = np.exp(G)[:, :, None] * np.einsum("hij,thj->thi", s0, q[a:b])
+        S[n] = np.exp(G[-1])[:, None, None] * s0
+    return o, S
+
+
 # ---- prefill (both schedules) ----
 
 # name: (sequence lengths, H, d, dtype, chunk); fp32 inputs take chunk 16.  The
@@ -133,6 +153,20 @@ def test_prefill_orthogonal_keys(name, keep_lm):
     onehot_keys(d, 811)
     o, sout = run_prefill(d, keep_lm, chunk)
     o_ref, s_ref = orthogonal_closed_form(d)
+    e_o, e_s = rel_err(host64(o), o_ref), rel_err(host64(sout), s_ref)
+    say(f"  o {e_o:.2e} state {e_s:.2e}")
+    assert e_o <= tol_for(d) and e_s <= tol_for(d)
+
+
+@pytest.mark.parametrize("keep_lm", [False, True], ids=["scan", "chunk-parallel"])
+@pytest.mark.parametrize("name", list(PREFILL))
+def test_prefill_pure_decay(name, keep_lm):
+    lens, H, dd, dtype, chunk = PREFILL[name]
+    say(f"prefill pure decay {name} {'chunk-parallel' if keep_lm else 'scan'}")
+    d = generate(lens, H, dd, dd, dtype=dtype, state0=True, seed=840, gate="slow")
+    d["beta"][:] = 0.0
+    o, sout = run_prefill(d, keep_lm, chunk)
+    o_ref, s_ref = decay_closed_form(d)
     e_o, e_s = rel_err(host64(o), o_ref), rel_err(host64(sout), s_ref)
     say(f"  o {e_o:.2e} state {e_s:.2e}")
     assert e_o <= tol_for(d) and e_s <= tol_for(d)
@@ -210,6 +244,19 @@ def test_decode_orthogonal_keys(name):
     onehot_keys(d, 831)
     o, state = run_decode_case(d, L, path)
     o_ref, s_ref = orthogonal_closed_form(d)
+    e_o, e_s = rel_err(host64(o), o_ref), rel_err(host64(state), s_ref)
+    say(f"  o {e_o:.2e} state {e_s:.2e}")
+    assert e_o <= tol_for(d) and e_s <= tol_for(d)
+
+
+@pytest.mark.parametrize("name", list(DECODE))
+def test_decode_pure_decay(name):
+    N, L, H, dd, dtype, path = DECODE[name]
+    say(f"decode pure decay {name}")
+    d = generate([L] * N, H, dd, dd, dtype=dtype, state0=True, seed=850)
+    d["beta"][:] = 0.0
+    o, state = run_decode_case(d, L, path)
+    o_ref, s_ref = decay_closed_form(d)
     e_o, e_s = rel_err(host64(o), o_ref), rel_err(host64(state), s_ref)
     say(f"  o {e_o:.2e} state {e_s:.2e}")
     assert e_o <= tol_for(d) and e_s <= tol_for(d)
