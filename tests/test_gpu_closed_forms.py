@@ -11,7 +11,8 @@ from the inputs (not by the oracle):
 Keys for the orthogonal case are signed one-hot rows under a random permutation
 per (sequence, head): orthonormal and exact in bf16.  Every entry point runs
 both cases: decode (token by token), multi-token decode (chunked and token by
-token), and prefill under both schedules.  Outputs are fp32;
+token), and prefill under both schedules; the fixup scan on its own is checked
+with scaled-identity transfer matrices.  Outputs are fp32;
 max|gpu - ref| / max|ref| <= 1e-3 (bf16 inputs) or 1e-5 (fp32 inputs)."""
 import numpy as np
 import pytest
@@ -260,3 +261,40 @@ def test_decode_pure_decay(name):
     e_o, e_s = rel_err(host64(o), o_ref), rel_err(host64(state), s_ref)
     say(f"  o {e_o:.2e} state {e_s:.2e}")
     assert e_o <= tol_for(d) and e_s <= tol_for(d)
+
+
+# ---- the fixup scan on its own ----
+
+@pytest.mark.parametrize("with_state", [True, False])
+@pytest.mark.parametrize("D,H,chunks", [(128, 3, [5, 0, 40, 1]), (64, 2, [300, 7]),
+                                        (128, 1, [600])])  # one long chain
+def test_fixup_scaled_identity_transfer(with_state, D, H, chunks):
+    """gdr_state_fixup with M_c = a_c I: fixed[c] = a_c fixed[c-1] + L_c, a
+    running sum (fixed[first] = L when there is no initial state)."""
+    import gated_delta_rule_100_amd as gdr
+    say(f"fixup scaled identity D={D} H={H} chunks={chunks} with_state={with_state}")
+    rng = np.random.Generator(np.random.PCG64(860 + D))
+    offs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    nch = int(offs[-1])
+    L = rng.standard_normal((nch, H, D, D)).astype(np.float32)
+    a = np.exp(-rng.random((nch, H))).astype(np.float32)          # in (1/e, 1]
+    M = np.zeros((nch, H, D, D), dtype=np.float32)
+    M[:, :, np.arange(D), np.arange(D)] = a[:, :, None]             # symmetric: layout-free
+    s0 = (0.5 * rng.standard_normal((len(chunks), H, D, D))).astype(np.float32)
+    fixed = torch.full((nch, H, D, D), float("nan"), device="cuda")
+    gdr.gdr_state_fixup(torch.from_numpy(L).cuda(), torch.from_numpy(M).cuda(),
+                        torch.from_numpy(s0).cuda() if with_state else None,
+                        torch.from_numpy(offs).cuda(), fixed)
+    torch.cuda.synchronize()
+    ref = np.zeros((nch, H, D, D))
+    for n in range(len(chunks)):
+        prev = s0[n].astype(np.float64) if with_state else None
+        for c in range(int(offs[n]), int(offs[n + 1])):
+            if prev is None:
+                ref[c] = L[c]
+            else:
+                ref[c] = a[c].astype(np.float64)[:, None, None] * prev + L[c]
+            prev = ref[c]
+    e = rel_err(host64(fixed), ref)
+    say(f"  fixed {e:.2e}")
+    assert e <= 1e-5
