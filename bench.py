@@ -19,7 +19,8 @@ Decode is measured cold: four state buffers (512 MiB, more than the 256 MB
 Infinity Cache) are used in rotation.  Prefill writes a 1 GiB scrub buffer
 before every timed launch (outside the timed events).  Warm figures (one
 decode state buffer, prefill without the scrub) are reported beside them as
-`warm`, for context.  Inputs are resident in HBM before timing starts.  Kernel times come from HIP events recorded on the
+`warm`, for context (not with --no-other-prefill).  Inputs are resident in HBM
+before timing starts.  Kernel times come from HIP events recorded on the
 stream the kernels are launched on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -348,11 +349,22 @@ def main():
             "value": round(DEC_STATE_BYTES / t / 1e9, 2), "unit": "state GB/s",
             "us": round(m["ms_mean"] * 1e3, 2),
             "tokens_per_s": round(DEC_N * m["T"] / t, 1)}
-    # warm figures for context: decode on one state buffer, prefill without
-    # the scrub
-    dec_w = bench_decode(torch, gdr, args.steps, args.warmup, nbuf=1)
-    pre_w = bench_prefill(torch, gdr, args.steps, args.warmup, cold=False)
-    print(f"[bench] warm decode {dec_w} prefill {pre_w}", file=sys.stderr, flush=True)
+    # warm figures for context (with the other workloads): decode on one state
+    # buffer, prefill without the scrub
+    warm = None
+    if not args.no_other_prefill:
+        dec_w = bench_decode(torch, gdr, args.steps, args.warmup, nbuf=1)
+        pre_w = bench_prefill(torch, gdr, args.steps, args.warmup, cold=False)
+        print(f"[bench] warm decode {dec_w} prefill {pre_w}", file=sys.stderr, flush=True)
+        warm = {
+            "note": "context, not the headline: decode reuses one 128 MiB state buffer (small "
+                    "enough for the 256 MB Infinity Cache) and prefill runs back to back "
+                    "without the scrub",
+            "decode_ms": round(dec_w["ms_mean"], 5),
+            "decode_state_gbs": round(DEC_STATE_BYTES / (dec_w["ms_mean"] / 1e3) / 1e9, 2),
+            "prefill_ms": round(pre_w["ms_mean"], 5),
+            "prefill_tokens_per_s": round(PRE_TOKENS / (pre_w["ms_mean"] / 1e3), 1),
+        }
     copy_gbs = copy_bandwidth(torch)
     print(f"[bench] device copy {copy_gbs:.1f} GB/s", file=sys.stderr, flush=True)
     cpu = None
@@ -400,15 +412,8 @@ def main():
         },
         "cpu_baseline": cpu,
     }
-    out["warm"] = {
-        "note": "context, not the headline: decode reuses one 128 MiB state buffer (small "
-                "enough for the 256 MB Infinity Cache) and prefill runs back to back without "
-                "the scrub",
-        "decode_ms": round(dec_w["ms_mean"], 5),
-        "decode_state_gbs": round(DEC_STATE_BYTES / (dec_w["ms_mean"] / 1e3) / 1e9, 2),
-        "prefill_ms": round(pre_w["ms_mean"], 5),
-        "prefill_tokens_per_s": round(PRE_TOKENS / (pre_w["ms_mean"] / 1e3), 1),
-    }
+    if warm is not None:
+        out["warm"] = warm
     out.update(others)
     print(json.dumps(out))
 
