@@ -33,3 +33,11 @@ def test_other_prefill_workloads():
     assert bench.io_min_bytes(3) == 32768 * 32 * TOKEN_HEAD + 2 * 8 * 32 * STATE == 1_115_684_864
     # long: 131072 tokens, 4 heads, one sequence without an initial state
     assert bench.io_min_bytes(4) == 131072 * 4 * TOKEN_HEAD + 4 * STATE == 541_327_360
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
