@@ -128,3 +128,33 @@ def test_binding_refuses_cpu_tensors(lib):
     with pytest.raises(g.GdrError):
         g.gdr_decode_step(q, q, q, torch.zeros(2, 2), torch.zeros(2, 2),
                           torch.zeros(2, 2, 64, 64), torch.zeros(2, 2, 64))
+
+
+def test_last_error_is_per_thread(lib):
+    # Two threads fail with different messages at the same time; each reads back
+    # its own detail (the header documents the detail as thread-local).
+    import threading
+    fake = 0x10000  # never dereferenced: validation fails first
+    args = [_p(fake)] * 7
+    barrier = threading.Barrier(2)
+    seen = {}
+
+    def fail_null():
+        assert lib.gdr_decode_step(*([None] + args[1:]), 2, 2, 128, 128, 0, 0, None) == 1
+        barrier.wait()
+        barrier.wait()
+        seen["null"] = lib.gdr_last_error().decode()
+
+    def fail_shape():
+        barrier.wait()
+        assert lib.gdr_decode_step(*args, 2, 2, 96, 96, 0, 0, None) == 2
+        barrier.wait()
+        seen["shape"] = lib.gdr_last_error().decode()
+
+    threads = [threading.Thread(target=fail_null), threading.Thread(target=fail_shape)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert "NULL" in seen["null"] and "NULL" not in seen["shape"], seen
+    assert seen["null"] != seen["shape"]
