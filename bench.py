@@ -211,7 +211,7 @@ def bench_prefill(torch, gdr, steps, warmup, idx=2, cp_form=False, cold=True):
     T, H, D, N, C = d["T"], d["H"], d["dk"], d["N"], d["chunk"]
     o = torch.empty(T, H, D, dtype=torch.bfloat16, device="cuda")
     sout = torch.empty(N, H, D, D, device="cuda")
-    ws = torch.empty(gdr.gdr_chunk_prefill_workspace_bytes(T, N, H, D, D, C),
+    ws = torch.empty(gdr.gdr_chunk_prefill_workspace_bytes(T, N, H, D, D, C, gdr.GDR_BF16),
                      dtype=torch.uint8, device="cuda")
     scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if cold else None  # 1 GiB
     stream = torch.cuda.current_stream()

@@ -66,7 +66,7 @@ def _load():
     lib.gdr_max_chunks.restype = I
     lib.gdr_chunk_layout.argtypes = [P, I, I, P, P, I, P]
     lib.gdr_chunk_layout.restype = I
-    lib.gdr_chunk_prefill_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.gdr_chunk_prefill_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.gdr_chunk_prefill_workspace_bytes.restype = S
     lib.gdr_chunk_prefill.argtypes = [P, P, P, P, P, P, I, P, P, P, P, P, P,
                                       I, I, I, I, I, I, I, P, S, P]
@@ -114,6 +114,15 @@ def _code(dt: torch.dtype) -> int:
     if dt == torch.float32:
         return GDR_FP32
     raise GdrError(f"unsupported dtype {dt}")
+
+
+def _stream_obj(stream):
+    """The launch stream as a torch stream (a raw hipStream_t handle is wrapped)."""
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
 
 
 def _stream(stream):
@@ -176,8 +185,11 @@ def gdr_max_chunks(T_total: int, N: int, chunk: int) -> int:
     return int(_load().gdr_max_chunks(T_total, N, chunk))
 
 
-def gdr_chunk_prefill_workspace_bytes(T_total, N, H, dk, dv, chunk) -> int:
-    return int(_load().gdr_chunk_prefill_workspace_bytes(T_total, N, H, dk, dv, chunk))
+def gdr_chunk_prefill_workspace_bytes(T_total, N, H, dk, dv, chunk, in_dtype=GDR_BF16) -> int:
+    """in_dtype: GDR_BF16 / GDR_FP32 or the torch dtype of q, k, v."""
+    if isinstance(in_dtype, torch.dtype):
+        in_dtype = _code(in_dtype)
+    return int(_load().gdr_chunk_prefill_workspace_bytes(T_total, N, H, dk, dv, chunk, in_dtype))
 
 
 def gdr_chunk_layout(cu_seqlens, chunk, chunk_offsets, chunk_indices, stream=None) -> None:
@@ -193,34 +205,26 @@ def gdr_chunk_layout(cu_seqlens, chunk, chunk_offsets, chunk_indices, stream=Non
     _check(st, "gdr_chunk_layout")
 
 
-def gdr_chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in, state_out, o, *, chunk=64,
-                      L_out=None, M_out=None, fixed_out=None, workspace=None,
-                      stream=None) -> None:
-    """Chunked prefill over packed sequences.  q, k [T, H, dk], v [T, H, dv];
-    g, beta [T, H] fp32; cu_seqlens [N+1] int32 (device); state_in
-    [N, H, dv, dk] fp32 or None; state_out [N, H, dv, dk] fp32; o [T, H, dv];
-    optional L_out / fixed_out [max_chunks, H, dv, dk], M_out [max_chunks, H,
-    dk, dk] with max_chunks = gdr_max_chunks(T, N, chunk).  workspace: a
-    uint8 device tensor of gdr_chunk_prefill_workspace_bytes(...) bytes, or
-    None to allocate one here."""
+def _prefill_args(q, k, v, g, beta, cu_seqlens, state_in, state_out, o, chunk, L_out, M_out,
+                  fixed_out, who):
+    """Checks the shapes and dtypes of a prefill call; returns the pointer and
+    size arguments shared by gdr_chunk_prefill and gdr_chunk_prefill_noalloc
+    (everything up to out_dtype) and (T, N, H, dk, dv)."""
     T, H, dk = q.shape
     dv = v.shape[2]
     N = cu_seqlens.shape[0] - 1
     if k.shape != q.shape or v.shape[:2] != (T, H) or g.shape != (T, H) or beta.shape != (T, H) \
             or state_out.shape != (N, H, dv, dk) or o.shape != (T, H, dv) \
             or (state_in is not None and state_in.shape != (N, H, dv, dk)):
-        raise GdrError("gdr_chunk_prefill: inconsistent shapes")
+        raise GdrError(f"{who}: inconsistent shapes")
     if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise GdrError("gdr_chunk_prefill: q, k, v must share a dtype")
+        raise GdrError(f"{who}: q, k, v must share a dtype")
     mc = gdr_max_chunks(T, N, chunk)
     for name, t, shape in (("L_out", L_out, (mc, H, dv, dk)), ("M_out", M_out, (mc, H, dk, dk)),
                            ("fixed_out", fixed_out, (mc, H, dv, dk))):
         if t is not None and tuple(t.shape) != shape:
-            raise GdrError(f"gdr_chunk_prefill: {name} must have shape {shape}")
-    need = gdr_chunk_prefill_workspace_bytes(T, N, H, dk, dv, chunk)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    st = _load().gdr_chunk_prefill(
+            raise GdrError(f"{who}: {name} must have shape {shape}")
+    args = [
         _dev_ptr(q, "q", _IO), _dev_ptr(k, "k", _IO), _dev_ptr(v, "v", _IO),
         _dev_ptr(g, "g", _F32), _dev_ptr(beta, "beta", _F32),
         _dev_ptr(cu_seqlens, "cu_seqlens", _I32), N,
@@ -228,15 +232,38 @@ def gdr_chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in, state_out, o, *, c
         _dev_ptr(state_out, "state_out", _F32), _dev_ptr(o, "o", _IO),
         _dev_ptr(L_out, "L_out", _F32, optional=True), _dev_ptr(M_out, "M_out", _F32, optional=True),
         _dev_ptr(fixed_out, "fixed_out", _F32, optional=True),
-        T, H, dk, dv, chunk, _code(q.dtype), _code(o.dtype),
-        _dev_ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream))
+        T, H, dk, dv, chunk, _code(q.dtype), _code(o.dtype)]
+    return args, (T, N, H, dk, dv)
+
+
+def gdr_chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in, state_out, o, *, chunk=64,
+                      L_out=None, M_out=None, fixed_out=None, workspace=None,
+                      stream=None) -> None:
+    """Chunked prefill over packed sequences.  q, k [T, H, dk], v [T, H, dv];
+    g, beta [T, H] fp32; cu_seqlens [N+1] int32 (device); state_in
+    [N, H, dv, dk] fp32 or None; state_out [N, H, dv, dk] fp32; o [T, H, dv];
+    optional L_out / fixed_out [max_chunks, H, dv, dk], M_out [max_chunks, H,
+    dk, dk] with max_chunks = gdr_max_chunks(T, N, chunk); M_out[c, h] is M_c
+    with S_end = S_start @ M_c + L_c.  workspace: a uint8 device tensor of
+    gdr_chunk_prefill_workspace_bytes(...) bytes, or None to allocate one here
+    (on the launch stream, so that the caching allocator does not hand its
+    memory to work on another stream while the kernels still use it)."""
+    args, (T, N, H, dk, dv) = _prefill_args(q, k, v, g, beta, cu_seqlens, state_in, state_out, o,
+                                            chunk, L_out, M_out, fixed_out, "gdr_chunk_prefill")
+    if workspace is None:
+        need = gdr_chunk_prefill_workspace_bytes(T, N, H, dk, dv, chunk, q.dtype)
+        with torch.cuda.stream(_stream_obj(stream)):
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = _load().gdr_chunk_prefill(
+        *args, _dev_ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(),
+        _stream(stream))
     _check(st, "gdr_chunk_prefill")
 
 
 def gdr_state_fixup(L, M, state_in, chunk_offsets, fixed, stream=None) -> None:
-    """fixed[c] = fixed[c-1] M_c + L_c over each sequence's chunk slots.
-    L, fixed [n_chunks, H, dv, dk], M [n_chunks, H, dk, dk] fp32; state_in
-    [N, H, dv, dk] fp32 or None; chunk_offsets [N+1] int32 (device)."""
+    """fixed[c] = fixed[c-1] @ M_c + L_c over each sequence's chunk slots.
+    L, fixed [n_chunks, H, dv, dk], M [n_chunks, H, dk, dk] fp32 (M[c, h] = M_c);
+    state_in [N, H, dv, dk] fp32 or None; chunk_offsets [N+1] int32 (device)."""
     n_chunks, H, dv, dk = L.shape
     N = chunk_offsets.shape[0] - 1
     if M.shape != (n_chunks, H, dk, dk) or fixed.shape != L.shape or \

@@ -15,11 +15,14 @@
 #include <string_view>
 
 #include "../../include/gdr.h"
+#include "api_internal.h"
 #include "launch.h"
 
 namespace {
-
 thread_local char g_last_error[512] = "";
+}  // namespace
+
+namespace gdr {
 
 gdr_status fail(gdr_status s, const char* fmt, ...) {
   va_list ap;
@@ -39,11 +42,7 @@ gdr_status hip_status(hipError_t e, const char* what) {
   return fail(GDR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-bool supported_dims(int dk, int dv) { return (dk == 64 && dv == 64) || (dk == 128 && dv == 128); }
-
-bool valid_dtype(int d) { return d == GDR_BF16 || d == GDR_FP32; }
+namespace {
 
 // Per-device properties, filled once per device.
 struct DeviceProps {
@@ -51,11 +50,12 @@ struct DeviceProps {
   bool gfx950 = false;
   char arch[64] = "";
 };
-constexpr int kMaxDevices = 64;
 DeviceProps g_props[kMaxDevices];
 std::mutex g_props_mu;
 
-gdr_status check_device() {
+}  // namespace
+
+gdr_status check_device(int* device) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_status(e, "hipGetDevice");
@@ -71,8 +71,24 @@ gdr_status check_device() {
     p.filled = true;
   }
   if (!p.gfx950) return fail(GDR_ERR_UNSUPPORTED, "device %d is %s; libgdr is built for gfx950", dev, p.arch);
+  if (device) *device = dev;
   return GDR_OK;
 }
+
+}  // namespace gdr
+
+namespace {
+
+using gdr::check_device;
+using gdr::fail;
+using gdr::hip_status;
+using gdr::ok;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_dims(int dk, int dv) { return (dk == 64 && dv == 64) || (dk == 128 && dv == 128); }
+
+bool valid_dtype(int d) { return d == GDR_BF16 || d == GDR_FP32; }
 
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -168,7 +184,7 @@ SegScanSizes segscan_sizes(int T_total, int N, int H, int d, int chunk, int max_
   return z;
 }
 
-// segment offsets | segment indices | cu_seg | offs_seg | L | M^T | end | start
+// segment offsets | segment indices | cu_seg | offs_seg | L | M | end | start
 size_t segscan_workspace(const SegScanSizes& z, int N) {
   if (z.seg == 0) return 0;
   return align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1)) +
@@ -177,7 +193,203 @@ size_t segscan_workspace(const SegScanSizes& z, int N) {
          4 * align_up(z.state_bytes);
 }
 
+// A failed launch, reported as "<entry point>: <phase>: <HIP error>".
+gdr_status hip_fail(hipError_t e, const char* who, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(GDR_ERR_HIP, "%s: %s: %s", who, what, hipGetErrorString(e));
+}
+
 }  // namespace
+
+namespace gdr {
+
+// Validation and dispatch of gdr_chunk_prefill.  `who` names the entry point
+// in error messages; with static_scratch the workspace is the library's own
+// scratch array, and a call that needs more than it holds is refused as
+// unsupported.
+gdr_status chunk_prefill(const char* who, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const int32_t* cu_seqlens, int N,
+                         const float* state_in, float* state_out, void* o, float* L_out,
+                         float* M_out, float* fixed_out, int T_total, int H, int dk, int dv,
+                         int chunk, gdr_dtype in_dtype, gdr_dtype out_dtype, void* workspace,
+                         size_t workspace_bytes, bool static_scratch, gdr_stream_t stream) {
+  if (!cu_seqlens || !state_out) return fail(GDR_ERR_INVALID_ARG, "%s: NULL cu_seqlens/state_out", who);
+  if (T_total > 0 && (!q || !k || !v || !g || !beta || !o))
+    return fail(GDR_ERR_INVALID_ARG, "%s: NULL tensor pointer", who);
+  if (T_total < 0 || N <= 0 || H <= 0)
+    return fail(GDR_ERR_INVALID_ARG, "%s: T_total=%d N=%d H=%d", who, T_total, N, H);
+  if (N > 65536 || H > 65535) return fail(GDR_ERR_INVALID_ARG, "%s: N or H too large", who);
+  if (!supported_dims(dk, dv))
+    return fail(GDR_ERR_UNSUPPORTED, "%s: (dk, dv) = (%d, %d) not in {(64,64), (128,128)}", who, dk, dv);
+  if (chunk != 16 && chunk != 64)
+    return fail(GDR_ERR_UNSUPPORTED, "%s: chunk=%d not in {16, 64}", who, chunk);
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(GDR_ERR_UNSUPPORTED, "%s: dtype codes must be GDR_BF16 or GDR_FP32", who);
+  const void* ptrs[] = {q, k, v, g, beta, state_in, state_out, o, L_out, M_out, fixed_out, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(GDR_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", who);
+  const int mc = gdr_max_chunks(T_total, N, chunk);
+  if (mc < 0) return fail(GDR_ERR_INVALID_ARG, "%s: too many chunks", who);
+  if (static_cast<int64_t>(T_total) * H > INT32_MAX || static_cast<int64_t>(mc) * H > INT32_MAX)
+    return fail(GDR_ERR_INVALID_ARG, "%s: T_total*H too large", who);
+
+  // workspace carve-up: offsets | indices | factors [| segments] (sequential
+  // scan), or offsets | indices | [L] | [M] | [fixed] | [segments]
+  // (chunk-parallel form)
+  const Schedule sched = schedule(L_out, M_out, T_total, N, H, chunk, in_dtype);
+  const bool scan = sched != kChunkParallel;
+  const size_t per = static_cast<size_t>(mc) * H * sizeof(float);
+  size_t need = layout_workspace(N, mc);
+  SegSizes segz;
+  SegScanSizes ssz;
+  if (scan) {
+    need += scan_workspace(mc, H, chunk);
+    if (sched == kSegmentedScan) {
+      ssz = segscan_sizes(T_total, N, H, dk, chunk, mc);
+      need += segscan_workspace(ssz, N);
+    }
+  } else {
+    if (!L_out) need += align_up(per * dv * dk);
+    if (!M_out) need += align_up(per * dk * dk);
+    if (!fixed_out) need += align_up(per * dv * dk);
+    segz = seg_sizes(T_total, N, H, dk, chunk, mc);
+    need += seg_workspace(segz, N);
+  }
+  if (static_scratch && need > workspace_bytes)
+    return fail(GDR_ERR_UNSUPPORTED,
+                "%s: this call needs %zu bytes of scratch and the library's static scratch holds "
+                "%zu; call gdr_chunk_prefill with a workspace instead", who, need, workspace_bytes);
+  if (workspace_bytes < need || (!workspace && need > 0))
+    return fail(GDR_ERR_INVALID_ARG, "%s: workspace of %zu bytes, need %zu", who, workspace_bytes, need);
+  gdr_status s = check_device();
+  if (s != GDR_OK) return s;
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* offs = reinterpret_cast<int32_t*>(ws);
+  ws += align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1));
+  int32_t* cidx = reinterpret_cast<int32_t*>(ws);
+  ws += align_up(sizeof(int32_t) * 2 * static_cast<size_t>(mc));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = gdr::launch_layout(cu_seqlens, N, chunk, offs, cidx, mc, st);
+  if (e != hipSuccess) return hip_fail(e, who, "layout");
+
+  if (scan) {
+    const gdr::ChunkFactorSizes z = gdr::chunk_factor_sizes(mc, H, chunk);
+    gdr::ChunkFactors f;
+    f.t = reinterpret_cast<uint16_t*>(ws);
+    ws += align_up(z.t);
+    f.p = reinterpret_cast<uint16_t*>(ws);
+    ws += align_up(z.p);
+    f.gate = reinterpret_cast<float*>(ws);
+    if (T_total > 0) {
+      e = gdr::launch_chunk_factors(q, k, g, beta, cu_seqlens, cidx, f, mc, T_total, H, dk, chunk,
+                                    st);
+      if (e != hipSuccess) return hip_fail(e, who, "chunk factors");
+    }
+    ws += align_up(z.gate);
+    if (sched == kScan) {
+      e = gdr::launch_chunk_scan(q, k, v, cu_seqlens, offs, f, state_in, state_out, fixed_out, o,
+                                 N, H, dk, chunk, mc, T_total, out_dtype, 0, st);
+      return hip_fail(e, who, "chunk scan");
+    }
+    // segmented scan
+    const int ms = ssz.max_segs;
+    int32_t* seg_offs = reinterpret_cast<int32_t*>(ws);
+    ws += align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1));
+    int32_t* seg_idx = reinterpret_cast<int32_t*>(ws);
+    ws += align_up(sizeof(int32_t) * 2 * static_cast<size_t>(ms));
+    int32_t* cu_seg = reinterpret_cast<int32_t*>(ws);
+    ws += align_up(sizeof(int32_t) * (static_cast<size_t>(ms) + 1));
+    int32_t* offs_seg = reinterpret_cast<int32_t*>(ws);
+    ws += align_up(sizeof(int32_t) * (static_cast<size_t>(ms) + 1));
+    float* seg_L = reinterpret_cast<float*>(ws);
+    ws += align_up(ssz.state_bytes);
+    float* seg_M = reinterpret_cast<float*>(ws);
+    ws += align_up(ssz.state_bytes);
+    float* seg_end = reinterpret_cast<float*>(ws);
+    ws += align_up(ssz.state_bytes);
+    float* seg_start = reinterpret_cast<float*>(ws);
+    e = gdr::launch_layout(offs, N, ssz.seg, seg_offs, seg_idx, ms, st);
+    if (e == hipSuccess)
+      e = gdr::launch_segment_ranges(cu_seqlens, offs, seg_idx, N, ssz.seg, chunk, ms, cu_seg,
+                                     offs_seg, st);
+    // local end state of every segment from zero
+    if (e == hipSuccess)
+      e = gdr::launch_chunk_scan(q, k, v, cu_seg, offs_seg, f, nullptr, seg_L, nullptr, nullptr,
+                                 ms, H, dk, chunk, mc, T_total, out_dtype, 0, st);
+    // transfer matrix of every segment: identity start, v = 0
+    if (e == hipSuccess)
+      e = gdr::launch_chunk_scan(q, k, nullptr, cu_seg, offs_seg, f, nullptr, seg_M, nullptr,
+                                 nullptr, ms, H, dk, chunk, mc, T_total, out_dtype,
+                                 gdr::kScanIdentityStart, st);
+    // segment-level fixup: the end state of every segment
+    if (e == hipSuccess)
+      e = gdr::launch_fixup_mode(0, seg_L, seg_M, state_in, seg_offs, nullptr, 0, nullptr,
+                                 seg_end, nullptr, ms, H, N, dk, 2, st);
+    if (e == hipSuccess)
+      e = gdr::launch_segment_starts(state_in, seg_end, seg_idx, ms, H, dk, seg_start, st);
+    // outputs (and chunk-end states) from the true segment starts
+    if (e == hipSuccess)
+      e = gdr::launch_chunk_scan(q, k, v, cu_seg, offs_seg, f, seg_start, nullptr, fixed_out, o,
+                                 ms, H, dk, chunk, mc, T_total, out_dtype, 0, st);
+    if (e != hipSuccess) return hip_fail(e, who, "segmented scan");
+    e = gdr::launch_final_state(state_in, seg_end, seg_offs, N, H, dk, dv, ms, state_out, st);
+    return hip_fail(e, who, "final state");
+  }
+
+  float* L = L_out;
+  if (!L) { L = reinterpret_cast<float*>(ws); ws += align_up(per * dv * dk); }
+  float* M = M_out;
+  if (!M) { M = reinterpret_cast<float*>(ws); ws += align_up(per * dk * dk); }
+  float* fixed = fixed_out;
+  if (!fixed) { fixed = reinterpret_cast<float*>(ws); ws += align_up(per * dv * dk); }
+  int32_t* seg_offs = nullptr;
+  int32_t* seg_idx = nullptr;
+  float *seg_L = nullptr, *seg_M = nullptr, *seg_fixed = nullptr;
+  if (segz.seg > 0) {
+    seg_offs = reinterpret_cast<int32_t*>(ws);
+    ws += align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1));
+    seg_idx = reinterpret_cast<int32_t*>(ws);
+    ws += align_up(sizeof(int32_t) * 2 * static_cast<size_t>(segz.max_segs));
+    seg_L = reinterpret_cast<float*>(ws);
+    ws += align_up(segz.state_bytes);
+    seg_M = reinterpret_cast<float*>(ws);
+    ws += align_up(segz.state_bytes);
+    seg_fixed = reinterpret_cast<float*>(ws);
+    ws += align_up(segz.state_bytes);
+  }
+
+  if (T_total > 0) {
+    e = gdr::launch_chunk_local(k, v, g, beta, cu_seqlens, cidx, L, M, mc, T_total, H, dk, dv,
+                                chunk, in_dtype, st);
+    if (e != hipSuccess) return hip_fail(e, who, "chunk_local");
+    const int planes = in_dtype == GDR_BF16 ? 2 : 3;
+    if (segz.seg == 0) {
+      e = gdr::launch_fixup(L, M, state_in, offs, N, fixed, mc, H, dk, dv, planes, st);
+      if (e != hipSuccess) return hip_fail(e, who, "fixup");
+    } else {
+      // two-level scan: segments of segz.seg chunks
+      e = gdr::launch_layout(offs, N, segz.seg, seg_offs, seg_idx, segz.max_segs, st);
+      if (e == hipSuccess)
+        e = gdr::launch_fixup_mode(1, L, M, nullptr, offs, seg_idx, segz.seg, nullptr, seg_L,
+                                   seg_M, mc, H, segz.max_segs, dk, planes, st);
+      if (e == hipSuccess)
+        e = gdr::launch_fixup_mode(0, seg_L, seg_M, state_in, seg_offs, nullptr, 0, nullptr,
+                                   seg_fixed, nullptr, segz.max_segs, H, N, dk, planes, st);
+      if (e == hipSuccess)
+        e = gdr::launch_fixup_mode(2, L, M, state_in, offs, seg_idx, segz.seg, seg_fixed, fixed,
+                                   nullptr, mc, H, segz.max_segs, dk, planes, st);
+      if (e != hipSuccess) return hip_fail(e, who, "segmented fixup");
+    }
+    e = gdr::launch_chunk_out(q, k, v, g, beta, cu_seqlens, cidx, state_in, fixed, o, mc, T_total,
+                              H, dk, dv, chunk, in_dtype, out_dtype, st);
+    if (e != hipSuccess) return hip_fail(e, who, "chunk_out");
+  }
+  e = gdr::launch_final_state(state_in, fixed, offs, N, H, dk, dv, mc, state_out, st);
+  return hip_fail(e, who, "final state");
+}
+
+}  // namespace gdr
 
 extern "C" {
 
@@ -259,18 +471,23 @@ gdr_status gdr_chunk_layout(const int32_t* cu_seqlens, int N, int chunk, int32_t
                     "gdr_chunk_layout launch");
 }
 
-size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int dv, int chunk) {
+size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int dv, int chunk,
+                                         gdr_dtype in_dtype) {
   const int mc = gdr_max_chunks(T_total, N, chunk);
-  if (mc < 0 || H <= 0 || !supported_dims(dk, dv)) return 0;
+  if (mc < 0 || H <= 0 || !supported_dims(dk, dv) || (chunk != 16 && chunk != 64) ||
+      !valid_dtype(in_dtype))
+    return 0;
   size_t cp = 0;
   const size_t per = static_cast<size_t>(mc) * H * sizeof(float);
   cp += align_up(per * dv * dk);  // L
   cp += align_up(per * dk * dk);  // M
   cp += align_up(per * dv * dk);  // fixed
   cp += seg_workspace(seg_sizes(T_total, N, H, dk, chunk, mc), N);
-  const size_t sc = chunk == 64 ? scan_workspace(mc, H, chunk) +
-                                      segscan_workspace(segscan_sizes(T_total, N, H, dk, chunk, mc), N)
-                                : 0;
+  // the scan schedules take bf16 inputs at chunk 64 only
+  const size_t sc = schedule(nullptr, nullptr, T_total, N, H, chunk, in_dtype) != kChunkParallel
+                        ? scan_workspace(mc, H, chunk) +
+                              segscan_workspace(segscan_sizes(T_total, N, H, dk, chunk, mc), N)
+                        : 0;
   return layout_workspace(N, mc) + (cp > sc ? cp : sc);
 }
 
@@ -280,178 +497,9 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
                              float* M_out, float* fixed_out, int T_total, int H, int dk, int dv,
                              int chunk, gdr_dtype in_dtype, gdr_dtype out_dtype, void* workspace,
                              size_t workspace_bytes, gdr_stream_t stream) {
-  if (!cu_seqlens || !state_out) return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: NULL cu_seqlens/state_out");
-  if (T_total > 0 && (!q || !k || !v || !g || !beta || !o))
-    return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: NULL tensor pointer");
-  if (T_total < 0 || N <= 0 || H <= 0)
-    return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: T_total=%d N=%d H=%d", T_total, N, H);
-  if (N > 65536 || H > 65535) return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: N or H too large");
-  if (!supported_dims(dk, dv))
-    return fail(GDR_ERR_UNSUPPORTED, "gdr_chunk_prefill: (dk, dv) = (%d, %d) not in {(64,64), (128,128)}", dk, dv);
-  if (chunk != 16 && chunk != 64)
-    return fail(GDR_ERR_UNSUPPORTED, "gdr_chunk_prefill: chunk=%d not in {16, 64}", chunk);
-  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
-    return fail(GDR_ERR_UNSUPPORTED, "gdr_chunk_prefill: dtype codes must be GDR_BF16 or GDR_FP32");
-  if (in_dtype == GDR_FP32 && chunk != 16)
-    return fail(GDR_ERR_UNSUPPORTED, "gdr_chunk_prefill: fp32 inputs need chunk=16");
-  const void* ptrs[] = {q, k, v, g, beta, state_in, state_out, o, L_out, M_out, fixed_out, workspace};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: pointers must be 16-byte aligned");
-  const int mc = gdr_max_chunks(T_total, N, chunk);
-  if (mc < 0) return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: too many chunks");
-  if (static_cast<int64_t>(T_total) * H > INT32_MAX || static_cast<int64_t>(mc) * H > INT32_MAX)
-    return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: T_total*H too large");
-
-  // workspace carve-up: offsets | indices | factors [| segments] (sequential
-  // scan), or offsets | indices | [L] | [M] | [fixed] | [segments]
-  // (chunk-parallel form)
-  const Schedule sched = schedule(L_out, M_out, T_total, N, H, chunk, in_dtype);
-  const bool scan = sched != kChunkParallel;
-  const size_t per = static_cast<size_t>(mc) * H * sizeof(float);
-  size_t need = layout_workspace(N, mc);
-  SegSizes segz;
-  SegScanSizes ssz;
-  if (scan) {
-    need += scan_workspace(mc, H, chunk);
-    if (sched == kSegmentedScan) {
-      ssz = segscan_sizes(T_total, N, H, dk, chunk, mc);
-      need += segscan_workspace(ssz, N);
-    }
-  } else {
-    if (!L_out) need += align_up(per * dv * dk);
-    if (!M_out) need += align_up(per * dk * dk);
-    if (!fixed_out) need += align_up(per * dv * dk);
-    segz = seg_sizes(T_total, N, H, dk, chunk, mc);
-    need += seg_workspace(segz, N);
-  }
-  if (workspace_bytes < need || (!workspace && need > 0))
-    return fail(GDR_ERR_INVALID_ARG, "gdr_chunk_prefill: workspace of %zu bytes, need %zu", workspace_bytes, need);
-  gdr_status s = check_device();
-  if (s != GDR_OK) return s;
-
-  char* ws = static_cast<char*>(workspace);
-  int32_t* offs = reinterpret_cast<int32_t*>(ws);
-  ws += align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1));
-  int32_t* cidx = reinterpret_cast<int32_t*>(ws);
-  ws += align_up(sizeof(int32_t) * 2 * static_cast<size_t>(mc));
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = gdr::launch_layout(cu_seqlens, N, chunk, offs, cidx, mc, st);
-  if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: layout");
-
-  if (scan) {
-    const gdr::ChunkFactorSizes z = gdr::chunk_factor_sizes(mc, H, chunk);
-    gdr::ChunkFactors f;
-    f.t = reinterpret_cast<uint16_t*>(ws);
-    ws += align_up(z.t);
-    f.p = reinterpret_cast<uint16_t*>(ws);
-    ws += align_up(z.p);
-    f.gate = reinterpret_cast<float*>(ws);
-    if (T_total > 0) {
-      e = gdr::launch_chunk_factors(q, k, g, beta, cu_seqlens, cidx, f, mc, T_total, H, dk, chunk,
-                                    st);
-      if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: chunk factors");
-    }
-    ws += align_up(z.gate);
-    if (sched == kScan) {
-      e = gdr::launch_chunk_scan(q, k, v, cu_seqlens, offs, f, state_in, state_out, fixed_out, o,
-                                 N, H, dk, chunk, mc, T_total, out_dtype, 0, st);
-      return hip_status(e, "gdr_chunk_prefill: chunk scan");
-    }
-    // segmented scan
-    const int ms = ssz.max_segs;
-    int32_t* seg_offs = reinterpret_cast<int32_t*>(ws);
-    ws += align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1));
-    int32_t* seg_idx = reinterpret_cast<int32_t*>(ws);
-    ws += align_up(sizeof(int32_t) * 2 * static_cast<size_t>(ms));
-    int32_t* cu_seg = reinterpret_cast<int32_t*>(ws);
-    ws += align_up(sizeof(int32_t) * (static_cast<size_t>(ms) + 1));
-    int32_t* offs_seg = reinterpret_cast<int32_t*>(ws);
-    ws += align_up(sizeof(int32_t) * (static_cast<size_t>(ms) + 1));
-    float* seg_L = reinterpret_cast<float*>(ws);
-    ws += align_up(ssz.state_bytes);
-    float* seg_Mt = reinterpret_cast<float*>(ws);
-    ws += align_up(ssz.state_bytes);
-    float* seg_end = reinterpret_cast<float*>(ws);
-    ws += align_up(ssz.state_bytes);
-    float* seg_start = reinterpret_cast<float*>(ws);
-    e = gdr::launch_layout(offs, N, ssz.seg, seg_offs, seg_idx, ms, st);
-    if (e == hipSuccess)
-      e = gdr::launch_segment_ranges(cu_seqlens, offs, seg_idx, N, ssz.seg, chunk, ms, cu_seg,
-                                     offs_seg, st);
-    // local end state of every segment from zero
-    if (e == hipSuccess)
-      e = gdr::launch_chunk_scan(q, k, v, cu_seg, offs_seg, f, nullptr, seg_L, nullptr, nullptr,
-                                 ms, H, dk, chunk, mc, T_total, out_dtype, 0, st);
-    // transfer matrix of every segment, transposed: identity start, v = 0
-    if (e == hipSuccess)
-      e = gdr::launch_chunk_scan(q, k, nullptr, cu_seg, offs_seg, f, nullptr, seg_Mt, nullptr,
-                                 nullptr, ms, H, dk, chunk, mc, T_total, out_dtype,
-                                 gdr::kScanIdentityStart | gdr::kScanTransposedOut, st);
-    // segment-level fixup: the end state of every segment
-    if (e == hipSuccess)
-      e = gdr::launch_fixup_mode(0, seg_L, seg_Mt, state_in, seg_offs, nullptr, 0, nullptr,
-                                 seg_end, nullptr, ms, H, N, dk, 2, st);
-    if (e == hipSuccess)
-      e = gdr::launch_segment_starts(state_in, seg_end, seg_idx, ms, H, dk, seg_start, st);
-    // outputs (and chunk-end states) from the true segment starts
-    if (e == hipSuccess)
-      e = gdr::launch_chunk_scan(q, k, v, cu_seg, offs_seg, f, seg_start, nullptr, fixed_out, o,
-                                 ms, H, dk, chunk, mc, T_total, out_dtype, 0, st);
-    if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: segmented scan");
-    e = gdr::launch_final_state(state_in, seg_end, seg_offs, N, H, dk, dv, ms, state_out, st);
-    return hip_status(e, "gdr_chunk_prefill: final state");
-  }
-
-  float* L = L_out;
-  if (!L) { L = reinterpret_cast<float*>(ws); ws += align_up(per * dv * dk); }
-  float* M = M_out;
-  if (!M) { M = reinterpret_cast<float*>(ws); ws += align_up(per * dk * dk); }
-  float* fixed = fixed_out;
-  if (!fixed) { fixed = reinterpret_cast<float*>(ws); ws += align_up(per * dv * dk); }
-  int32_t* seg_offs = nullptr;
-  int32_t* seg_idx = nullptr;
-  float *seg_L = nullptr, *seg_Mt = nullptr, *seg_fixed = nullptr;
-  if (segz.seg > 0) {
-    seg_offs = reinterpret_cast<int32_t*>(ws);
-    ws += align_up(sizeof(int32_t) * (static_cast<size_t>(N) + 1));
-    seg_idx = reinterpret_cast<int32_t*>(ws);
-    ws += align_up(sizeof(int32_t) * 2 * static_cast<size_t>(segz.max_segs));
-    seg_L = reinterpret_cast<float*>(ws);
-    ws += align_up(segz.state_bytes);
-    seg_Mt = reinterpret_cast<float*>(ws);
-    ws += align_up(segz.state_bytes);
-    seg_fixed = reinterpret_cast<float*>(ws);
-    ws += align_up(segz.state_bytes);
-  }
-
-  if (T_total > 0) {
-    e = gdr::launch_chunk_local(k, v, g, beta, cu_seqlens, cidx, L, M, mc, T_total, H, dk, dv,
-                                chunk, in_dtype, st);
-    if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: chunk_local");
-    const int planes = in_dtype == GDR_BF16 ? 2 : 3;
-    if (segz.seg == 0) {
-      e = gdr::launch_fixup(L, M, state_in, offs, N, fixed, mc, H, dk, dv, planes, st);
-      if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: fixup");
-    } else {
-      // two-level scan: segments of segz.seg chunks
-      e = gdr::launch_layout(offs, N, segz.seg, seg_offs, seg_idx, segz.max_segs, st);
-      if (e == hipSuccess)
-        e = gdr::launch_fixup_mode(1, L, M, nullptr, offs, seg_idx, segz.seg, nullptr, seg_L,
-                                   seg_Mt, mc, H, segz.max_segs, dk, planes, st);
-      if (e == hipSuccess)
-        e = gdr::launch_fixup_mode(0, seg_L, seg_Mt, state_in, seg_offs, nullptr, 0, nullptr,
-                                   seg_fixed, nullptr, segz.max_segs, H, N, dk, planes, st);
-      if (e == hipSuccess)
-        e = gdr::launch_fixup_mode(2, L, M, state_in, offs, seg_idx, segz.seg, seg_fixed, fixed,
-                                   nullptr, mc, H, segz.max_segs, dk, planes, st);
-      if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: segmented fixup");
-    }
-    e = gdr::launch_chunk_out(q, k, v, g, beta, cu_seqlens, cidx, state_in, fixed, o, mc, T_total,
-                              H, dk, dv, chunk, in_dtype, out_dtype, st);
-    if (e != hipSuccess) return hip_status(e, "gdr_chunk_prefill: chunk_out");
-  }
-  e = gdr::launch_final_state(state_in, fixed, offs, N, H, dk, dv, mc, state_out, st);
-  return hip_status(e, "gdr_chunk_prefill: final state");
+  return gdr::chunk_prefill("gdr_chunk_prefill", q, k, v, g, beta, cu_seqlens, N, state_in,
+                            state_out, o, L_out, M_out, fixed_out, T_total, H, dk, dv, chunk,
+                            in_dtype, out_dtype, workspace, workspace_bytes, false, stream);
 }
 
 gdr_status gdr_state_fixup(const float* L, const float* M, const float* state_in,

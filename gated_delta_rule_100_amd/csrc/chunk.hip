@@ -30,9 +30,8 @@
 // PR #6291 page, "Mamba-2 SSD optimisation, round 4", code analysis 3).
 //
 // Products run on v_mfma_f32_16x16x{16,32}_bf16 with fp32 operands split into
-// bf16 planes (mfma_planes.h).  M is written transposed (row b of slot c holds
-// column b of M_c), which is the layout the fixup scan loads with 16-byte
-// reads.
+// bf16 planes (mfma_planes.h).  L and M are written in the orientation of the
+// recurrence: slot c holds M_c[a][b] at row a, column b (S_end = S0 M_c + L_c).
 #include "launch.h"
 #include "mfma_planes.h"
 
@@ -645,7 +644,8 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
   floatx4 Wacc[Cfg::NT][Cfg::DPW], Uacc[Cfg::NT][Cfg::DPW];
   w.solve_wy(Wacc, Uacc);
 
-  // L = Ut^T diag(D) K (rows of this wave's feature tiles), M^T stored.
+  // L = Ut^T diag(D) K and M = gamma_C I - W^T diag(D) K, rows of this wave's
+  // feature tiles (16 lanes store 64 contiguous bytes of a row).
   const float gam_end = w.sgam[C - 1];
   const size_t base = (static_cast<size_t>(cid) * H + h) * D * D;
 #pragma unroll
@@ -668,13 +668,11 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
       }
       const int i0 = 16 * b + 4 * w.g4, j = 16 * bj + w.c16;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Lout[base + static_cast<size_t>(i0 + e) * D + j] = l[e];
-      float4 mt;
-      mt.x = (i0 + 0 == j ? gam_end : 0.f) - m[0];
-      mt.y = (i0 + 1 == j ? gam_end : 0.f) - m[1];
-      mt.z = (i0 + 2 == j ? gam_end : 0.f) - m[2];
-      mt.w = (i0 + 3 == j ? gam_end : 0.f) - m[3];
-      *reinterpret_cast<float4*>(Mout + base + static_cast<size_t>(j) * D + i0) = mt;
+      for (int e = 0; e < 4; ++e) {
+        const size_t at = base + static_cast<size_t>(i0 + e) * D + j;
+        Lout[at] = l[e];
+        Mout[at] = (i0 + e == j ? gam_end : 0.f) - m[e];
+      }
     }
   }
 }
@@ -984,7 +982,11 @@ hipError_t launch_chunk_local(const void* k, const void* v, const float* g, cons
     if (chunk == 64) GDR_LOCAL(64, 64, Dt::BF16);
     GDR_LOCAL(64, 16, Dt::BF16);
   }
-  if (dk == 128) GDR_LOCAL(128, 16, Dt::F32);
+  if (dk == 128) {
+    if (chunk == 64) GDR_LOCAL(128, 64, Dt::F32);
+    GDR_LOCAL(128, 16, Dt::F32);
+  }
+  if (chunk == 64) GDR_LOCAL(64, 64, Dt::F32);
   GDR_LOCAL(64, 16, Dt::F32);
 #undef GDR_LOCAL
 }
@@ -1008,7 +1010,11 @@ hipError_t launch_chunk_out(const void* q, const void* k, const void* v, const f
     if (chunk == 64) GDR_OUT(64, 64, Dt::BF16);
     GDR_OUT(64, 16, Dt::BF16);
   }
-  if (dk == 128) GDR_OUT(128, 16, Dt::F32);
+  if (dk == 128) {
+    if (chunk == 64) GDR_OUT(128, 64, Dt::F32);
+    GDR_OUT(128, 16, Dt::F32);
+  }
+  if (chunk == 64) GDR_OUT(64, 64, Dt::F32);
   GDR_OUT(64, 16, Dt::F32);
 #undef GDR_OUT
 }

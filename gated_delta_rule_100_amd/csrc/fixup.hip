@@ -1,145 +1,28 @@
 // fixup.hip -- inter-chunk state fixup and final-state copy on gfx950.
 //
 // fixed[c] = fixed[c-1] M_c + L_c is a chain of dependent matrix products per
-// (sequence, head); the rows of the state are independent (row i of the
-// result only needs row i of the previous state), so the work is split over
-// workgroups of R state rows.  Each workgroup walks its sequence's chunks in
-// order, the way run_simt_fixup_loop on the FlashInfer PR #3866 page does
-// ("CP delta-rule precompute optimisation for ultra-low parallelism", code
-// changes 2): it keeps its R rows in LDS, each thread owns one output column
-// and one half of the contraction, loads its column of M_c straight into
-// registers, and preloads chunk c+1's M and L columns while chunk c is
-// accumulated.  The two half-contractions meet in LDS, the new rows are
-// published to LDS and to fixed[c].  Start (init_state_tile on the same page):
-// with an initial state the scan begins at the sequence's first chunk; without
-// one the first fixed state is L of that chunk and the scan begins at the next.
-// All arithmetic is fp32 FMA.
+// (sequence, head) (the fixup of the FlashInfer PR #3866 page, "CP delta-rule
+// precompute optimisation for ultra-low parallelism", code changes 2: the
+// state multiplies M_c from the left, accumulate_state_fragment).  Row i of
+// the new state only needs row i of the previous one, so the work is split
+// over workgroups of state rows; each walks its sequence's chunks in order.
 #include "launch.h"
 #include "mfma_planes.h"
 
 namespace gdr {
 namespace {
 
-constexpr int kFixupRows = 4;
-
-template <int DK, int DV, int R>
-__global__ __launch_bounds__(2 * DK) void fixup_kernel(const float* __restrict__ L,
-                                                       const float* __restrict__ M,
-                                                       const float* __restrict__ state_in,
-                                                       const int32_t* __restrict__ offs,
-                                                       float* __restrict__ fixed, int n_chunks,
-                                                       int H) {
-  constexpr int KH = DK / 2;  // contraction half owned by a thread
-  const int row0 = blockIdx.x * R;
-  const int h = blockIdx.y;
-  const int n = blockIdx.z;
-  const int col = threadIdx.x % DK;
-  const int kh = threadIdx.x / DK;
-
-  int c_end = offs[n + 1];
-  int c_begin = offs[n];
-  c_end = c_end < n_chunks ? c_end : n_chunks;
-  c_begin = c_begin < 0 ? 0 : c_begin;
-  if (c_begin >= c_end) return;
-
-  __shared__ float s_lds[R][DK];
-  __shared__ float part[R][DK];
-
-  auto l_at = [&](int c, int i) -> size_t {
-    return ((static_cast<size_t>(c) * H + h) * DV + row0 + i) * DK + col;
-  };
-  auto m_base = [&](int c) -> size_t { return (static_cast<size_t>(c) * H + h) * DK * DK; };
-
-  int start;
-  if (state_in != nullptr) {
-    if (kh == 0) {
-#pragma unroll
-      for (int i = 0; i < R; ++i)
-        s_lds[i][col] = state_in[((static_cast<size_t>(n) * H + h) * DV + row0 + i) * DK + col];
-    }
-    start = c_begin;
-  } else {
-    if (kh == 0) {
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const float x = L[l_at(c_begin, i)];
-        s_lds[i][col] = x;
-        fixed[l_at(c_begin, i)] = x;
-      }
-    }
-    start = c_begin + 1;
-  }
-  __syncthreads();
-  if (start >= c_end) return;
-
-  // M is stored transposed: the column `col` of M_c is row `col` of the slot.
-  float m_cur[KH], l_cur[R];
-  {
-    const float* Mc = M + m_base(start) + static_cast<size_t>(col) * DK + kh * KH;
-#pragma unroll
-    for (int kk = 0; kk < KH; ++kk) m_cur[kk] = Mc[kk];
-#pragma unroll
-    for (int i = 0; i < R; ++i) l_cur[i] = kh == 0 ? L[l_at(start, i)] : 0.f;
-  }
-
-  for (int c = start; c < c_end; ++c) {
-    const bool more = c + 1 < c_end;
-    float m_nxt[KH], l_nxt[R];
-    if (more) {
-      const float* Mc = M + m_base(c + 1) + static_cast<size_t>(col) * DK + kh * KH;
-#pragma unroll
-      for (int kk = 0; kk < KH; ++kk) m_nxt[kk] = Mc[kk];
-#pragma unroll
-      for (int i = 0; i < R; ++i) l_nxt[i] = kh == 0 ? L[l_at(c + 1, i)] : 0.f;
-    }
-
-    float acc[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) acc[i] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KH; kk += 4) {
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const float4 s = *reinterpret_cast<const float4*>(&s_lds[i][kh * KH + kk]);
-        acc[i] = fmaf(s.x, m_cur[kk + 0], acc[i]);
-        acc[i] = fmaf(s.y, m_cur[kk + 1], acc[i]);
-        acc[i] = fmaf(s.z, m_cur[kk + 2], acc[i]);
-        acc[i] = fmaf(s.w, m_cur[kk + 3], acc[i]);
-      }
-    }
-    if (kh == 1) {
-#pragma unroll
-      for (int i = 0; i < R; ++i) part[i][col] = acc[i];
-    }
-    __syncthreads();
-    if (kh == 0) {
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const float x = (acc[i] + part[i][col]) + l_cur[i];
-        fixed[l_at(c, i)] = x;
-        s_lds[i][col] = x;
-      }
-    }
-    __syncthreads();
-    if (more) {
-#pragma unroll
-      for (int kk = 0; kk < KH; ++kk) m_cur[kk] = m_nxt[kk];
-#pragma unroll
-      for (int i = 0; i < R; ++i) l_cur[i] = l_nxt[i];
-    }
-  }
-}
-
 // Matrix-core fixup: ROWS state rows per workgroup (16, 32 or 64: one to four
 // 16-row MFMA tiles) and one wave per 16-wide output column tile (8 waves at
 // d = 128).  Per chunk:
 // S' = S M_c + L_c with S as bf16 planes in LDS (double-buffered, so one
-// barrier per chunk).  M is read transposed (row b of a slot holds column b
-// of M_c), so lane (c, g) of the B operand -- M[32kb + 8g .. 8g+7][16w + c] --
-// is 32 contiguous bytes, loaded while the previous chunk is multiplied.  L
-// is loaded in the output layout.  Workgroups of one unit (and head) are
-// placed on one XCD (dispatch is round-robin over the 8 XCDs by workgroup
-// id), so M_c is fetched from HBM once and served to all of them from L2.
+// barrier per chunk).  Lane (c, g) of the B operand holds
+// M[32kb + 8g .. 8g+7][16w + c]: eight loads, each of which reads 64
+// contiguous bytes of a row of M_c across the 16 lanes of a group, issued
+// while the previous chunk is multiplied.  L is loaded in the output layout.
+// Workgroups of one unit (and head) are placed on one XCD (dispatch is
+// round-robin over the 8 XCDs by workgroup id), so M_c is fetched from HBM
+// once and served to all of them from L2.
 //
 // Each chunk costs every workgroup a full M_c from L2, so a long chain is
 // bound by that per-step transfer; long sequences therefore use a two-level
@@ -150,7 +33,7 @@ __global__ __launch_bounds__(2 * DK) void fixup_kernel(const float* __restrict__
 //   kCompose  units are segments; rows 0..D-1 run from a zero state and give
 //             the segment's local state L_s (written once), rows D..2D-1 start
 //             from the identity without L and give the segment's transfer
-//             M_s = M_c0 M_c1 ... (written transposed, like M);
+//             M_s = M_c0 M_c1 ... (its rows are the rows of that state);
 //   kApply    units are segments; the start state is the previous segment's
 //             scanned state (or the sequence's initial state) and fixed[c] is
 //             written for every chunk.
@@ -160,9 +43,9 @@ enum FixMode { kSeq = 0, kCompose = 1, kApply = 2 };
 
 template <int D, int P, int MODE, int ROWS>
 __global__ __launch_bounds__(D * 4) void fixup_mfma_kernel(
-    const float* __restrict__ L, const float* __restrict__ Mt, const float* __restrict__ state_in,
+    const float* __restrict__ L, const float* __restrict__ M, const float* __restrict__ state_in,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ seg_idx, int seg,
-    const float* __restrict__ seg_start, float* __restrict__ out, float* __restrict__ out_mt,
+    const float* __restrict__ seg_start, float* __restrict__ out, float* __restrict__ out_m,
     int n_chunks, int H, int n_units) {
   constexpr int NTHR = D * 4;       // one wave per 16 output columns
   constexpr int RT = ROWS / 16;     // 16-row MFMA tiles per workgroup
@@ -235,18 +118,17 @@ __global__ __launch_bounds__(D * 4) void fixup_mfma_kernel(
   }
   __syncthreads();
 
-  typedef float4 MRaw[KB][2];
+  typedef float MRaw[KB][8];
   typedef float LRaw[RT][4];
   // Loads are unconditional (a chunk past the end re-reads the last one).
   auto fetch = [&](int c, MRaw& m, LRaw& l) {
     c = c < c_end ? c : c_end - 1;
-    const float4* src = reinterpret_cast<const float4*>(
-        Mt + (static_cast<size_t>(c) * H + h) * D * D + static_cast<size_t>(col) * D + 8 * g4);
+    const float* src = M + (static_cast<size_t>(c) * H + h) * D * D +
+                       static_cast<size_t>(8 * g4) * D + col;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      m[kb][0] = src[8 * kb];
-      m[kb][1] = src[8 * kb + 1];
-    }
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m[kb][j] = src[static_cast<size_t>(32 * kb + j) * D];
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
@@ -263,11 +145,7 @@ __global__ __launch_bounds__(D * 4) void fixup_mfma_kernel(
   float lc[RT][4];
   auto convert = [&]() {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const float x[8] = {m[kb][0].x, m[kb][0].y, m[kb][0].z, m[kb][0].w,
-                          m[kb][1].x, m[kb][1].y, m[kb][1].z, m[kb][1].w};
-      split8<P>(x, mb[kb]);
-    }
+    for (int kb = 0; kb < KB; ++kb) split8<P>(m[kb], mb[kb]);
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
@@ -316,24 +194,19 @@ __global__ __launch_bounds__(D * 4) void fixup_mfma_kernel(
   }
 
   if (MODE == kCompose) {
-    // Final rows of the segment: L_s rows in state layout, M_s transposed.
+    // Final rows of the segment: L_s or M_s, both in state layout.
     if (start >= c_end) {  // a one-chunk segment without transfer rows: L_s = L of that chunk
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
         for (int e = 0; e < 4; ++e) last[r][e] = L[st_at(c_begin, 16 * r + 4 * g4 + e, col)];
     }
-    const size_t base = (static_cast<size_t>(u) * H + h) * D * D;
+    float* dst = (trans_rows ? out_m : out) + (static_cast<size_t>(u) * H + h) * D * D;
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       const int row = row0 + 16 * r + 4 * g4;
-      if (trans_rows) {
-        *reinterpret_cast<float4*>(out_mt + base + static_cast<size_t>(col) * D + row) =
-            make_float4(last[r][0], last[r][1], last[r][2], last[r][3]);
-      } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) out[base + static_cast<size_t>(row + e) * D + col] = last[r][e];
-      }
+      for (int e = 0; e < 4; ++e) dst[static_cast<size_t>(row + e) * D + col] = last[r][e];
     }
   }
 }
@@ -364,9 +237,9 @@ __global__ __launch_bounds__(256) void final_state_kernel(const float* __restric
 
 }  // namespace
 
-hipError_t launch_fixup_mode(int mode, const float* L, const float* Mt, const float* state_in,
+hipError_t launch_fixup_mode(int mode, const float* L, const float* M, const float* state_in,
                              const int32_t* offs, const int32_t* seg_idx, int seg,
-                             const float* seg_start, float* out, float* out_mt, int n_chunks,
+                             const float* seg_start, float* out, float* out_m, int n_chunks,
                              int H, int n_units, int dk, int planes, hipStream_t stream) {
   if (n_units <= 0) return hipSuccess;
   const int pairs = n_units * H;
@@ -380,8 +253,8 @@ hipError_t launch_fixup_mode(int mode, const float* L, const float* Mt, const fl
   const int rbu = (dk / rows) * copies;
   const dim3 grid(kXcds * ((pairs + kXcds - 1) / kXcds) * rbu);
 #define GDR_FIX_R(D_, P_, M_, R_)                                                               \
-  hipLaunchKernelGGL((fixup_mfma_kernel<D_, P_, M_, R_>), grid, dim3(D_ * 4), 0, stream, L, Mt,  \
-                     state_in, offs, seg_idx, seg, seg_start, out, out_mt, n_chunks, H, n_units)
+  hipLaunchKernelGGL((fixup_mfma_kernel<D_, P_, M_, R_>), grid, dim3(D_ * 4), 0, stream, L, M,   \
+                     state_in, offs, seg_idx, seg, seg_start, out, out_m, n_chunks, H, n_units)
 #define GDR_FIX(D_, P_, M_)                                                                     \
   do {                                                                                          \
     if (rows == 64) GDR_FIX_R(D_, P_, M_, 64);                                                  \
@@ -410,16 +283,6 @@ hipError_t launch_fixup(const float* L, const float* M, const float* state_in,
                         const int32_t* chunk_offsets, int N, float* fixed, int n_chunks, int H,
                         int dk, int dv, int planes, hipStream_t stream) {
   (void)dv;
-  if (planes == 0) {
-    if (dk == 128) {
-      hipLaunchKernelGGL((fixup_kernel<128, 128, kFixupRows>), dim3(128 / kFixupRows, H, N),
-                         dim3(256), 0, stream, L, M, state_in, chunk_offsets, fixed, n_chunks, H);
-    } else {
-      hipLaunchKernelGGL((fixup_kernel<64, 64, kFixupRows>), dim3(64 / kFixupRows, H, N),
-                         dim3(128), 0, stream, L, M, state_in, chunk_offsets, fixed, n_chunks, H);
-    }
-    return hipGetLastError();
-  }
   return launch_fixup_mode(kSeq, L, M, state_in, chunk_offsets, nullptr, 0, nullptr, fixed,
                            nullptr, n_chunks, H, N, dk, planes, stream);
 }

@@ -26,21 +26,22 @@ hipError_t launch_mtp(const void* q, const void* k, const void* v, const float* 
 hipError_t launch_layout(const int32_t* cu_seqlens, int N, int chunk, int32_t* chunk_offsets,
                          int32_t* chunk_indices, int max_chunks, hipStream_t stream);
 
-// Inter-chunk fixup: fixed[c] = fixed[c-1] M_c + L_c per (sequence, head).
-// planes = 2 or 3: matrix-core scan with the state and M carried as that many
-// bf16 planes (3 keeps fp32 precision); planes = 0: fp32 FMA scan.
+// Inter-chunk fixup: fixed[c] = fixed[c-1] M_c + L_c per (sequence, head),
+// with M_c[a][b] at row a, column b of its slot.  planes = 2 or 3: the state
+// and M are carried as that many bf16 planes on the matrix cores (3 keeps fp32
+// precision).
 hipError_t launch_fixup(const float* L, const float* M, const float* state_in,
                         const int32_t* chunk_offsets, int N, float* fixed, int n_chunks, int H,
                         int dk, int dv, int planes, hipStream_t stream);
 
 // Fixup variants over units (sequences or segments of `seg` chunks); see
 // fixup.hip.  mode 0: per-sequence scan writing every chunk state to `out`;
-// mode 1: per-segment local state (out) and transposed transfer product
-// (out_mt); mode 2: per-segment scan from the scanned segment starts
-// (seg_start) writing every chunk state to `out`.
-hipError_t launch_fixup_mode(int mode, const float* L, const float* Mt, const float* state_in,
+// mode 1: per-segment local state (out) and transfer product (out_m); mode 2:
+// per-segment scan from the scanned segment starts (seg_start) writing every
+// chunk state to `out`.
+hipError_t launch_fixup_mode(int mode, const float* L, const float* M, const float* state_in,
                              const int32_t* offs, const int32_t* seg_idx, int seg,
-                             const float* seg_start, float* out, float* out_mt, int n_chunks,
+                             const float* seg_start, float* out, float* out_m, int n_chunks,
                              int H, int n_units, int dk, int planes, hipStream_t stream);
 
 // Chunk-local precompute: L_c and M_c for every chunk slot < max_chunks.
@@ -100,10 +101,10 @@ hipError_t launch_chunk_factors(const void* q, const void* k, const float* g, co
 // when state_out is NULL), and (when fixed != NULL) the state at every chunk
 // end.  v == NULL takes v as zero.  flags: kScanIdentityStart starts every
 // (sequence, head) from the identity instead of state_in (dv = dk), which with
-// v == NULL makes the final state the sequence's transfer matrix;
-// kScanTransposedOut writes each final state transposed.
+// v == NULL makes the final state the sequence's transfer matrix (the map
+// S -> S M of the recurrence without its v k^T terms, row a of the state
+// being row a of M).
 constexpr int kScanIdentityStart = 1;
-constexpr int kScanTransposedOut = 2;
 hipError_t launch_chunk_scan(const void* q, const void* k, const void* v,
                              const int32_t* cu_seqlens, const int32_t* chunk_offsets,
                              const ChunkFactors& f, const float* state_in, float* state_out,

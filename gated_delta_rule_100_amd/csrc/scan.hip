@@ -628,15 +628,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
     }
   }
 
-  if (state_out && (flags & kScanTransposedOut)) {
-    // column vrow of the (sequence, head)'s matrix: element (j, vrow) = S[vrow][j]
-    float* so = state_out + (static_cast<size_t>(n) * H + h) * D * D;
-#pragma unroll
-    for (int jl = 0; jl < JT; ++jl)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        so[static_cast<size_t>(16 * (jt0 + jl) + 4 * g4 + e) * D + vrow] = S[jl][e];
-  } else if (state_out) {
+  if (state_out) {
 #pragma unroll
     for (int jl = 0; jl < JT; ++jl)
       *reinterpret_cast<floatx4*>(state_out + sbase + 16 * (jt0 + jl) + 4 * g4) = S[jl];

@@ -157,11 +157,13 @@ gdr_status gdr_chunk_layout(const int32_t* cu_seqlens, int N, int chunk,
 
 /*
  * gdr_chunk_prefill_workspace_bytes -- device workspace that gdr_chunk_prefill
- * needs when L_out, M_out and fixed_out are all NULL, for either schedule (an
- * upper bound for every other case).  Returns 0 on bad arguments.
+ * needs for inputs of in_dtype when L_out, M_out and fixed_out are all NULL,
+ * for whichever schedule the call takes (an upper bound for every other case).
+ * Returns 0 on bad arguments (also for a shape or dtype gdr_chunk_prefill
+ * refuses).
  */
 size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int dv,
-                                         int chunk);
+                                         int chunk, gdr_dtype in_dtype);
 
 /*
  * gdr_chunk_prefill -- chunked prefill over packed variable-length sequences.
@@ -174,20 +176,23 @@ size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int 
  *   state_out   [N, H, dv, dk]    fp32 final states (may equal state_in)
  *   o           [T_total, H, dv]  out_dtype
  *   L_out       [max_chunks, H, dv, dk] fp32 or NULL: local state of every chunk
- *               (the chunk run from a zero state)
+ *               (the chunk run from a zero state): L_out[c][h][i][j] = L_c[i][j]
  *   M_out       [max_chunks, H, dk, dk] fp32 or NULL: transfer matrix of every
- *               chunk, stored TRANSPOSED: M_out[c][h][b][a] = M_c[a][b], where
- *               S_end = S_start M_c + L_c (row b of a slot is column b of M_c,
- *               the layout the fixup reads with contiguous loads)
+ *               chunk, M_out[c][h][a][b] = M_c[a][b], in the orientation of
+ *               the recurrence: S_end = S_start M_c + L_c, i.e.
+ *               S_end[i][b] = sum_a S_start[i][a] M_c[a][b] + L_c[i][b]
+ *               (M_c = gamma_c I - W^T diag(D) K, the product of the chunk's
+ *               per-token maps alpha_t (I - beta_t k_t k_t^T) in token order)
  *   fixed_out   [max_chunks, H, dv, dk] fp32 or NULL: state at the end of every
  *               chunk
  *   (max_chunks = gdr_max_chunks(T_total, N, chunk); chunk slot
  *    chunk_offsets[n] + j belongs to chunk j of sequence n; slots past the real
  *    chunk count are not written)
- *   T_total >= 0, N > 0, H > 0; chunk in {16, 64}
+ *   T_total >= 0, N > 0, H > 0; chunk in {16, 64}; in_dtype bf16 or fp32 at
+ *   either chunk size
  *   workspace   device scratch of workspace_bytes bytes (see
  *               gdr_chunk_prefill_workspace_bytes); may be NULL only when the
- *               bound is 0
+ *               bound is 0; its contents on entry do not matter
  * Sequences of length 0 are allowed: their final state is the initial state
  * (or zero).  q, k, v, g, beta and o must not overlap each other or the
  * state/L/M/fixed buffers.  All work is enqueued on `stream`, in one of the
@@ -195,7 +200,7 @@ size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int 
  *   - chunk-parallel: layout, chunk-local L/M, fixup over the chunks of each
  *     sequence (two-level for long sequences with few heads), chunk outputs,
  *     final states.  Taken when L_out or M_out is given, and for fp32 inputs
- *     or chunk 16;
+ *     or chunk 16 (fp32 inputs keep every product at fp32 precision);
  *   - sequential scan: layout, per-chunk factors T = (I + A)^{-1} and
  *     P = (Q K^T) (.) Gamma, then one pass per (sequence, head, block of state
  *     rows) that applies the UT transform and the fixup in factored form
@@ -220,9 +225,10 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v,
 /*
  * gdr_state_fixup -- the inter-chunk fixup alone.
  *
- *   L             [n_chunks, H, dv, dk] fp32 local states
- *   M             [n_chunks, H, dk, dk] fp32 transfer matrices, transposed as
- *                 in gdr_chunk_prefill: M[c][h][b][a] = M_c[a][b]
+ *   L             [n_chunks, H, dv, dk] fp32 local states, L[c][h][i][j] = L_c[i][j]
+ *   M             [n_chunks, H, dk, dk] fp32 transfer matrices in the
+ *                 orientation of the recurrence, M[c][h][a][b] = M_c[a][b]
+ *                 (the same layout as gdr_chunk_prefill's M_out)
  *   state_in      [N, H, dv, dk] fp32, or NULL (no initial state)
  *   chunk_offsets [N+1] int32 device: sequence n owns chunk slots
  *                 [chunk_offsets[n], chunk_offsets[n+1])
@@ -232,11 +238,12 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v,
  *                 fixed[c]  = fixed[c-1] M_c + L_c      (later chunks of n)
  *   n_chunks      slots in L, M and fixed; chunk ids at or past it are ignored
  * The FlashInfer PR #3866 page ("CP delta-rule precompute optimisation for
- * ultra-low parallelism", code changes 2: init_state_tile,
- * accumulate_state_fragment, run_simt_fixup_loop) describes this scan; here it
- * runs one workgroup per (sequence, head, block of state rows) and preloads
- * chunk c+1's M and L while chunk c is accumulated.
- * fixed must not overlap L, M or state_in.
+ * ultra-low parallelism", code changes 2) describes this scan: the state
+ * multiplies M_c from the left, and without an initial state the first chunk's
+ * state is its local state.  Here it runs one workgroup per (sequence, head,
+ * block of state rows) on the matrix cores with the state and M_c split into
+ * three bf16 planes each (fp32 precision), and loads chunk c+1's M and L while
+ * chunk c is multiplied.  fixed must not overlap L, M or state_in.
  */
 gdr_status gdr_state_fixup(const float* L, const float* M, const float* state_in,
                            const int32_t* chunk_offsets, int N, float* fixed,

@@ -54,9 +54,17 @@ def test_max_chunks_and_workspace(lib):
     assert g.gdr_max_chunks(-1, 1, 64) == -1
     assert g.gdr_max_chunks(10, 0, 64) == -1
     mc = g.gdr_max_chunks(16384, 4, 64)
-    ws = g.gdr_chunk_prefill_workspace_bytes(16384, 4, 16, 128, 128, 64)
-    assert ws >= mc * 16 * 128 * 128 * 4 * 3
+    for dt in (g.GDR_BF16, g.GDR_FP32):
+        ws = g.gdr_chunk_prefill_workspace_bytes(16384, 4, 16, 128, 128, 64, dt)
+        # the chunk-parallel form with L, M and fixed in the workspace
+        assert ws >= mc * 16 * 128 * 128 * 4 * 3
     assert g.gdr_chunk_prefill_workspace_bytes(16384, 4, 16, 96, 96, 64) == 0
+    assert g.gdr_chunk_prefill_workspace_bytes(16384, 4, 16, 128, 128, 32) == 0
+    assert lib.gdr_chunk_prefill_workspace_bytes(16384, 4, 16, 128, 128, 64, 7) == 0
+    # the torch dtype of q names the input dtype too
+    import torch
+    assert g.gdr_chunk_prefill_workspace_bytes(100, 1, 2, 64, 64, 16, torch.float32) == \
+        g.gdr_chunk_prefill_workspace_bytes(100, 1, 2, 64, 64, 16, g.GDR_FP32)
 
 
 def _p(x):
@@ -109,10 +117,16 @@ def test_prefill_and_fixup_reject_bad_arguments(lib):
     assert call(cu=None) == 1
     assert call(chunk=32) == 2
     assert call(dk=64, dv=128) == 2
-    assert call(ind=1, chunk=64) == 2       # fp32 inputs need chunk 16
+    assert call(ind=2) == 2                 # no such dtype
     assert call(T=-1) == 1
     assert call(wsb=16) == 1
     assert "workspace" in lib.gdr_last_error().decode()
+    # fp32 inputs are accepted at both chunk sizes: these calls pass every
+    # shape and dtype check and stop at the (too small) workspace, before the
+    # device is touched
+    for chunk in (16, 64):
+        assert call(ind=1, chunk=chunk, wsb=16) == 1
+        assert "workspace" in lib.gdr_last_error().decode()
     assert call(o=_p(0x10002)) == 1
     assert lib.gdr_state_fixup(None, f, None, f, 1, f, 4, 1, 128, 128, None) == 1
     assert lib.gdr_state_fixup(f, f, None, f, 1, f, 4, 1, 64, 128, None) == 2

@@ -101,12 +101,14 @@ def decay_closed_form(d):
 
 # ---- prefill (both schedules) ----
 
-# name: (sequence lengths, H, d, dtype, chunk); fp32 inputs take chunk 16.  The
-# orthogonal-key test clips each length to d.
+# name: (sequence lengths, H, d, dtype, chunk); fp32 inputs take the
+# chunk-parallel form at either chunk size.  The orthogonal-key test clips each
+# length to d.
 PREFILL = {
     "bf16-ragged": ([128, 64, 1, 100, 0, 77], 3, 128, "bf16", 64),
     "bf16-d64": ([64, 30, 65, 129], 2, 64, "bf16", 64),
     "f32-ragged-C16": ([128, 17, 0, 90], 2, 128, "f32", 16),
+    "f32-ragged-C64": ([128, 17, 0, 90], 2, 128, "f32", 64),
 }
 
 
@@ -136,9 +138,9 @@ def test_prefill_identity_steps(name, keep_lm):
     identity_inputs(d)
     o, sout = run_prefill(d, keep_lm, chunk)
     s0 = torch.from_numpy(d["state0"]).cuda()
-    if keep_lm or chunk != 64:
-        # the chunk-parallel schedule (also the one for chunk 16) multiplies by
-        # M = I on bf16 planes: equal to rounding
+    if keep_lm or chunk != 64 or dtype == "f32":
+        # the chunk-parallel schedule (also the one for chunk 16 and fp32
+        # inputs) multiplies by M = I on bf16 planes: equal to rounding
         assert rel_err(host64(sout), d["state0"]) <= tol_for(d)
     else:
         assert torch.equal(sout, s0), "the state must come back unchanged"

@@ -43,8 +43,7 @@ def test_fixup_matches_oracle(with_state, d_, H, lens):
     s0 = d["state0"].astype(np.float64) if with_state else None
     say(f"fixup d={d_} H={H} chunk={chunk} with_state={with_state} n_chunks={L.shape[0]}")
     Lg = torch.from_numpy(L.astype(np.float32)).cuda()
-    # the fixup takes M transposed: slot[c][h][b][a] = M_c[a][b]
-    Mg = torch.from_numpy(np.ascontiguousarray(M.astype(np.float32).transpose(0, 1, 3, 2))).cuda()
+    Mg = torch.from_numpy(M.astype(np.float32)).cuda()  # M[c, h] = M_c as the oracle forms it
     fixed = torch.full_like(Lg, float("nan"))
     sin = torch.from_numpy(d["state0"]).cuda() if with_state else None
     gdr.gdr_state_fixup(Lg, Mg, sin, torch.from_numpy(offs.astype(np.int32)).cuda(), fixed)

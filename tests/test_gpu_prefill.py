@@ -61,8 +61,7 @@ def check_against_oracle(d, res, chunk, check_locals=True):
                             d["state0"])
         n = r2["L"].shape[0]
         errs["L"] = rel_err(host64(res["L"][:n]), r2["L"])
-        # M is stored transposed: slot[c][h][b][a] = M_c[a][b]
-        errs["M"] = rel_err(host64(res["M"][:n].transpose(-1, -2)), r2["M"])
+        errs["M"] = rel_err(host64(res["M"][:n]), r2["M"])
     say(f"  errors: {errs}")
     for key, e in errs.items():
         assert e <= tol, (key, e)
@@ -91,6 +90,18 @@ CASES = {
     # many (sequence, head) pairs: the fixup takes 32 and 64 state rows per workgroup
     "many-heads-H64-rows32": (2, dict(seqlens=[150, 70], H=64, gate="slow")),
     "many-heads-H128-rows64": (2, dict(seqlens=[100], H=128, gate="slow")),
+    # fp32 inputs at chunk 64 (the chunk-parallel form on three bf16 planes per
+    # operand), reduced versions of the prefill, varlen and long workloads:
+    # ragged, empty and length-1 sequences; every gate variant; with and
+    # without an initial state; L and M checked against the chunked oracle
+    "f32-C64-prefill-ragged": (2, dict(seqlens=[256, 130, 1, 0, 64], H=2, dtype="f32")),
+    "f32-C64-prefill-slow-no-state": (2, dict(seqlens=[200, 65], H=2, dtype="f32", gate="slow",
+                                              state0=False)),
+    "f32-C64-varlen-steep": (3, dict(seqlens=[1, 63, 64, 65, 0, 129], H=2, dtype="f32",
+                                     gate="steep")),
+    "f32-C64-varlen-unit": (3, dict(seqlens=[100, 0, 1, 77], H=2, dtype="f32", gate="unit")),
+    "f32-C64-long-slow": (4, dict(seqlens=[4096], H=2, dtype="f32", gate="slow")),
+    "f32-C64-d64": (2, dict(seqlens=[150, 64, 3], H=3, dk=64, dv=64, dtype="f32", gate="slow")),
 }
 
 
@@ -184,6 +195,29 @@ def test_prefill_scan_forms_agree_bitwise():
         c0 = int(np.sum((np.array(lens[:n]) + 63) // 64))
         nc = (b - a + 63) // 64
         assert torch.equal(single["fixed"][:nc], packed["fixed"][c0:c0 + nc])
+
+
+def test_prefill_workspace_on_side_stream():
+    """With no workspace given, the binding allocates one on the launch stream:
+    a prefill on a side stream followed at once by allocations and writes on
+    the current stream gives the same bits as a prefill on the current stream."""
+    d = workload(3, seed=119, seqlens=[300, 1, 64, 129], H=4)
+    say("prefill on a side stream with the binding's own workspace")
+    import gated_delta_rule_100_amd as gdr
+    ref = run_prefill(d, schedule="none")
+    di = dev_inputs(d)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    o = torch.empty_like(ref["o"])
+    sout = torch.empty_like(ref["state_out"])
+    gdr.gdr_chunk_prefill(di["q"], di["k"], di["v"], di["g"], di["beta"], di["cu"], di["state0"],
+                          sout, o, chunk=64, stream=side)
+    junk = [torch.full((1 << 22,), float(i), device="cuda") for i in range(8)]
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    del junk
+    assert torch.equal(o, ref["o"])
+    assert torch.equal(sout, ref["state_out"])
 
 
 def test_prefill_all_sequences_empty():
@@ -303,6 +337,9 @@ def test_split_prefill_resumes():
 # transfer matrices, segment fixup, final pass from the true starts).
 LONG_CASES = {
     "long-T32768-H1-slow": (4, dict(seqlens=[32768], H=1, gate="slow")),
+    # fp32 inputs always take the chunk-parallel form: here its two-level fixup
+    "long-T32768-H1-f32-state": (4, dict(seqlens=[32768], H=1, gate="slow", dtype="f32",
+                                         state0=True)),
     "long-T32768-H1-unit-state": (4, dict(seqlens=[32768], H=1, gate="unit", state0=True)),
     "long-T32768-H1-std-state": (4, dict(seqlens=[32768], H=1, state0=True)),
     "long-varlen-ragged-empty-H1": (4, dict(seqlens=[30000, 0, 19500], H=1, gate="slow",

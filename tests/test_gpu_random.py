@@ -52,3 +52,18 @@ def test_prefill_random_config(seed):
         f"state0={c['state0']} ask={c['schedule']}")
     res = run_prefill(d, schedule=c["schedule"], state_in="given" if c["state0"] else None)
     check_against_oracle(d, res, d["chunk"])
+
+
+@pytest.mark.parametrize("seed", list(range(430, 440)))
+def test_prefill_random_config_f32(seed):
+    """The same draws with fp32 inputs (chunk 64, the chunk-parallel form on
+    three bf16 planes per operand), compared at 1e-5."""
+    c = random_case(seed)
+    if sum(c["lens"]) == 0:
+        c["lens"][0] = 1
+    d = workload(2, seed=seed, seqlens=c["lens"], H=c["H"], dk=c["d"], dv=c["d"],
+                 gate=c["gate"], state0=c["state0"], dtype="f32")
+    say(f"random fp32 prefill seed {seed}: lens={c['lens']} H={c['H']} d={c['d']} "
+        f"gate={c['gate']} state0={c['state0']} ask={c['schedule']}")
+    res = run_prefill(d, schedule=c["schedule"], state_in="given" if c["state0"] else None)
+    check_against_oracle(d, res, d["chunk"])
