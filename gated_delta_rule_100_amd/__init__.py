@@ -25,6 +25,7 @@ __all__ = [
     "gdr_decode_step",
     "gdr_decode_mtp",
     "gdr_chunk_prefill",
+    "gdr_chunk_prefill_noalloc",
     "gdr_chunk_prefill_workspace_bytes",
     "gdr_state_fixup",
     "gdr_chunk_layout",
@@ -71,6 +72,9 @@ def _load():
     lib.gdr_chunk_prefill.argtypes = [P, P, P, P, P, P, I, P, P, P, P, P, P,
                                       I, I, I, I, I, I, I, P, S, P]
     lib.gdr_chunk_prefill.restype = I
+    lib.gdr_chunk_prefill_noalloc.argtypes = [P, P, P, P, P, P, I, P, P, P, P, P, P,
+                                              I, I, I, I, I, I, I, P]
+    lib.gdr_chunk_prefill_noalloc.restype = I
     lib.gdr_state_fixup.argtypes = [P, P, P, P, I, P, I, I, I, I, P]
     lib.gdr_state_fixup.restype = I
     lib.gdr_status_string.argtypes = [I]
@@ -258,6 +262,19 @@ def gdr_chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in, state_out, o, *, c
         *args, _dev_ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(),
         _stream(stream))
     _check(st, "gdr_chunk_prefill")
+
+
+def gdr_chunk_prefill_noalloc(q, k, v, g, beta, cu_seqlens, state_in, state_out, o, *, chunk=64,
+                              L_out=None, M_out=None, fixed_out=None, stream=None) -> None:
+    """gdr_chunk_prefill on the library's static device scratch: no workspace
+    argument and no allocation, for callers that cannot allocate (e.g. under
+    HIP graph capture).  Same arguments and results as gdr_chunk_prefill; a
+    call that needs more than the scratch holds raises GdrError.  Calls that
+    overlap on one device share the scratch and race."""
+    args, _ = _prefill_args(q, k, v, g, beta, cu_seqlens, state_in, state_out, o, chunk, L_out,
+                            M_out, fixed_out, "gdr_chunk_prefill_noalloc")
+    st = _load().gdr_chunk_prefill_noalloc(*args, _stream(stream))
+    _check(st, "gdr_chunk_prefill_noalloc")
 
 
 def gdr_state_fixup(L, M, state_in, chunk_offsets, fixed, stream=None) -> None:

@@ -259,10 +259,15 @@ gdr_status chunk_prefill(const char* who, const void* q, const void* k, const vo
     return fail(GDR_ERR_UNSUPPORTED,
                 "%s: this call needs %zu bytes of scratch and the library's static scratch holds "
                 "%zu; call gdr_chunk_prefill with a workspace instead", who, need, workspace_bytes);
-  if (workspace_bytes < need || (!workspace && need > 0))
+  if (!static_scratch && (workspace_bytes < need || (!workspace && need > 0)))
     return fail(GDR_ERR_INVALID_ARG, "%s: workspace of %zu bytes, need %zu", who, workspace_bytes, need);
-  gdr_status s = check_device();
+  int dev = 0;
+  gdr_status s = check_device(&dev);
   if (s != GDR_OK) return s;
+  if (static_scratch) {
+    s = static_scratch_address(dev, &workspace);
+    if (s != GDR_OK) return s;
+  }
 
   char* ws = static_cast<char*>(workspace);
   int32_t* offs = reinterpret_cast<int32_t*>(ws);

@@ -20,6 +20,10 @@ gdr_status hip_status(hipError_t e, const char* what);
 // and, when `device` is given, stores its id there.
 gdr_status check_device(int* device = nullptr);
 
+// The device address of the library's static scratch (noalloc.hip) on device
+// `device` (the current device), looked up once per device.
+gdr_status static_scratch_address(int device, void** ptr);
+
 // Validation and dispatch of gdr_chunk_prefill (arguments as in gdr.h).  `who`
 // names the entry point in error messages.  With static_scratch the workspace
 // is the library's own scratch array of workspace_bytes bytes, and a call that

@@ -223,6 +223,32 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v,
                              gdr_stream_t stream);
 
 /*
+ * gdr_chunk_prefill_noalloc -- gdr_chunk_prefill without a workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Arguments, layouts, schedules and results are those of gdr_chunk_prefill
+ * (bit for bit: the same kernels run), minus workspace and workspace_bytes.
+ * The workspace is instead a static device array of the library, 128 MiB
+ * (134,217,728 bytes) on each GPU it runs on, held from the first call on that
+ * GPU until the process ends.  A call that needs more than that (see
+ * gdr_chunk_prefill_workspace_bytes; e.g. 4 sequences x 4096 tokens x 16 heads
+ * at d = 128 needs about 107 MB) returns GDR_ERR_UNSUPPORTED with a message
+ * and launches nothing.  Nothing is allocated or freed, here or on later
+ * calls.  All calls on one GPU share its array, which keeps the last call's
+ * contents (no call depends on them): calls that may overlap on one GPU, from
+ * two streams or two threads, race and must be serialised by the caller.
+ */
+gdr_status gdr_chunk_prefill_noalloc(const void* q, const void* k, const void* v,
+                                     const float* g, const float* beta,
+                                     const int32_t* cu_seqlens, int N,
+                                     const float* state_in, float* state_out, void* o,
+                                     float* L_out, float* M_out, float* fixed_out,
+                                     int T_total, int H, int dk, int dv, int chunk,
+                                     gdr_dtype in_dtype, gdr_dtype out_dtype,
+                                     gdr_stream_t stream);
+
+/*
  * gdr_state_fixup -- the inter-chunk fixup alone.
  *
  *   L             [n_chunks, H, dv, dk] fp32 local states, L[c][h][i][j] = L_c[i][j]
