@@ -7,28 +7,45 @@ One step = one pass over both forms of the path on synthetic inputs:
   * prefill: chunked prefill of 4 sequences x 4096 tokens, 16 heads,
              dk = dv = 128, chunk 64, bf16 q/k/v, fp32 gates and states.
 The headline `value` is the decode state bandwidth (state bytes read + written
-per step / decode time); the prefill throughput is reported beside it.  The
-other prefill workloads (varlen: 8 sequences, 32768 tokens, 32 heads; long:
-one 131072-token sequence, 4 heads) are timed after the step, outside it, and
-reported as `prefill_varlen` and `prefill_long`, the prefill workload in the
-chunk-parallel form (the caller asks for every chunk's L and M) as
-`prefill_cp`, and multi-token decode (8 draft tokens per sequence on the decode
-workload's shape) as `decode_mtp`.
+per launch / decode launch time); the prefill throughput is reported beside it.
+Timed after the step, outside it, and reported beside it:
+  * `prefill_varlen`: 8 sequences, 32768 tokens, 32 heads;
+  * `prefill_long`: one 131072-token sequence, 4 heads (segmented scan);
+  * `prefill_cp` / `prefill_long_cp`: the prefill and long workloads with
+    every chunk's L and M returned as well (the chunk-local kernel writes them
+    beside the scan);
+  * `fixup_long`: gdr_state_fixup alone over the long workload's 2048 chunks
+    per head (L and M returned by its prefill): the dependent chain of
+    S_{c+1} = S_c M_c + L_c, reported per step;
+  * `decode_mtp`: multi-token decode (8 draft tokens per sequence on the decode
+    workload's shape).
 
-Decode is measured cold: four state buffers (512 MiB, more than the 256 MB
-Infinity Cache) are used in rotation.  Prefill writes a 1 GiB scrub buffer
-before every timed launch (outside the timed events).  Warm figures (one
-decode state buffer, prefill without the scrub) are reported beside them as
-`warm`, for context (not with --no-other-prefill).  Inputs are resident in HBM
-before timing starts.  Kernel times come from HIP events recorded on the
-stream the kernels are launched on.
+Timing.  HIP events recorded on the launch stream.  A short GPU spin is queued
+before each timed batch, so the host has enqueued the launches before the GPU
+reaches them and they run back to back (host overhead between launches does
+not enter the events).  Prefill figures are the median over per-launch
+durations (two events around each launch).  The decode and multi-token
+kernels (43 and 65 us) are timed as the average launch duration over a region
+of back-to-back launches between two events, because an event pair around
+every launch adds about 1.5 us of marker gap to each; the per-launch median is
+reported beside it.  Decode is cold: four state buffers (512 MiB, more than
+the 256 MB Infinity Cache) in rotation.  Prefill writes a 1 GiB scrub buffer
+before every timed launch (outside its events).  Warm figures (one decode
+state buffer, prefill without the scrub) are reported as `warm`, for context.
+Inputs are resident in HBM before timing starts.
+
+Records.  HBM traffic, instruction mix and per-kernel durations come from
+rocprofv3 runs of this script committed under profiles/ as JSON records; each
+lists the sources it was taken on, and a record is used only while those
+sources are unchanged (else its fields are null).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-other-prefill] [--prefill-only IDX]
+                       [--no-other-prefill] [--only NAME]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -37,7 +54,9 @@ import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+MIN_SAMPLES = 20       # per-launch samples of every figure outside the step
 
 # decode workload: N=64, H=32, d=128
 DEC_N, DEC_H, DEC_D = 64, 32, 128
@@ -59,6 +78,10 @@ PRE_CP_BYTES = PRE_IO_BYTES + PRE_CHUNK_HEADS * 393216
 PRE_FACTOR_W = 12288 + 12288 + 1024
 PRE_FACTOR_R = PRE_FACTOR_W + 2 * 16384
 PRE_SCAN_BYTES = PRE_IO_BYTES + PRE_CHUNK_HEADS * (PRE_FACTOR_W + PRE_FACTOR_R)
+# long workload: one sequence of 131072 tokens, 4 heads: 2048 chunks per head
+LONG_T, LONG_H, LONG_CHUNKS = 131072, 4, 2048
+# one fixup step per (chunk, head): read M_c and L_c, write fixed[c] (64 KiB each)
+FIX_STEP_BYTES = 3 * 128 * 128 * 4
 
 
 def io_min_bytes(idx):
@@ -74,22 +97,40 @@ def io_min_bytes(idx):
     return tokens * H * (3 * D * 2 + D * 2 + 8) + states
 
 
-def parse():
+def cp_form_bytes(idx):
+    """The chunk-parallel form's bytes: the I/O minimum plus L and M written and
+    read once and the chunk-end states written and read once (6 states of
+    64 KiB per chunk-head at d = 128)."""
+    chunk_heads = {2: PRE_CHUNK_HEADS, 4: LONG_CHUNKS * LONG_H}[idx]
+    return io_min_bytes(idx) + chunk_heads * 393216
+
+
+def lm_request_bytes(idx):
+    """Bytes of a bf16 prefill that also returns L and M: the I/O minimum, L and
+    M written once (2 states of 64 KiB per chunk-head), and the scan's chunk
+    factors written and read back with the second read of q and k."""
+    chunk_heads = {2: PRE_CHUNK_HEADS, 4: LONG_CHUNKS * LONG_H}[idx]
+    return io_min_bytes(idx) + chunk_heads * (2 * 65536 + PRE_FACTOR_W + PRE_FACTOR_R)
+
+
+ONLY = ("decode", "prefill", "varlen", "long", "prefill_cp", "long_cp", "fixup_long", "mtp")
+
+
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-prefill", action="store_true",
-                    help="skip timing the varlen and long-sequence prefill workloads and "
-                         "multi-token decode")
+                    help="skip the figures outside the step (other prefill workloads, the "
+                         "chunk-parallel forms, the long fixup chain, multi-token decode, warm)")
     ap.add_argument("--cpu-seconds", type=float, default=16.0,
                     help="approximate CPU time budget of the oracle baseline")
-    ap.add_argument("--prefill-only", type=int, default=None, metavar="IDX",
-                    help="time only the chunked prefill of synthetic workload IDX (2: B=4 T=4096 "
-                         "H=16; 3: varlen 8 sequences 32768 tokens H=32; 4: B=1 T=131072 H=4) and "
-                         "print one JSON line; for per-kernel profiles")
-    return ap.parse_args()
+    ap.add_argument("--only", choices=ONLY, default=None,
+                    help="time only this figure (--steps launches) and print one JSON line; "
+                         "for per-kernel profiles")
+    return ap.parse_args(argv)
 
 
 def to_dev(d, torch):
@@ -103,6 +144,66 @@ def to_dev(d, torch):
     out["state0"] = None if d["state0"] is None else torch.from_numpy(d["state0"]).cuda()
     out["cu"] = torch.from_numpy(d["cu_seqlens"].astype(np.int32)).cuda()
     return out
+
+
+_SPIN = {}
+
+
+def _spin(torch, stream, ms):
+    """Queue about `ms` milliseconds of GPU spinning on `stream` (torch's sleep
+    kernel, calibrated once), so that the launches queued after it run back to
+    back on the GPU."""
+    if "cycles_per_ms" not in _SPIN:
+        try:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            torch.cuda._sleep(1_000_000)
+            e1.record()
+            torch.cuda.synchronize()
+            _SPIN["cycles_per_ms"] = 1_000_000 / max(e0.elapsed_time(e1), 1e-3)
+        except (AttributeError, RuntimeError):
+            _SPIN["cycles_per_ms"] = None
+    if _SPIN["cycles_per_ms"]:
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(int(ms * _SPIN["cycles_per_ms"]))
+
+
+def region(torch, launch, n, stream, lead_ms=None):
+    """n back-to-back launches between two events on `stream`: the average
+    launch duration over the timed region (ms) and the host wall time."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _spin(torch, stream, lead_ms if lead_ms is not None else min(5.0 + 1.0 * n, 60.0))
+    e0.record(stream)
+    for i in range(n):
+        launch(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n, time.perf_counter() - t0
+
+
+def per_launch(torch, launch, n, stream, before=None, lead_ms=None):
+    """n launches, each between two events on `stream`; returns the per-launch
+    durations (ms) and the host wall time.  before(i) runs ahead of launch i,
+    outside its events."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _spin(torch, stream, lead_ms if lead_ms is not None else min(5.0 + 1.0 * n, 60.0))
+    for i in range(n):
+        if before is not None:
+            before(i)
+        ev[i][0].record(stream)
+        launch(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    return dict(ms=float(np.median(ms)), ms_mean=float(np.mean(ms)), ms_min=float(np.min(ms)),
+                ms_max=float(np.max(ms)), n=int(n), wall_s=wall)
 
 
 def bench_decode(torch, gdr, steps, warmup, nbuf=4):
@@ -122,20 +223,10 @@ def bench_decode(torch, gdr, steps, warmup, nbuf=4):
 
     for i in range(warmup):
         launch(i)
-    torch.cuda.synchronize()
-    # back-to-back launches between two events on the launch stream: the
-    # average is the kernel's launch duration over the timed region
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(steps):
-        launch(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / steps
-    return dict(ms_mean=float(ms), wall_s=wall)
+    r = per_launch(torch, launch, steps, stream)
+    r["ms_median"] = r["ms"]
+    r["ms"], r["wall_s"] = region(torch, launch, steps, stream)
+    return r
 
 
 def bench_mtp(torch, gdr, steps, warmup, T=8):
@@ -157,15 +248,11 @@ def bench_mtp(torch, gdr, steps, warmup, T=8):
 
     for i in range(warmup):
         launch(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(steps):
-        launch(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    return dict(ms_mean=float(ms), T=T)
+    r = per_launch(torch, launch, steps, stream)
+    r["ms_median"] = r["ms"]
+    r["ms"], r["wall_s"] = region(torch, launch, steps, stream)
+    r["T"] = T
+    return r
 
 
 def copy_bandwidth(torch, reps=10):
@@ -173,38 +260,33 @@ def copy_bandwidth(torch, reps=10):
     src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     dst.copy_(src)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    s = e0.elapsed_time(e1) / reps / 1e3
+    stream = torch.cuda.current_stream()
+    r = per_launch(torch, lambda i: dst.copy_(src), reps, stream)
     del src, dst
-    return 2 * (1 << 30) / s / 1e9
+    return 2 * (1 << 30) / (r["ms"] / 1e3) / 1e9
 
 
-def recorded_traffic(kernel_file, record):
-    """HBM traffic of the decode kernel from the committed rocprofv3 counter
-    record, if it was taken on the current kernel source (else None)."""
-    import hashlib
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", record)
-    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gated_delta_rule_100_amd",
-                       "csrc", kernel_file)
+def _sha256(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def load_record(name):
+    """A committed profile record (profiles/<name>), or None if it is missing
+    or any source it was taken on has changed since."""
     try:
-        rec = json.load(open(path))
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    except (OSError, ValueError):
+        rec = json.load(open(os.path.join(ROOT, "profiles", name)))
+        for path, digest in rec["sources"].items():
+            if _sha256(os.path.join(ROOT, path)) != digest:
+                return None
+    except (OSError, ValueError, KeyError):
         return None
-    if rec.get("source_sha256") != digest:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
 
 
-def bench_prefill(torch, gdr, steps, warmup, idx=2, cp_form=False, cold=True):
+def bench_prefill(torch, gdr, steps, warmup, idx=2, cp_form=False, cold=True, keep=False):
     """One prefill workload; cold writes a 1 GiB scrub buffer before every timed
-    iteration, warm (cold=False) times back-to-back iterations."""
+    launch, warm (cold=False) times back-to-back launches.  keep returns the
+    device buffers too."""
     from gdr_synth import workload
     d = workload(idx)
     di = to_dev(d, torch)
@@ -216,40 +298,60 @@ def bench_prefill(torch, gdr, steps, warmup, idx=2, cp_form=False, cold=True):
     scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if cold else None  # 1 GiB
     stream = torch.cuda.current_stream()
     L = M = None
-    if cp_form:  # asking for L and M takes the chunk-parallel form
+    if cp_form:  # every chunk's L and M returned as well
         mc = gdr.gdr_max_chunks(T, N, C)
         L = torch.empty(mc, H, D, D, device="cuda")
         M = torch.empty(mc, H, D, D, device="cuda")
 
-    def launch():
+    def launch(i):
         gdr.gdr_chunk_prefill(di["q"], di["k"], di["v"], di["g"], di["beta"], di["cu"],
                               di["state0"], sout, o, chunk=C, L_out=L, M_out=M, workspace=ws,
                               stream=stream)
 
-    for _ in range(warmup):
-        launch()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
+    def before(i):
         if cold:
             scrub.fill_(float(i))
-        ev[i][0].record(stream)
-        launch()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = [a.elapsed_time(b) for a, b in ev]
-    return dict(ms_mean=float(np.mean(ms)), ms_median=float(np.median(ms)),
-                ms_min=float(np.min(ms)), wall_s=wall, workload=d["name"], tokens=T)
+
+    for i in range(warmup):
+        launch(i)
+    r = per_launch(torch, launch, steps, stream, before=before)
+    r.update(workload=d["name"], tokens=T)
+    del scrub, ws
+    if keep:
+        r["buffers"] = dict(d=d, L=L, M=M)
+    return r
+
+
+def bench_fixup_long(torch, gdr, steps, warmup):
+    """gdr_state_fixup alone over the long workload's chunks: L and M of its
+    2048 chunks per head (returned by a prefill) through the chain
+    fixed[c] = fixed[c-1] M_c + L_c, no initial state.  L + M + fixed are
+    1.5 GiB, so every launch is cold."""
+    r0 = bench_prefill(torch, gdr, 1, 1, 4, cp_form=True, cold=False, keep=True)
+    b = r0["buffers"]
+    L, M = b["L"], b["M"]
+    n = LONG_CHUNKS
+    offs = torch.tensor([0, n], dtype=torch.int32, device="cuda")
+    L, M = L[:n].contiguous(), M[:n].contiguous()
+    fixed = torch.empty_like(L)
+    stream = torch.cuda.current_stream()
+
+    def launch(i):
+        gdr.gdr_state_fixup(L, M, None, offs, fixed, stream=stream)
+
+    for i in range(warmup):
+        launch(i)
+    r = per_launch(torch, launch, steps, stream)
+    del L, M, fixed, b
+    return r
 
 
 def cpu_baseline(budget_s):
     """The fp64 oracle (token-by-token recurrence, OpenMP over (sequence, head))
     on the host cores: the whole decode workload repeated for about half the
     budget, and whole 4096-token sequences of the prefill workload (every
-    (sequence, head) pair costs the same) for about the other half."""
+    (sequence, head) pair costs the same) for about the other half; then one
+    (sequence, head) pair of the prefill workload on one thread."""
     import oracle
     from gdr_synth import workload
     threads = oracle.max_threads()
@@ -258,7 +360,7 @@ def cpu_baseline(budget_s):
     t0 = time.perf_counter()
     while True:
         oracle.recurrent(d1["q"], d1["k"], d1["v"], d1["g"], d1["beta"], d1["cu_seqlens"],
-                         d1["state0"])
+                         d1["state0"], threads=threads)
         reps += 1
         if time.perf_counter() - t0 > budget_s / 2 or reps >= 500:
             break
@@ -271,11 +373,15 @@ def cpu_baseline(budget_s):
     while done < len(pairs):
         batch = pairs[done:done + max(threads, 1)]
         oracle.recurrent(d2["q"], d2["k"], d2["v"], d2["g"], d2["beta"], d2["cu_seqlens"],
-                         d2["state0"], pairs=batch)
+                         d2["state0"], pairs=batch, threads=threads)
         done += len(batch)
         if time.perf_counter() - t0 > budget_s / 2:
             break
     pre_s = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.recurrent(d2["q"], d2["k"], d2["v"], d2["g"], d2["beta"], d2["cu_seqlens"],
+                     d2["state0"], pairs=[(0, 0)], threads=1)
+    pair_1t = time.perf_counter() - t0
     return {
         "value": round(DEC_STATE_BYTES / dec_s / 1e9, 3),
         "unit": "GB/s",
@@ -283,8 +389,11 @@ def cpu_baseline(budget_s):
         "kind": "oracle",
         "sample": f"fp64 token-by-token recurrence: the whole decode workload (64x32 states, "
                   f"d=128) {reps} time(s), {dec_s * 1e3:.1f} ms each; prefill: {done} of the 64 "
-                  f"(sequence, head) pairs of 4096 tokens in {pre_s:.1f} s",
+                  f"(sequence, head) pairs of 4096 tokens in {pre_s:.1f} s; one pair on one "
+                  f"thread in {pair_1t:.2f} s",
         "prefill_tokens_per_s": round(done * PRE_T / pre_s / PRE_H, 1),
+        "one_thread_s_per_pair": round(pair_1t, 3),
+        "one_thread_prefill_tokens_per_s": round(PRE_T / pair_1t / PRE_H, 1),
         "cpu": _cpu_model(),
     }
 
@@ -299,91 +408,151 @@ def _cpu_model():
     return platform.processor() or platform.machine()
 
 
-def main():
-    args = parse()
+def _timing(r):
+    """ms: the figure's time (per-launch median, or the region average where
+    ms_median is given: then ms_mean and ms_min are per-launch too)."""
+    out = {"ms": round(r["ms"], 5), "ms_mean": round(r["ms_mean"], 5),
+           "ms_min": round(r["ms_min"], 5), "samples": r["n"]}
+    if "ms_median" in r:
+        out["ms_per_launch_median"] = round(r["ms_median"], 5)
+    return out
+
+
+def prefill_line(r, idx, lm=False):
+    t = r["ms"] / 1e3
+    line = {"workload": r["workload"] + (" with L and M returned" if lm else ""),
+            "value": round(r["tokens"] / t, 1), "unit": "tokens/s", **_timing(r),
+            "io_min_frac": round(io_min_bytes(idx) / t / 1e9 / HBM_PEAK_GBS, 4)}
+    if lm:
+        line["schedule"] = ("chunk-local L and M written in parallel, states and outputs by the "
+                            "factored scan")
+        line["own_bytes_frac"] = round(lm_request_bytes(idx) / t / 1e9 / HBM_PEAK_GBS, 4)
+    return line
+
+
+def prefill_roofline(pre_ms):
+    """The prefill's binding resource from the committed counter record: the
+    scan kernel is a chain of 64 dependent chunk steps per (sequence, head)."""
+    rec = load_record("prefill_B4_T4096_H16_counters.json")
+    out = {"kernel": "chunk_scan_kernel (after chunk_factors_kernel)",
+           "bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "achieved": round(PRE_IO_BYTES / (pre_ms / 1e3) / 1e9, 1),
+           "frac": round(PRE_IO_BYTES / (pre_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+           "algorithmic_bytes": PRE_IO_BYTES,
+           "binding": "latency of the dependent chunk chain (64 steps per sequence and head)",
+           "record": None, "traffic": None}
+    if rec is None:
+        return out
+    out["record"] = "profiles/prefill_B4_T4096_H16_counters.json"
+    out["traffic"] = rec.get("hbm_bytes_per_launch")
+    out["kernels"] = rec.get("kernels")
+    return out
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1:
         print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by sequence and head with no exchange)",
               file=sys.stderr)
         sys.exit(2)
-    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, ROOT)
     import torch
     import gated_delta_rule_100_amd as gdr
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
-    if args.prefill_only is not None:
-        pre = bench_prefill(torch, gdr, args.steps, args.warmup, args.prefill_only)
-        print(json.dumps({"workload": pre["workload"], "prefill_ms": round(pre["ms_mean"], 4),
-                          "tokens_per_s": round(pre["tokens"] / (pre["ms_mean"] / 1e3), 1),
-                          "steps": args.steps, "warmup": args.warmup}))
+    K, W = args.steps, args.warmup
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.only is not None:
+        what = args.only
+        if what == "decode":
+            r = bench_decode(torch, gdr, K, W)
+        elif what == "mtp":
+            r = bench_mtp(torch, gdr, K, W)
+        elif what == "fixup_long":
+            r = bench_fixup_long(torch, gdr, K, W)
+        else:
+            idx = {"prefill": 2, "varlen": 3, "long": 4, "prefill_cp": 2, "long_cp": 4}[what]
+            r = bench_prefill(torch, gdr, K, W, idx, cp_form=what.endswith("_cp"))
+        print(json.dumps({"only": what, **_timing(r), "steps": K, "warmup": W}))
         return
-    print(f"[bench] decode: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
-    dec = bench_decode(torch, gdr, args.steps, args.warmup)
-    print(f"[bench] decode {dec}", file=sys.stderr, flush=True)
-    pre = bench_prefill(torch, gdr, args.steps, args.warmup)
-    print(f"[bench] prefill {pre}", file=sys.stderr, flush=True)
-    # the other prefill workloads, reported beside the step (not part of it)
+
+    log(f"decode: warmup {W}, steps {K}")
+    dec = bench_decode(torch, gdr, K, W)
+    log(f"decode {dec}")
+    pre = bench_prefill(torch, gdr, K, W)
+    log(f"prefill {pre}")
+    # figures outside the step
     others = {}
+    warm = None
     if not args.no_other_prefill:
+        n = max(K, MIN_SAMPLES)
+        w = min(W, 2)
         for idx, key in ((3, "prefill_varlen"), (4, "prefill_long")):
-            r = bench_prefill(torch, gdr, max(3, min(args.steps, 10)), min(args.warmup, 2), idx)
-            print(f"[bench] {key} {r}", file=sys.stderr, flush=True)
-            t = r["ms_mean"] / 1e3
-            others[key] = {"workload": r["workload"], "value": round(r["tokens"] / t, 1),
-                           "unit": "tokens/s", "ms": round(r["ms_mean"], 4),
-                           "io_min_frac": round(io_min_bytes(idx) / t / 1e9 / HBM_PEAK_GBS, 4)}
-        r = bench_prefill(torch, gdr, max(3, min(args.steps, 10)), min(args.warmup, 2), 2,
-                          cp_form=True)
-        print(f"[bench] prefill_cp {r}", file=sys.stderr, flush=True)
-        t = r["ms_mean"] / 1e3
-        others["prefill_cp"] = {
-            "workload": r["workload"] + " (chunk-parallel form: L and M requested)",
-            "value": round(r["tokens"] / t, 1), "unit": "tokens/s", "ms": round(r["ms_mean"], 4),
-            "cp_form_frac": round(PRE_CP_BYTES / t / 1e9 / HBM_PEAK_GBS, 4)}
-        m = bench_mtp(torch, gdr, args.steps, args.warmup)
-        print(f"[bench] decode_mtp {m}", file=sys.stderr, flush=True)
-        t = m["ms_mean"] / 1e3
+            r = bench_prefill(torch, gdr, n, w, idx)
+            log(f"{key} {r}")
+            others[key] = prefill_line(r, idx)
+        for idx, key in ((2, "prefill_cp"), (4, "prefill_long_cp")):
+            r = bench_prefill(torch, gdr, n, w, idx, cp_form=True)
+            log(f"{key} {r}")
+            others[key] = prefill_line(r, idx, lm=True)
+        r = bench_fixup_long(torch, gdr, n, w)
+        log(f"fixup_long {r}")
+        t = r["ms"] / 1e3
+        others["fixup_long"] = {
+            "workload": "gdr_state_fixup over the long workload's L and M: 2048 dependent chunk "
+                        "steps per head, 4 heads, d=128, no initial state",
+            **_timing(r), "us_per_step": round(r["ms"] * 1e3 / LONG_CHUNKS, 3),
+            "hbm_frac": round(LONG_CHUNKS * LONG_H * FIX_STEP_BYTES / t / 1e9 / HBM_PEAK_GBS, 4)}
+        m = bench_mtp(torch, gdr, n, W)
+        log(f"decode_mtp {m}")
+        t = m["ms"] / 1e3
         others["decode_mtp"] = {
             "workload": f"multi-token decode N=64 T={m['T']} H=32 dk=dv=128 bf16, no per-token states",
             "value": round(DEC_STATE_BYTES / t / 1e9, 2), "unit": "state GB/s",
-            "us": round(m["ms_mean"] * 1e3, 2),
+            "us": round(m["ms"] * 1e3, 2), **_timing(m),
             "tokens_per_s": round(DEC_N * m["T"] / t, 1)}
-    # warm figures for context (with the other workloads): decode on one state
-    # buffer, prefill without the scrub
-    warm = None
-    if not args.no_other_prefill:
-        dec_w = bench_decode(torch, gdr, args.steps, args.warmup, nbuf=1)
-        pre_w = bench_prefill(torch, gdr, args.steps, args.warmup, cold=False)
-        print(f"[bench] warm decode {dec_w} prefill {pre_w}", file=sys.stderr, flush=True)
+        # warm figures for context: decode on one state buffer, prefill without the scrub
+        dec_w = bench_decode(torch, gdr, n, W, nbuf=1)
+        pre_w = bench_prefill(torch, gdr, n, W, cold=False)
+        log(f"warm decode {dec_w} prefill {pre_w}")
         warm = {
             "note": "context, not the headline: decode reuses one 128 MiB state buffer (small "
                     "enough for the 256 MB Infinity Cache) and prefill runs back to back "
                     "without the scrub",
-            "decode_ms": round(dec_w["ms_mean"], 5),
-            "decode_state_gbs": round(DEC_STATE_BYTES / (dec_w["ms_mean"] / 1e3) / 1e9, 2),
-            "prefill_ms": round(pre_w["ms_mean"], 5),
-            "prefill_tokens_per_s": round(PRE_TOKENS / (pre_w["ms_mean"] / 1e3), 1),
+            "decode_ms": round(dec_w["ms"], 5),
+            "decode_state_gbs": round(DEC_STATE_BYTES / (dec_w["ms"] / 1e3) / 1e9, 2),
+            "prefill_ms": round(pre_w["ms"], 5),
+            "prefill_tokens_per_s": round(PRE_TOKENS / (pre_w["ms"] / 1e3), 1),
         }
+        long_rec = load_record("prefill_long_T131072_H4_phases.json")
+        if long_rec is not None:
+            others["prefill_long"]["phases_us"] = long_rec.get("phases_us")
+            others["prefill_long"]["phases_record"] = "profiles/prefill_long_T131072_H4_phases.json"
     copy_gbs = copy_bandwidth(torch)
-    print(f"[bench] device copy {copy_gbs:.1f} GB/s", file=sys.stderr, flush=True)
+    log(f"device copy {copy_gbs:.1f} GB/s")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_seconds)
-        print(f"[bench] cpu {cpu}", file=sys.stderr, flush=True)
+        log(f"cpu {cpu}")
 
-    dec_s = dec["ms_mean"] / 1e3
-    pre_s = pre["ms_mean"] / 1e3
+    dec_s = dec["ms"] / 1e3
+    pre_s = pre["ms"] / 1e3
     dec_gbs = DEC_STATE_BYTES / dec_s / 1e9
     achieved = DEC_ALG_BYTES / dec_s / 1e9
+    dec_rec = load_record("decode_N64_H32_d128_traffic.json")
     out = {
         "metric": "GDR decode state GB/s (% HBM peak); chunked-prefill tokens/s at H=16,d=128",
         "value": round(dec_gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(dec["ms_mean"] + pre["ms_mean"], 4),
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(dec["ms"] + pre["ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -393,23 +562,26 @@ def main():
         "config": {"workload": "decode N=64 H=32 dk=dv=128 bf16, state 128 MiB in place "
                                "(cold: 4 rotating buffers) + chunked prefill B=4 T=4096 H=16 "
                                "dk=dv=128 C=64 bf16",
-                   "decode_ms": round(dec["ms_mean"], 5), "prefill_ms": round(pre["ms_mean"], 5)},
+                   "decode_ms": round(dec["ms"], 5), "prefill_ms": round(pre["ms"], 5),
+                   "timing": "decode: average launch duration over the timed region of back-to-"
+                             "back launches (HIP events on the launch stream); prefill: median of "
+                             "per-launch HIP events"},
         "pct_hbm_peak": round(100.0 * dec_gbs / HBM_PEAK_GBS, 2),
         "device_copy_gbs": round(copy_gbs, 1),
+        "decode": _timing(dec),
         "prefill": {
-            "value": round(PRE_TOKENS / pre_s, 1), "unit": "tokens/s",
-            "ms": round(pre["ms_mean"], 4),
+            "value": round(PRE_TOKENS / pre_s, 1), "unit": "tokens/s", **_timing(pre),
             "schedule": "chunk factors + sequential chunk scan (factored fixup)",
             "io_min_frac": round(PRE_IO_BYTES / pre_s / 1e9 / HBM_PEAK_GBS, 4),
             "scan_form_frac": round(PRE_SCAN_BYTES / pre_s / 1e9 / HBM_PEAK_GBS, 4),
-            "cp_form_frac": round(PRE_CP_BYTES / pre_s / 1e9 / HBM_PEAK_GBS, 4),
         },
         "roofline": {
             "bound": "hbm", "kernel": "decode_kernel<128,128,bf16,bf16,2> (32 state rows per workgroup)",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic("decode.hip", "decode_N64_H32_d128_traffic.json"),
+            "traffic": None if dec_rec is None else dec_rec.get("hbm_bytes_per_launch"),
         },
+        "prefill_roofline": prefill_roofline(pre["ms"]),
         "cpu_baseline": cpu,
     }
     if warm is not None:

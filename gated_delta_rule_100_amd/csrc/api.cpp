@@ -145,14 +145,16 @@ size_t scan_workspace(int mc, int H, int chunk) {
 // chunks and runs three scan passes over all segments at once -- local end
 // states from zero, transfer matrices (identity start, v = 0), and the final
 // pass from the true segment starts -- with the segment-level fixup of the
-// chunk-parallel form between them.  The chunk-parallel form (chunk-local L
-// and M, fixup, chunk outputs) serves requests for L or M, fp32 inputs and
+// chunk-parallel form between them.  When the caller asks for L or M, the
+// chunk-local kernel writes them into the caller's buffers in parallel and
+// the chain still runs in factored form (reading 25.6 KB of factors per
+// chunk-head instead of L_c and M_c, 128 KiB).  The chunk-parallel form
+// (chunk-local L and M, dense fixup, chunk outputs) serves fp32 inputs and
 // chunk 16.
 enum Schedule { kChunkParallel = 0, kScan = 1, kSegmentedScan = 2 };
 
-Schedule schedule(const float* L_out, const float* M_out, int T_total, int N, int H, int chunk,
-                  int in_dtype) {
-  if (L_out || M_out || in_dtype != GDR_BF16 || chunk != 64) return kChunkParallel;
+Schedule schedule(int T_total, int N, int H, int chunk, int in_dtype) {
+  if (in_dtype != GDR_BF16 || chunk != 64) return kChunkParallel;
   return fixup_segment(T_total, N, H, chunk) == 0 ? kScan : kSegmentedScan;
 }
 
@@ -236,7 +238,7 @@ gdr_status chunk_prefill(const char* who, const void* q, const void* k, const vo
   // workspace carve-up: offsets | indices | factors [| segments] (sequential
   // scan), or offsets | indices | [L] | [M] | [fixed] | [segments]
   // (chunk-parallel form)
-  const Schedule sched = schedule(L_out, M_out, T_total, N, H, chunk, in_dtype);
+  const Schedule sched = schedule(T_total, N, H, chunk, in_dtype);
   const bool scan = sched != kChunkParallel;
   const size_t per = static_cast<size_t>(mc) * H * sizeof(float);
   size_t need = layout_workspace(N, mc);
@@ -287,6 +289,11 @@ gdr_status chunk_prefill(const char* who, const void* q, const void* k, const vo
     ws += align_up(z.p);
     f.gate = reinterpret_cast<float*>(ws);
     if (T_total > 0) {
+      if (L_out || M_out) {  // requested local states and transfer matrices
+        e = gdr::launch_chunk_local(k, v, g, beta, cu_seqlens, cidx, L_out, M_out, mc, T_total, H,
+                                    dk, dv, chunk, in_dtype, st);
+        if (e != hipSuccess) return hip_fail(e, who, "chunk_local");
+      }
       e = gdr::launch_chunk_factors(q, k, g, beta, cu_seqlens, cidx, f, mc, T_total, H, dk, chunk,
                                     st);
       if (e != hipSuccess) return hip_fail(e, who, "chunk factors");
@@ -488,12 +495,12 @@ size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int 
   cp += align_up(per * dk * dk);  // M
   cp += align_up(per * dv * dk);  // fixed
   cp += seg_workspace(seg_sizes(T_total, N, H, dk, chunk, mc), N);
-  // the scan schedules take bf16 inputs at chunk 64 only
-  const size_t sc = schedule(nullptr, nullptr, T_total, N, H, chunk, in_dtype) != kChunkParallel
-                        ? scan_workspace(mc, H, chunk) +
-                              segscan_workspace(segscan_sizes(T_total, N, H, dk, chunk, mc), N)
-                        : 0;
-  return layout_workspace(N, mc) + (cp > sc ? cp : sc);
+  // bf16 inputs at chunk 64 always take a scan schedule, the others the
+  // chunk-parallel form
+  if (schedule(T_total, N, H, chunk, in_dtype) != kChunkParallel)
+    return layout_workspace(N, mc) + scan_workspace(mc, H, chunk) +
+           segscan_workspace(segscan_sizes(T_total, N, H, dk, chunk, mc), N);
+  return layout_workspace(N, mc) + cp;
 }
 
 gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const float* g,

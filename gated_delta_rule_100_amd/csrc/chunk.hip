@@ -78,7 +78,12 @@ struct ChunkCfg {
   static constexpr int OFF_AOFF = KVW_BYTES;
   static constexpr int OFF_DIAG = OFF_AOFF + AOFF_BYTES;
   static constexpr int OFF_P = OFF_DIAG + NT * DIAG_BLK;
-  static constexpr int OFF_GATE = OFF_P + P_BYTES;
+  // the chunk-local kernel also solves the undecayed system (I + A') W' =
+  // diag(beta) K for M: a second set of A blocks and diagonal inverses
+  static constexpr bool TWO_A = !OUT && !TF;
+  static constexpr int OFF_A2 = OFF_P + P_BYTES;            // A' strictly lower blocks
+  static constexpr int OFF_DIAG2 = OFF_A2 + (TWO_A ? AOFF_BYTES : 0);
+  static constexpr int OFF_GATE = OFF_DIAG2 + (TWO_A ? NT * DIAG_BLK : 0);
   static constexpr int BYTES = OFF_GATE + GATE_BYTES;
   static_assert(D % 64 == 0 && (C == 16 || C == 64), "shape");
 };
@@ -119,14 +124,18 @@ struct ChunkWork {
   __device__ uint16_t* Vr() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_VR); }
   __device__ uint16_t* Wp() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_W); }
   __device__ uint16_t* Tl() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_TL); }
-  __device__ uint16_t* Aoff(int blk) const {
-    return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_AOFF) + blk * PT * Cfg::BLK_PS;
+  // Set 0: A (decayed) and its diagonal inverses; set 1 (chunk-local kernel
+  // only): A'_ts = beta_t (k_t . k_s) without the decay and its inverses.
+  __device__ uint16_t* Aoff(int blk, int set = 0) const {
+    return reinterpret_cast<uint16_t*>(smem + (set ? Cfg::OFF_A2 : Cfg::OFF_AOFF)) +
+           blk * PT * Cfg::BLK_PS;
   }
-  __device__ float* Adiag(int i) const {
-    return reinterpret_cast<float*>(smem + Cfg::OFF_DIAG + i * Cfg::DIAG_BLK);
+  __device__ float* Adiag(int i, int set = 0) const {
+    return reinterpret_cast<float*>(smem + (set ? Cfg::OFF_DIAG2 : Cfg::OFF_DIAG) + i * Cfg::DIAG_BLK);
   }
-  __device__ uint16_t* Tdiag(int i) const {
-    return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_DIAG + i * Cfg::DIAG_BLK);
+  __device__ uint16_t* Tdiag(int i, int set = 0) const {
+    return reinterpret_cast<uint16_t*>(smem + (set ? Cfg::OFF_DIAG2 : Cfg::OFF_DIAG) +
+                                       i * Cfg::DIAG_BLK);
   }
   __device__ uint16_t* Pp() const { return reinterpret_cast<uint16_t*>(smem + Cfg::OFF_P); }
 
@@ -263,23 +272,28 @@ struct ChunkWork {
     *(tid < C ? sb + tid : spare + 1) = bv * keep;
     lds_barrier();  // row loads may stay in flight
     if (tid < C) {
-      // Sequential prefix in a fixed order: every thread forms the same G_C.
-      float G = 0.f, Gt = 0.f;
+      // Sequential prefix in a fixed order, so every thread forms the same
+      // G_C, accumulated in fp64: the decays e^{G} have a relative error equal
+      // to the absolute error of G, and an fp32 prefix over 64 gates carries
+      // about |G| 2^-24 per step (about 1e-5 at G = -55), which would show in
+      // gamma_C and so in M.  gamma and D come from the fp64 sums, rounded once.
+      double G = 0.0, Gt = 0.0;
       for (int s = 0; s < C; ++s) {
-        G += sg[s];
+        G += static_cast<double>(sg[s]);
         if (s == tid) Gt = G;
       }
-      const float gam = expf(Gt);
-      sG[tid] = Gt;
+      const float gam = static_cast<float>(exp(Gt));
+      sG[tid] = static_cast<float>(Gt);
       sgam[tid] = gam;
-      sD[tid] = expf(G - Gt);
+      sD[tid] = static_cast<float>(exp(G - Gt));
       sbg[tid] = sb[tid] * gam;
     }
     lds_barrier();
   }
 
   // A_ts = beta_t Gamma_ts (k_t . k_s), s < t: diagonal blocks in fp32
-  // (zero on and above the diagonal), strictly lower blocks as planes.
+  // (zero on and above the diagonal), strictly lower blocks as planes; in the
+  // chunk-local kernel also A'_ts = beta_t (k_t . k_s) (set 1).
   __device__ void gram_kk(const bf16x8 (&kf)[NT][KB][PI]) {
     int tcount = 0;
 #pragma unroll
@@ -294,15 +308,20 @@ struct ChunkWork {
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g4 + e;
           const int t = 16 * ti + r, s = 16 * tj + c16;
-          const float a = s < t ? sb[t] * expf(sG[t] - sG[s]) * acc[e] : 0.f;
-          if (ti == tj) {
-            Adiag(ti)[r * Cfg::LDA + c16] = a;
-          } else {
-            uint16_t sp[PT];
-            split_planes<PT>(a, sp);
-            uint16_t* blk = Aoff(ti * (ti - 1) / 2 + tj);
+          const float a1 = s < t ? sb[t] * acc[e] : 0.f;
+          const float a = s < t ? a1 * expf(sG[t] - sG[s]) : 0.f;
 #pragma unroll
-            for (int p = 0; p < PT; ++p) blk[p * Cfg::BLK_PS + r * Cfg::LDB + c16] = sp[p];
+          for (int set = 0; set < (Cfg::TWO_A ? 2 : 1); ++set) {
+            const float x = set ? a1 : a;
+            if (ti == tj) {
+              Adiag(ti, set)[r * Cfg::LDA + c16] = x;
+            } else {
+              uint16_t sp[PT];
+              split_planes<PT>(x, sp);
+              uint16_t* blk = Aoff(ti * (ti - 1) / 2 + tj, set);
+#pragma unroll
+              for (int p = 0; p < PT; ++p) blk[p * Cfg::BLK_PS + r * Cfg::LDB + c16] = sp[p];
+            }
           }
         }
       }
@@ -426,11 +445,13 @@ struct ChunkWork {
   }
 
   // T_ii = (I + A_ii)^{-1} for every diagonal block, by substitution in fp32
-  // (wave i, lane j computes column j), stored as planes over A_ii.
+  // (wave i, lane j computes column j; lanes 16 + j do the same for A' in the
+  // chunk-local kernel), stored as planes over A_ii.
   __device__ void invert_diagonal() {
-    if (wave < NT && (tid & 63) < 16) {
-      const int j = tid & 15;
-      const float* A = Adiag(wave);
+    const int lane = tid & 63;
+    if (wave < NT && lane < (Cfg::TWO_A ? 32 : 16)) {
+      const int j = lane & 15, set = lane >> 4;
+      const float* A = Adiag(wave, set);
       float a[16][16];
 #pragma unroll
       for (int t = 1; t < 16; ++t)
@@ -449,7 +470,7 @@ struct ChunkWork {
 #pragma unroll
         for (int t = s + 1; t < 16; ++t) x[t] = fmaf(-a[t][s], x[s], x[t]);
       }
-      uint16_t* T = Tdiag(wave);
+      uint16_t* T = Tdiag(wave, set);
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
         uint16_t sp[PT];
@@ -491,27 +512,35 @@ struct ChunkWork {
     }
   }
 
-  // Block forward substitution, all in this wave's registers:
-  // W = (I + A)^{-1} diag(beta gamma) K and Ut = (I + A)^{-1} diag(beta) V for
-  // the wave's feature tiles.
+  // Block forward substitution, all in this wave's registers, for the wave's
+  // feature tiles:
+  //   Ut = (I + A)^{-1} diag(beta) V, and
+  //   W  = (I + A)^{-1} diag(beta gamma) K      (PRIME = false), or
+  //   W' = (I + A')^{-1} diag(beta) K           (PRIME = true; A' undecayed, set 1)
+  // where W = diag(gamma) W'.
+  template <bool PRIME>
   __device__ void solve_wy(floatx4 (&Wacc)[NT][DPW], floatx4 (&Uacc)[NT][DPW]) const {
+    constexpr int WS = PRIME ? 1 : 0;  // block set of the W system
+    static_assert(!PRIME || Cfg::TWO_A, "the undecayed system needs the second block set");
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      shortx4 tii[PT];
+      shortx4 tii[PT], tiw[PT];
       load_lds4<PT>(Tdiag(i) + c16 * Cfg::LDB + 4 * g4, Cfg::BLK_PS, tii);
+      load_lds4<PT>(Tdiag(i, WS) + c16 * Cfg::LDB + 4 * g4, Cfg::BLK_PS, tiw);
 #pragma unroll
       for (int bb = 0; bb < DPW; ++bb) {
         const int b = wave + 4 * bb;
-        floatx4 rw = rhs(Kr(), sbg, i, b);
+        floatx4 rw = rhs(Kr(), PRIME ? sb : sbg, i, b);
         floatx4 ru = rhs(Vr(), sb, i, b);
         floatx4 sw = {0.f, 0.f, 0.f, 0.f}, su = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < i; ++j) {
-          shortx4 aij[PT], xw[PT], xu[PT];
+          shortx4 aij[PT], awj[PT], xw[PT], xu[PT];
           load_lds4<PT>(Aoff(i * (i - 1) / 2 + j) + c16 * Cfg::LDB + 4 * g4, Cfg::BLK_PS, aij);
+          load_lds4<PT>(Aoff(i * (i - 1) / 2 + j, WS) + c16 * Cfg::LDB + 4 * g4, Cfg::BLK_PS, awj);
           split4<PT>(Wacc[j][bb], xw);
           split4<PT>(Uacc[j][bb], xu);
-          mma16_planes<PT, PT>(sw, aij, xw);
+          mma16_planes<PT, PT>(sw, awj, xw);
           mma16_planes<PT, PT>(su, aij, xu);
         }
         rw -= sw;
@@ -520,7 +549,7 @@ struct ChunkWork {
         split4<PT>(rw, pw);
         split4<PT>(ru, pu);
         floatx4 w = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
-        mma16_planes<PT, PT>(w, tii, pw);
+        mma16_planes<PT, PT>(w, tiw, pw);
         mma16_planes<PT, PT>(u, tii, pu);
         Wacc[i][bb] = w;
         Uacc[i][bb] = u;
@@ -642,10 +671,17 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
   w.invert_diagonal();
 
   floatx4 Wacc[Cfg::NT][Cfg::DPW], Uacc[Cfg::NT][Cfg::DPW];
-  w.solve_wy(Wacc, Uacc);
+  w.template solve_wy<true>(Wacc, Uacc);
 
-  // L = Ut^T diag(D) K and M = gamma_C I - W^T diag(D) K, rows of this wave's
-  // feature tiles (16 lanes store 64 contiguous bytes of a row).
+  // L = Ut^T diag(D) K and M = gamma_C I - W^T diag(D) K = gamma_C (I - W'^T K)
+  // (W^T diag(D) = W'^T diag(gamma_t D_t) and gamma_t D_t = gamma_C: the decays
+  // are scalars and factor out of the transfer matrix, which is
+  // gamma_C prod_t (I - beta_t k_t k_t^T)).  Forming M from the undecayed W'
+  // keeps every operand of order one, so M keeps fp32 precision when gamma_C
+  // is near the bottom of the fp32 range (operands of that size would have
+  // their last bf16 plane below the normal range, where the matrix cores
+  // flush it).  Rows of this wave's feature tiles; 16 lanes store 64
+  // contiguous bytes of a row.
   const float gam_end = w.sgam[C - 1];
   const size_t base = (static_cast<size_t>(cid) * H + h) * D * D;
 #pragma unroll
@@ -655,7 +691,7 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
 #pragma unroll
     for (int kb = 0; kb < Cfg::CB; ++kb) {
       w.template tile_frag<true>(Uacc, bb, kb, AU[kb]);
-      w.template tile_frag<true>(Wacc, bb, kb, AW[kb]);
+      w.template tile_frag<false>(Wacc, bb, kb, AW[kb]);
     }
     for (int bj = 0; bj < Cfg::ND; ++bj) {
       floatx4 l = {0.f, 0.f, 0.f, 0.f}, m = {0.f, 0.f, 0.f, 0.f};
@@ -670,8 +706,8 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const size_t at = base + static_cast<size_t>(i0 + e) * D + j;
-        Lout[at] = l[e];
-        Mout[at] = (i0 + e == j ? gam_end : 0.f) - m[e];
+        if (Lout) Lout[at] = l[e];
+        if (Mout) Mout[at] = gam_end * ((i0 + e == j ? 1.f : 0.f) - m[e]);
       }
     }
   }
@@ -723,7 +759,7 @@ __global__ __launch_bounds__(256, 2) void chunk_out_kernel(
   w.invert_diagonal();
 
   floatx4 Wacc[NT][DPW], Uacc[NT][DPW];
-  w.solve_wy(Wacc, Uacc);
+  w.template solve_wy<false>(Wacc, Uacc);
   __syncthreads();  // K and V are consumed; W planes take their place
 
 #pragma unroll

@@ -136,14 +136,16 @@ __global__ __launch_bounds__(D * 4) void fixup_mfma_kernel(
         l[r][e] = trans_rows ? 0.f : L[st_at(c, 16 * r + 4 * g4 + e, col)];
   };
 
-  // Raw operands of chunk c+1 are loaded at the top of iteration c and turned
-  // into planes at its end, after the barrier: the loaded registers never
-  // cross the loop back-edge, so nothing has to wait for them early.
-  MRaw m;
-  LRaw l;
+  // Raw operands run two chunks ahead: the loads of chunk c+2 are issued at
+  // the top of step c (into the registers chunk c's operands were loaded into,
+  // already converted), and chunk c+1's, loaded during step c-1, become
+  // planes at the end of step c, after the barrier.  Loaded registers never
+  // cross a loop back-edge unconverted, so nothing waits for a load early.
+  MRaw ma, mb_raw;
+  LRaw la, lb;
   bf16x8 mb[KB][P];
   float lc[RT][4];
-  auto convert = [&]() {
+  auto convert = [&](const MRaw& m, const LRaw& l) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) split8<P>(m[kb], mb[kb]);
 #pragma unroll
@@ -151,12 +153,15 @@ __global__ __launch_bounds__(D * 4) void fixup_mfma_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) lc[r][e] = l[r][e];
   };
-  fetch(start, m, l);
-  convert();
+  fetch(start, ma, la);
+  fetch(start + 1, mb_raw, lb);
+  convert(ma, la);
   int buf = 0;
   float last[RT][4] = {};
-  for (int c = start; c < c_end; ++c) {
-    fetch(c + 1, m, l);  // next chunk's operands are in flight during this one
+  // One chunk step: S' = S M_c + L_c from the planes of buffer `buf`; mf, lf
+  // receive chunk c+2's operands, mc, lcr (chunk c+1's) are converted last.
+  auto step = [&](int c, MRaw& mf, LRaw& lf, const MRaw& mc, const LRaw& lcr) {
+    fetch(c + 2, mf, lf);
 
     // S' tiles = S M_c: two accumulators per tile (even / odd k blocks) keep
     // the dependent MFMA chains short.
@@ -189,8 +194,15 @@ __global__ __launch_bounds__(D * 4) void fixup_mfma_kernel(
       }
     }
     buf ^= 1;
-    __syncthreads();
-    convert();
+    // The new rows are in LDS for every wave; global loads (the next chunks'
+    // operands) and stores (fixed[c]) stay in flight: __syncthreads() would
+    // drain them and expose a memory round trip per chunk.
+    lds_barrier();
+    convert(mc, lcr);
+  };
+  for (int c = start; c < c_end; c += 2) {
+    step(c, ma, la, mb_raw, lb);
+    if (c + 1 < c_end) step(c + 1, mb_raw, lb, ma, la);
   }
 
   if (MODE == kCompose) {

@@ -44,7 +44,8 @@ hipError_t launch_fixup_mode(int mode, const float* L, const float* M, const flo
                              const float* seg_start, float* out, float* out_m, int n_chunks,
                              int H, int n_units, int dk, int planes, hipStream_t stream);
 
-// Chunk-local precompute: L_c and M_c for every chunk slot < max_chunks.
+// Chunk-local precompute: L_c and M_c for every chunk slot < max_chunks (L or
+// M may be NULL: not stored).
 hipError_t launch_chunk_local(const void* k, const void* v, const float* g, const float* beta,
                               const int32_t* cu_seqlens, const int32_t* chunk_indices,
                               float* L, float* M, int max_chunks, int T_total, int H, int dk,

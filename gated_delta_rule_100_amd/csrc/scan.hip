@@ -342,296 +342,308 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
   }
 
   // ---- compute waves ----
-  // Wave (rt, hp): state rows 16 rt .. 16 rt + 15 of this workgroup's block,
-  // column tiles hp JT .. hp JT + JT - 1.
-  const int rt = wave / NH, hp = wave % NH;
-  const int vrow = Cfg::ROWS * vb + 16 * rt + c16;  // state row held by this lane
-  const int jt0 = hp * JT;                          // first column tile held
-  const size_t sbase = (static_cast<size_t>(n) * H + h) * D * D + static_cast<size_t>(vrow) * D;
-  floatx4 S[JT];
+  // The column half hp is a compile-time constant of each instantiation, so
+  // that the choice of output tiles and exchange slots costs no instructions.
+  auto compute_waves = [&](auto hpc) {
+    // Wave (rt, hp): state rows 16 rt .. 16 rt + 15 of this workgroup's
+    // block, column tiles hp JT .. hp JT + JT - 1.
+    constexpr int hp = decltype(hpc)::value;
+    const int rt = wave / NH;
+    const int vrow = Cfg::ROWS * vb + 16 * rt + c16;  // state row held by this lane
+    const int jt0 = hp * JT;                          // first column tile held
+    const size_t sbase = (static_cast<size_t>(n) * H + h) * D * D + static_cast<size_t>(vrow) * D;
+    floatx4 S[JT];
 #pragma unroll
-  for (int jl = 0; jl < JT; ++jl) {
-    const int jt = jt0 + jl;
-    if (flags & kScanIdentityStart) {
+    for (int jl = 0; jl < JT; ++jl) {
+      const int jt = jt0 + jl;
+      if (flags & kScanIdentityStart) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[jl][e] = vrow == 16 * jt + 4 * g4 + e ? 1.f : 0.f;
-    } else {
-      S[jl] = state_in ? *reinterpret_cast<const floatx4*>(state_in + sbase + 16 * jt + 4 * g4)
-                       : floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < 4; ++e) S[jl][e] = vrow == 16 * jt + 4 * g4 + e ? 1.f : 0.f;
+      } else {
+        S[jl] = state_in ? *reinterpret_cast<const floatx4*>(state_in + sbase + 16 * jt + 4 * g4)
+                         : floatx4{0.f, 0.f, 0.f, 0.f};
+      }
     }
-  }
-  // Output token tiles of this wave: all of them when NH = 1; with NH = 2 the
-  // column halves split them so that each does three 32-deep blocks of
-  // U^T P^T: half 0 takes tiles 0 and 3, half 1 tiles 1 and 2 (tile a needs
-  // blocks kb <= a / 2; four token tiles, C = 64).  Tile u of half x (NH = 2):
-  auto otile = [](int x, int u) { return u == 0 ? x : 3 - x; };
-  float* xch = reinterpret_cast<float*>(smem + Cfg::OFF_X);
-  auto xslot = [&](int w, int x) {
-    return reinterpret_cast<floatx4*>(xch) + (x * kComputeWaves + w) * 64 + lane;
-  };
+    // Output token tiles of this wave: all of them when NH = 1; with NH = 2 the
+    // column halves split them so that each does three 32-deep blocks of
+    // U^T P^T: half 0 takes tiles 0 and 3, half 1 tiles 1 and 2 (tile a needs
+    // blocks kb <= a / 2; four token tiles, C = 64).  Tile u of half x (NH = 2):
+    auto otile = [](int x, int u) { return u == 0 ? x : 3 - x; };
+    float* xch = reinterpret_cast<float*>(smem + Cfg::OFF_X);
+    auto xslot = [&](int w, int x) {
+      return reinterpret_cast<floatx4*>(xch) + (x * kComputeWaves + w) * 64 + lane;
+    };
 
-  if (c1 > c0) {
-    // The state registers are carried through the loop: drain their loads
-    // here, or a wait for them inside the loop would also wait for later
-    // stores on every iteration.
-    __builtin_amdgcn_s_waitcnt(0);
-    bare_barrier();  // B0: chunk c0 is in LDS
+    if (c1 > c0) {
+      // The state registers are carried through the loop: drain their loads
+      // here, or a wait for them inside the loop would also wait for later
+      // stores on every iteration.
+      __builtin_amdgcn_s_waitcnt(0);
+      bare_barrier();  // B0: chunk c0 is in LDS
 
-    // One chunk step; the chunk buffer is a compile-time constant (chunk s of
-    // the sequence sits in buffer (s - c0) & 1), so that each of the two
-    // copies of the step below reads LDS at loop-invariant addresses.
-    auto step = [&](int s, auto bsel) {
-      using B = decltype(bsel);
-      const unsigned char* buf = smem + B::value * Cfg::BUF;
-      const uint16_t* Kl = reinterpret_cast<const uint16_t*>(buf + Cfg::OFF_K);
-      const uint16_t* Ql = reinterpret_cast<const uint16_t*>(buf + Cfg::OFF_Q);
-      const uint16_t* Tl = reinterpret_cast<const uint16_t*>(buf + Cfg::OFF_T);
-      const uint16_t* Pl = reinterpret_cast<const uint16_t*>(buf + Cfg::OFF_P);
-      const uint16_t* Vl = reinterpret_cast<const uint16_t*>(buf + Cfg::OFF_V);
-      const float* Gl = reinterpret_cast<const float*>(buf + Cfg::OFF_G);
+      // One chunk step; the chunk buffer is a compile-time constant (chunk s of
+      // the sequence sits in buffer (s - c0) & 1), so that each of the two
+      // copies of the step below reads LDS at loop-invariant addresses.
+      auto step = [&](int s, auto bsel) {
+        using B = decltype(bsel);
+        const unsigned char* buf = smem + B::value * Cfg::BUF;
+        const uint16_t* Kl = reinterpret_cast<const uint16_t*>(buf + Cfg::OFF_K);
+        const uint16_t* Ql = reinterpret_cast<const uint16_t*>(buf + Cfg::OFF_Q);
+        const uint16_t* Tl = reinterpret_cast<const uint16_t*>(buf + Cfg::OFF_T);
+        const uint16_t* Pl = reinterpret_cast<const uint16_t*>(buf + Cfg::OFF_P);
+        const uint16_t* Vl = reinterpret_cast<const uint16_t*>(buf + Cfg::OFF_V);
+        const float* Gl = reinterpret_cast<const float*>(buf + Cfg::OFF_G);
 
-      // Z = K S^T (rows: tokens) and Y^T = S Q^T (rows: state rows), as the
-      // sum of two partial contractions over the column halves of S (the
-      // 32-deep blocks kb < KH, then kb >= KH), which are added last.  S^T
-      // enters as operand planes in natural order (lane group g holds columns
-      // 32 kb + 8 g .. +7): the two stacked D tiles are split, then regrouped
-      // with permlane swaps.  The 16x16x32 A and B fragments have the same
-      // lane layout, so these registers serve as B (rows of S^T) in K S^T and
-      // as A (rows of S) in S Q^T.
-      constexpr int NCH = 2 / NH;  // column halves contracted by this wave
-      floatx4 Zh[NCH][NT], Yh[NCH][NT];
+        // Z = K S^T (rows: tokens) and Y^T = S Q^T (rows: state rows), as the
+        // sum of two partial contractions over the column halves of S (the
+        // 32-deep blocks kb < KH, then kb >= KH), which are added last.  S^T
+        // enters as operand planes in natural order (lane group g holds columns
+        // 32 kb + 8 g .. +7): the two stacked D tiles are split, then regrouped
+        // with permlane swaps.  The 16x16x32 A and B fragments have the same
+        // lane layout, so these registers serve as B (rows of S^T) in K S^T and
+        // as A (rows of S) in S Q^T.
+        constexpr int NCH = 2 / NH;  // column halves contracted by this wave
+        floatx4 Zh[NCH][NT], Yh[NCH][NT];
 #pragma unroll
-      for (int hc = 0; hc < NCH; ++hc) {
-#pragma unroll
-        for (int a = 0; a < NT; ++a) {
-          Zh[hc][a] = floatx4{0.f, 0.f, 0.f, 0.f};
-          if constexpr (OUT) Yh[hc][a] = floatx4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int kl = 0; kl < KH; ++kl) {
-          const int kbl = hc * KH + kl;  // block among this wave's columns
-          const int kb = hp * (KB / NH) + kbl;
-          bf16x8 sbk[2];
-          {
-            float x[8];
-#pragma unroll
-            for (int e2 = 0; e2 < 8; ++e2) x[e2] = S[2 * kbl + e2 / 4][e2 & 3];
-            split8<2>(x, sbk);
-#pragma unroll
-            for (int p = 0; p < 2; ++p) sbk[p] = slot_to_natural(sbk[p]);
-          }
-          bf16x8 ka[NT], qa[NT];
+        for (int hc = 0; hc < NCH; ++hc) {
 #pragma unroll
           for (int a = 0; a < NT; ++a) {
-            const int t = 16 * a + c16, n8 = 4 * kb + g4;
-            ka[a] = *reinterpret_cast<const bf16x8*>(Kl + t * D + 8 * (n8 ^ swz_tr(t, CHD)));
-            if constexpr (OUT)
-              qa[a] = *reinterpret_cast<const bf16x8*>(Ql + t * D + 8 * (n8 ^ swz(t, CHD)));
+            Zh[hc][a] = floatx4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (OUT) Yh[hc][a] = floatx4{0.f, 0.f, 0.f, 0.f};
           }
-          // plane pairs, smallest terms first; the four token tiles are
-          // interleaved so that consecutive products are independent
 #pragma unroll
-          for (int a = 0; a < NT; ++a) Zh[hc][a] = mfma16x16x32(ka[a], sbk[1], Zh[hc][a]);
+          for (int kl = 0; kl < KH; ++kl) {
+            const int kbl = hc * KH + kl;  // block among this wave's columns
+            const int kb = hp * (KB / NH) + kbl;
+            bf16x8 sbk[2];
+            {
+              float x[8];
 #pragma unroll
-          for (int a = 0; a < NT; ++a) Zh[hc][a] = mfma16x16x32(ka[a], sbk[0], Zh[hc][a]);
+              for (int e2 = 0; e2 < 8; ++e2) x[e2] = S[2 * kbl + e2 / 4][e2 & 3];
+              split8<2>(x, sbk);
+#pragma unroll
+              for (int p = 0; p < 2; ++p) sbk[p] = slot_to_natural(sbk[p]);
+            }
+            bf16x8 ka[NT], qa[NT];
+#pragma unroll
+            for (int a = 0; a < NT; ++a) {
+              const int t = 16 * a + c16, n8 = 4 * kb + g4;
+              ka[a] = *reinterpret_cast<const bf16x8*>(Kl + t * D + 8 * (n8 ^ swz_tr(t, CHD)));
+              if constexpr (OUT)
+                qa[a] = *reinterpret_cast<const bf16x8*>(Ql + t * D + 8 * (n8 ^ swz(t, CHD)));
+            }
+            // plane pairs, smallest terms first; the four token tiles are
+            // interleaved so that consecutive products are independent
+#pragma unroll
+            for (int a = 0; a < NT; ++a) Zh[hc][a] = mfma16x16x32(ka[a], sbk[1], Zh[hc][a]);
+#pragma unroll
+            for (int a = 0; a < NT; ++a) Zh[hc][a] = mfma16x16x32(ka[a], sbk[0], Zh[hc][a]);
+            if constexpr (OUT) {
+#pragma unroll
+              for (int a = 0; a < NT; ++a) Yh[hc][a] = mfma16x16x32(sbk[1], qa[a], Yh[hc][a]);
+#pragma unroll
+              for (int a = 0; a < NT; ++a) Yh[hc][a] = mfma16x16x32(sbk[0], qa[a], Yh[hc][a]);
+            }
+          }
+        }
+        floatx4 Z[NT], Yo[NO];  // Yo: Y^T of this wave's output tiles
+        if constexpr (NH == 1) {
+#pragma unroll
+          for (int a = 0; a < NT; ++a) {
+            Z[a] = Zh[0][a] + Zh[1][a];
+            if constexpr (OUT) Yo[a] = Yh[0][a] + Yh[1][a];
+          }
+        } else {
+          // exchange with the wave holding the other column half (wave ^ 1):
+          // all of its partial Z, and its partial Y^T of this wave's tiles
+#pragma unroll
+          for (int a = 0; a < NT; ++a) *xslot(wave, a) = Zh[0][a];
           if constexpr (OUT) {
 #pragma unroll
-            for (int a = 0; a < NT; ++a) Yh[hc][a] = mfma16x16x32(sbk[1], qa[a], Yh[hc][a]);
+            for (int u = 0; u < NO; ++u) {
+              const int ap = otile(1 - hp, u);  // the partner's tile u
+              floatx4 y = Yh[0][0];
 #pragma unroll
-            for (int a = 0; a < NT; ++a) Yh[hc][a] = mfma16x16x32(sbk[0], qa[a], Yh[hc][a]);
+              for (int a = 1; a < NT; ++a) y = ap == a ? Yh[0][a] : y;
+              *xslot(wave, NT + u) = y;
+            }
+          }
+          // the LDS writes above must be complete before the barrier (gfx950
+          // does not wait for them at s_barrier)
+          lds_barrier();  // exchange written
+#pragma unroll
+          for (int a = 0; a < NT; ++a) Z[a] = Zh[0][a] + *xslot(wave ^ 1, a);
+          if constexpr (OUT) {
+#pragma unroll
+            for (int u = 0; u < NO; ++u) {
+              const int am = otile(hp, u);
+              floatx4 y = Yh[0][0];
+#pragma unroll
+              for (int a = 1; a < NT; ++a) y = am == a ? Yh[0][a] : y;
+              Yo[u] = y + *xslot(wave ^ 1, NT + u);
+            }
           }
         }
-      }
-      floatx4 Z[NT], Yo[NO];  // Yo: Y^T of this wave's output tiles
-      if constexpr (NH == 1) {
+
+        // R = diag(beta) (V - diag(gamma) Z) (v rows 16 a + 4 g + e at this
+        // lane's state row: a transpose read), as operand planes of 32 tokens
+        // (two stacked D tiles, slot order), then U = T R over the lower blocks:
+        // T rows are stored in slot order, so the T fragment of row 16 i + c and
+        // 32-block m is one 16-byte read per plane.  Both column halves form
+        // the same R and U.
+        floatx4 R[NT];
 #pragma unroll
         for (int a = 0; a < NT; ++a) {
-          Z[a] = Zh[0][a] + Zh[1][a];
-          if constexpr (OUT) Yo[a] = Yh[0][a] + Yh[1][a];
+          const floatx4 gam = *reinterpret_cast<const floatx4*>(Gl + 16 * a + 4 * g4);
+          const floatx4 bet = *reinterpret_cast<const floatx4*>(Gl + 2 * C + 16 * a + 4 * g4);
+          const shortx4 vv = v ? read_tr4(Vl, Cfg::ROWS, CHV, 16 * a, 16 * rt, c16, g4)
+                               : shortx4{0, 0, 0, 0};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            R[a][e] = bet[e] * (bf16_bits_to_f32(static_cast<uint16_t>(vv[e])) - gam[e] * Z[a][e]);
         }
-      } else {
-        // exchange with the wave holding the other column half (wave ^ 1):
-        // all of its partial Z, and its partial Y^T of this wave's tiles
+        bf16x8 rb[CB][2];
 #pragma unroll
-        for (int a = 0; a < NT; ++a) *xslot(wave, a) = Zh[0][a];
-        if constexpr (OUT) {
+        for (int m = 0; m < CB; ++m) {
+          float x[8];
 #pragma unroll
-          for (int u = 0; u < NO; ++u) {
-            const int ap = otile(1 - hp, u);  // the partner's tile u
-            floatx4 y = Yh[0][0];
-#pragma unroll
-            for (int a = 1; a < NT; ++a) y = ap == a ? Yh[0][a] : y;
-            *xslot(wave, NT + u) = y;
-          }
+          for (int e2 = 0; e2 < 8; ++e2) x[e2] = R[2 * m + e2 / 4][e2 & 3];
+          split8<2>(x, rb[m]);
         }
-        // the LDS writes above must be complete before the barrier (gfx950
-        // does not wait for them at s_barrier)
-        lds_barrier();  // exchange written
+        floatx4 U[NT];
 #pragma unroll
-        for (int a = 0; a < NT; ++a) Z[a] = Zh[0][a] + *xslot(wave ^ 1, a);
-        if constexpr (OUT) {
+        for (int i = 0; i < NT; ++i) {
+          const int t = 16 * i + c16, ch = t < C / 2 ? CHC / 2 : CHC;
+          U[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int u = 0; u < NO; ++u) {
-            const int am = otile(hp, u);
-            floatx4 y = Yh[0][0];
-#pragma unroll
-            for (int a = 1; a < NT; ++a) y = am == a ? Yh[0][a] : y;
-            Yo[u] = y + *xslot(wave ^ 1, NT + u);
-          }
-        }
-      }
-
-      // R = diag(beta) (V - diag(gamma) Z) (v rows 16 a + 4 g + e at this
-      // lane's state row: a transpose read), as operand planes of 32 tokens
-      // (two stacked D tiles, slot order), then U = T R over the lower blocks:
-      // T rows are stored in slot order, so the T fragment of row 16 i + c and
-      // 32-block m is one 16-byte read per plane.  Both column halves form
-      // the same R and U.
-      floatx4 R[NT];
-#pragma unroll
-      for (int a = 0; a < NT; ++a) {
-        const floatx4 gam = *reinterpret_cast<const floatx4*>(Gl + 16 * a + 4 * g4);
-        const floatx4 bet = *reinterpret_cast<const floatx4*>(Gl + 2 * C + 16 * a + 4 * g4);
-        const shortx4 vv = v ? read_tr4(Vl, Cfg::ROWS, CHV, 16 * a, 16 * rt, c16, g4)
-                             : shortx4{0, 0, 0, 0};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          R[a][e] = bet[e] * (bf16_bits_to_f32(static_cast<uint16_t>(vv[e])) - gam[e] * Z[a][e]);
-      }
-      bf16x8 rb[CB][2];
-#pragma unroll
-      for (int m = 0; m < CB; ++m) {
-        float x[8];
-#pragma unroll
-        for (int e2 = 0; e2 < 8; ++e2) x[e2] = R[2 * m + e2 / 4][e2 & 3];
-        split8<2>(x, rb[m]);
-      }
-      floatx4 U[NT];
-#pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        const int t = 16 * i + c16, ch = t < C / 2 ? CHC / 2 : CHC;
-        U[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m <= i / 2; ++m) {
-          bf16x8 tf[2];
-#pragma unroll
-          for (int p = 0; p < 2; ++p)
-            tf[p] = *reinterpret_cast<const bf16x8*>(Tl + p * TL + tl_row<C>(t) +
-                                                     8 * ((4 * m + g4) ^ swz(t, ch)));
-          U[i] = mfma16x16x32(tf[1], rb[m][0], U[i]);
-          U[i] = mfma16x16x32(tf[0], rb[m][1], U[i]);
-          U[i] = mfma16x16x32(tf[0], rb[m][0], U[i]);
-        }
-      }
-
-      // U as operand planes (32 tokens per block, slot order), plain and
-      // scaled by D.
-      bf16x8 ub[CB][2], udb[CB][2];
-#pragma unroll
-      for (int kb = 0; kb < CB; ++kb) {
-        float x[8], xd[8];
-#pragma unroll
-        for (int e2 = 0; e2 < 8; ++e2) {
-          const int a0 = 2 * kb + e2 / 4, e = e2 & 3;
-          x[e2] = U[a0][e];
-          xd[e2] = Gl[C + 16 * a0 + 4 * g4 + e] * U[a0][e];
-        }
-        if constexpr (OUT) split8<2>(x, ub[kb]);
-        split8<2>(xd, udb[kb]);
-      }
-
-      if constexpr (OUT) {
-        // O^T = Y^T diag(gamma) + U^T P^T for this wave's token tiles: lane
-        // (c, g) ends up with token 16 a + c and state rows 4 g .. 4 g + 3 of
-        // its row tile.  P is zero above the diagonal, so token tile a needs
-        // the 32-blocks kb <= a / 2.
-        floatx4 oa[NO];
-        int at[NO];
-#pragma unroll
-        for (int u = 0; u < NO; ++u) {
-          at[u] = NH == 1 ? u : otile(hp, u);
-          oa[u] = Yo[u] * Gl[16 * at[u] + c16];
-        }
-#pragma unroll
-        for (int kb = 0; kb < CB; ++kb) {
-          // tiles with a / 2 >= kb: NH = 1: a >= 2 kb; NH = 2: u >= kb
-          bf16x8 pa[NO][2];
-#pragma unroll
-          for (int u = 0; u < NO; ++u) {
-            if (NH == 1 ? u < 2 * kb : u < kb) continue;
-            const int t = 16 * at[u] + c16;
-            const int ch = (NH == 1 ? u < NT / 2 : u == 0) ? CHC / 2 : CHC;
+          for (int m = 0; m <= i / 2; ++m) {
+            bf16x8 tf[2];
 #pragma unroll
             for (int p = 0; p < 2; ++p)
-              pa[u][p] = *reinterpret_cast<const bf16x8*>(Pl + p * TL + tl_row<C>(t) +
-                                                          8 * ((4 * kb + g4) ^ swz(t, ch)));
+              tf[p] = *reinterpret_cast<const bf16x8*>(Tl + p * TL + tl_row<C>(t) +
+                                                       8 * ((4 * m + g4) ^ swz(t, ch)));
+            U[i] = mfma16x16x32(tf[1], rb[m][0], U[i]);
+            U[i] = mfma16x16x32(tf[0], rb[m][1], U[i]);
+            U[i] = mfma16x16x32(tf[0], rb[m][0], U[i]);
+          }
+        }
+
+        // U as operand planes (32 tokens per block, slot order), plain and
+        // scaled by D.
+        bf16x8 ub[CB][2], udb[CB][2];
+#pragma unroll
+        for (int kb = 0; kb < CB; ++kb) {
+          float x[8], xd[8];
+#pragma unroll
+          for (int e2 = 0; e2 < 8; ++e2) {
+            const int a0 = 2 * kb + e2 / 4, e = e2 & 3;
+            x[e2] = U[a0][e];
+            xd[e2] = Gl[C + 16 * a0 + 4 * g4 + e] * U[a0][e];
+          }
+          if constexpr (OUT) split8<2>(x, ub[kb]);
+          split8<2>(xd, udb[kb]);
+        }
+
+        if constexpr (OUT) {
+          // O^T = Y^T diag(gamma) + U^T P^T for this wave's token tiles: lane
+          // (c, g) ends up with token 16 a + c and state rows 4 g .. 4 g + 3 of
+          // its row tile.  P is zero above the diagonal, so token tile a needs
+          // the 32-blocks kb <= a / 2.
+          floatx4 oa[NO];
+          int at[NO];
+#pragma unroll
+          for (int u = 0; u < NO; ++u) {
+            at[u] = NH == 1 ? u : otile(hp, u);
+            oa[u] = Yo[u] * Gl[16 * at[u] + c16];
           }
 #pragma unroll
-          for (int u = 0; u < NO; ++u)
-            if (NH == 1 ? u >= 2 * kb : u >= kb) oa[u] = mfma16x16x32(ub[kb][1], pa[u][0], oa[u]);
+          for (int kb = 0; kb < CB; ++kb) {
+            // tiles with a / 2 >= kb: NH = 1: a >= 2 kb; NH = 2: u >= kb
+            bf16x8 pa[NO][2];
 #pragma unroll
-          for (int u = 0; u < NO; ++u)
-            if (NH == 1 ? u >= 2 * kb : u >= kb) oa[u] = mfma16x16x32(ub[kb][0], pa[u][1], oa[u]);
+            for (int u = 0; u < NO; ++u) {
+              if (NH == 1 ? u < 2 * kb : u < kb) continue;
+              const int t = 16 * at[u] + c16;
+              const int ch = (NH == 1 ? u < NT / 2 : u == 0) ? CHC / 2 : CHC;
 #pragma unroll
-          for (int u = 0; u < NO; ++u)
-            if (NH == 1 ? u >= 2 * kb : u >= kb) oa[u] = mfma16x16x32(ub[kb][0], pa[u][0], oa[u]);
+              for (int p = 0; p < 2; ++p)
+                pa[u][p] = *reinterpret_cast<const bf16x8*>(Pl + p * TL + tl_row<C>(t) +
+                                                            8 * ((4 * kb + g4) ^ swz(t, ch)));
+            }
+#pragma unroll
+            for (int u = 0; u < NO; ++u)
+              if (NH == 1 ? u >= 2 * kb : u >= kb) oa[u] = mfma16x16x32(ub[kb][1], pa[u][0], oa[u]);
+#pragma unroll
+            for (int u = 0; u < NO; ++u)
+              if (NH == 1 ? u >= 2 * kb : u >= kb) oa[u] = mfma16x16x32(ub[kb][0], pa[u][1], oa[u]);
+#pragma unroll
+            for (int u = 0; u < NO; ++u)
+              if (NH == 1 ? u >= 2 * kb : u >= kb) oa[u] = mfma16x16x32(ub[kb][0], pa[u][0], oa[u]);
+          }
+          int tok0;
+          const int cl = chunk_range(s, tok0);
+#pragma unroll
+          for (int u = 0; u < NO; ++u) {
+            const int t = 16 * at[u] + c16;
+            if (t < cl)
+              store4<OUTD>(o, (static_cast<size_t>(tok0 + t) * H + h) * D + Cfg::ROWS * vb + 16 * rt + 4 * g4,
+                           oa[u]);
+          }
         }
-        int tok0;
-        const int cl = chunk_range(s, tok0);
-#pragma unroll
-        for (int u = 0; u < NO; ++u) {
-          const int t = 16 * at[u] + c16;
-          if (t < cl)
-            store4<OUTD>(o, (static_cast<size_t>(tok0 + t) * H + h) * D + Cfg::ROWS * vb + 16 * rt + 4 * g4,
-                         oa[u]);
-        }
-      }
 
-      __builtin_amdgcn_sched_barrier(0);
-      // S <- gamma_C S + (diag(D) U)^T K, as S^T = gamma_C S^T + K^T diag(D) U,
-      // on this wave's column tiles.  K^T fragments (features 16 jt + c16;
-      // slots = tokens 32 kb + 4 g4 + e and 32 kb + 16 + 4 g4 + e) come from
-      // transpose reads of the K rows, running ahead of the products that
-      // consume them.
-      bf16x8 kt[CB][JT];
+        __builtin_amdgcn_sched_barrier(0);
+        // S <- gamma_C S + (diag(D) U)^T K, as S^T = gamma_C S^T + K^T diag(D) U,
+        // on this wave's column tiles.  K^T fragments (features 16 jt + c16;
+        // slots = tokens 32 kb + 4 g4 + e and 32 kb + 16 + 4 g4 + e) come from
+        // transpose reads of the K rows, running ahead of the products that
+        // consume them.
+        bf16x8 kt[CB][JT];
 #pragma unroll
-      for (int kb = 0; kb < CB; ++kb)
+        for (int kb = 0; kb < CB; ++kb)
 #pragma unroll
-        for (int jl = 0; jl < JT; ++jl) {
-          const shortx4 lo = read_tr4(Kl, D, CHD, 32 * kb, 16 * (jt0 + jl), c16, g4);
-          const shortx4 hi = read_tr4(Kl, D, CHD, 32 * kb + 16, 16 * (jt0 + jl), c16, g4);
-          kt[kb][jl] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          for (int jl = 0; jl < JT; ++jl) {
+            const shortx4 lo = read_tr4(Kl, D, CHD, 32 * kb, 16 * (jt0 + jl), c16, g4);
+            const shortx4 hi = read_tr4(Kl, D, CHD, 32 * kb + 16, 16 * (jt0 + jl), c16, g4);
+            kt[kb][jl] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+        const float gam_end = Gl[C - 1];
+#pragma unroll
+        for (int jl = 0; jl < JT; ++jl) S[jl] *= gam_end;
+#pragma unroll
+        for (int kb = 0; kb < CB; ++kb)
+#pragma unroll
+          for (int jl = 0; jl < JT; ++jl) {
+            bf16x8 kk[1] = {kt[kb][jl]};
+            mma_planes<1, 2>(S[jl], kk, udb[kb]);
+          }
+        lead_interleave<8, 2 * CB * JT>();
+        __builtin_amdgcn_sched_barrier(0);
+        if (fixed) {
+          float* fx = fixed + (static_cast<size_t>(s) * H + h) * D * D + static_cast<size_t>(vrow) * D;
+#pragma unroll
+          for (int jl = 0; jl < JT; ++jl)
+            *reinterpret_cast<floatx4*>(fx + 16 * (jt0 + jl) + 4 * g4) = S[jl];
         }
-      const float gam_end = Gl[C - 1];
-#pragma unroll
-      for (int jl = 0; jl < JT; ++jl) S[jl] *= gam_end;
-#pragma unroll
-      for (int kb = 0; kb < CB; ++kb)
-#pragma unroll
-        for (int jl = 0; jl < JT; ++jl) {
-          bf16x8 kk[1] = {kt[kb][jl]};
-          mma_planes<1, 2>(S[jl], kk, udb[kb]);
-        }
-      lead_interleave<8, 2 * CB * JT>();
-      __builtin_amdgcn_sched_barrier(0);
-      if (fixed) {
-        float* fx = fixed + (static_cast<size_t>(s) * H + h) * D * D + static_cast<size_t>(vrow) * D;
-#pragma unroll
-        for (int jl = 0; jl < JT; ++jl)
-          *reinterpret_cast<floatx4*>(fx + 16 * (jt0 + jl) + 4 * g4) = S[jl];
+        bare_barrier();  // chunk s is done with its buffer; chunk s + 1 is in LDS
+      };
+      for (int s = c0; s < c1; s += 2) {
+        step(s, std::integral_constant<int, 0>{});
+        if (s + 1 < c1) step(s + 1, std::integral_constant<int, 1>{});
       }
-      bare_barrier();  // chunk s is done with its buffer; chunk s + 1 is in LDS
-    };
-    for (int s = c0; s < c1; s += 2) {
-      step(s, std::integral_constant<int, 0>{});
-      if (s + 1 < c1) step(s + 1, std::integral_constant<int, 1>{});
     }
-  }
 
-  if (state_out) {
+    if (state_out) {
 #pragma unroll
-    for (int jl = 0; jl < JT; ++jl)
-      *reinterpret_cast<floatx4*>(state_out + sbase + 16 * (jt0 + jl) + 4 * g4) = S[jl];
+      for (int jl = 0; jl < JT; ++jl)
+        *reinterpret_cast<floatx4*>(state_out + sbase + 16 * (jt0 + jl) + 4 * g4) = S[jl];
+    }
+  };
+  if constexpr (NH == 1) {
+    compute_waves(std::integral_constant<int, 0>{});
+  } else if (wave % NH == 0) {
+    compute_waves(std::integral_constant<int, 0>{});
+  } else {
+    compute_waves(std::integral_constant<int, 1>{});
   }
 }
 

@@ -199,18 +199,20 @@ size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int 
  * following schedules, with the same results up to rounding order:
  *   - chunk-parallel: layout, chunk-local L/M, fixup over the chunks of each
  *     sequence (two-level for long sequences with few heads), chunk outputs,
- *     final states.  Taken when L_out or M_out is given, and for fp32 inputs
- *     or chunk 16 (fp32 inputs keep every product at fp32 precision);
+ *     final states.  Taken for fp32 inputs or chunk 16 (fp32 inputs keep
+ *     every product at fp32 precision);
  *   - sequential scan: layout, per-chunk factors T = (I + A)^{-1} and
  *     P = (Q K^T) (.) Gamma, then one pass per (sequence, head, block of state
  *     rows) that applies the UT transform and the fixup in factored form
  *     (S M_c + L_c = gamma_C S + (diag(D) T diag(beta) (V - diag(gamma) K S^T))^T K,
  *     without forming M, L, W or Ut) and writes the outputs, the final states
- *     and, when given, fixed_out.  Taken otherwise; for long sequences at low
- *     parallelism as a segmented scan: the same pass over segments of whole
- *     chunks from zero (segment local states) and from the identity with
- *     v = 0 (segment transfer matrices), the segment-level fixup, and a final
- *     pass from every segment's true start.
+ *     and, when given, fixed_out.  Taken for bf16 inputs at chunk 64; for long
+ *     sequences at low parallelism as a segmented scan: the same pass over
+ *     segments of whole chunks from zero (segment local states) and from the
+ *     identity with v = 0 (segment transfer matrices), the segment-level
+ *     fixup, and a final pass from every segment's true start.  When L_out or
+ *     M_out is given, the chunk-local kernel of the chunk-parallel form writes
+ *     them in parallel, before the scan.
  */
 gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v,
                              const float* g, const float* beta,

@@ -54,10 +54,18 @@ def test_max_chunks_and_workspace(lib):
     assert g.gdr_max_chunks(-1, 1, 64) == -1
     assert g.gdr_max_chunks(10, 0, 64) == -1
     mc = g.gdr_max_chunks(16384, 4, 64)
-    for dt in (g.GDR_BF16, g.GDR_FP32):
-        ws = g.gdr_chunk_prefill_workspace_bytes(16384, 4, 16, 128, 128, 64, dt)
-        # the chunk-parallel form with L, M and fixed in the workspace
-        assert ws >= mc * 16 * 128 * 128 * 4 * 3
+    assert mc == 260
+    # bf16 inputs at chunk 64 take the scan: the layout integers (offsets and
+    # chunk indices, each rounded up to 256 bytes) and the chunk factors, T and
+    # P as two bf16 planes of 3072 elements each plus 4 x 64 fp32 gate values
+    # per chunk-head: 25,600 bytes
+    ws = g.gdr_chunk_prefill_workspace_bytes(16384, 4, 16, 128, 128, 64, g.GDR_BF16)
+    assert ws == 256 + 2304 + mc * 16 * 25600
+    # fp32 inputs take the chunk-parallel form with L, M and fixed in the workspace
+    for chunk in (16, 64):
+        mcc = g.gdr_max_chunks(16384, 4, chunk)
+        ws = g.gdr_chunk_prefill_workspace_bytes(16384, 4, 16, 128, 128, chunk, g.GDR_FP32)
+        assert ws >= mcc * 16 * 128 * 128 * 4 * 3
     assert g.gdr_chunk_prefill_workspace_bytes(16384, 4, 16, 96, 96, 64) == 0
     assert g.gdr_chunk_prefill_workspace_bytes(16384, 4, 16, 128, 128, 32) == 0
     assert lib.gdr_chunk_prefill_workspace_bytes(16384, 4, 16, 128, 128, 64, 7) == 0

@@ -41,3 +41,34 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_cp_form_bytes():
+    # the chunk-parallel form adds 6 states per chunk-head: prefill 4096 chunk-heads,
+    # long 2048 chunks x 4 heads
+    assert bench.cp_form_bytes(2) == bench.PRE_CP_BYTES
+    assert bench.cp_form_bytes(4) == bench.io_min_bytes(4) + 8192 * 6 * STATE == 3_762_552_832
+    # one fixup step per (chunk, head): M_c and L_c read, fixed[c] written
+    assert bench.FIX_STEP_BYTES == 3 * STATE
+    # L and M returned by the scan schedule: written once, plus the factors
+    # (25,600 B written, read back with 32 KiB of q and k rows) per chunk-head
+    assert bench.lm_request_bytes(2) == bench.PRE_IO_BYTES + 4096 * (2 * STATE + 25600 + 25600 + 32768)
+
+
+def test_records_are_used_only_on_their_sources(tmp_path, monkeypatch):
+    import json
+    src = tmp_path / "k.hip"
+    src.write_text("kernel v1")
+    (tmp_path / "profiles").mkdir()
+    rec = {"sources": {"k.hip": bench._sha256(str(src))}, "hbm_bytes_per_launch": 7}
+    (tmp_path / "profiles" / "r.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.load_record("r.json")["hbm_bytes_per_launch"] == 7
+    src.write_text("kernel v2")
+    assert bench.load_record("r.json") is None
+    assert bench.load_record("missing.json") is None
+
+
+def test_only_choices():
+    assert bench.parse(["--only", "fixup_long"]).only == "fixup_long"
+    assert bench.parse([]).only is None and bench.parse([]).steps >= 20

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from gdr_synth import generate
-from gpu_util import BF16_TOL, dev_inputs, host64, rel_err, say
+from gpu_util import BF16_TOL, FP32_TOL, dev_inputs, host64, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -144,29 +144,35 @@ def test_prefill_tokens_past_2_31_elements():
     torch.cuda.empty_cache()
 
 
-def test_chunk_parallel_states_past_2_31_elements():
-    # The chunk-parallel schedule (L and M requested) on 4 sequences of 67200
-    # tokens at 32 heads: L, M and the fixed states hold 4204 chunk slots x 32
-    # heads x 128 x 128 = 2.2e9 elements each, so the chunks past slot 4096
-    # sit beyond 2^31.  Inputs drawn on the device from a seeded generator
-    # (the recipe of the token test above, S0 = 0).  The last sequence is
-    # checked against the oracle run on two of its heads: outputs, final
-    # state and the fixed state of its last chunks (slots past 4096).
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_chunk_states_past_2_31_elements(dt):
+    # L and M requested on 4 sequences of 67200 tokens at 32 heads: L, M and
+    # the fixed states hold 4204 chunk slots x 32 heads x 128 x 128 = 2.2e9
+    # elements each, so the chunks past slot 4096 sit beyond 2^31.  bf16
+    # inputs take the scan (L and M from the chunk-local kernel); fp32 inputs
+    # the chunk-parallel form (chunk-local, dense fixup, chunk outputs).
+    # Inputs drawn on the device from a seeded generator (the recipe of the
+    # token test above, S0 = 0).  The last sequence is checked against the
+    # oracle run on two of its heads: outputs, final state and the fixed
+    # states of its last chunks (slots past 4096), and L and M of its last
+    # chunk against the chunked oracle.
     import gated_delta_rule_100_amd as gdr
     Nn, L, Hh, C = 4, 67200, 32, 64
     T = Nn * L
     mc = gdr.gdr_max_chunks(T, Nn, C)
-    say(f"chunk-parallel prefill {Nn} x {L} tokens, H={Hh}: L/M/fixed of {mc * Hh * D * D:.3e} elements")
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    tol = BF16_TOL if dt == "bf16" else FP32_TOL
+    say(f"prefill {Nn} x {L} tokens, H={Hh}, {dt}: L/M/fixed of {mc * Hh * D * D:.3e} elements")
     gen = torch.Generator(device="cuda")
     gen.manual_seed(740)
 
     def unit_rows():
         x = torch.randn(T, Hh, D, generator=gen, device="cuda")
         x /= x.norm(dim=-1, keepdim=True)
-        return x.to(torch.bfloat16)
+        return x.to(tdt)
 
     q, k = unit_rows(), unit_rows()
-    v = torch.randn(T, Hh, D, generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn(T, Hh, D, generator=gen, device="cuda").to(tdt)
     g = -torch.nn.functional.softplus(torch.randn(T, Hh, generator=gen, device="cuda"))
     beta = torch.sigmoid(torch.randn(T, Hh, generator=gen, device="cuda"))
     cu = torch.arange(0, T + 1, L, dtype=torch.int32, device="cuda")
@@ -178,10 +184,12 @@ def test_chunk_parallel_states_past_2_31_elements():
     gdr.gdr_chunk_prefill(q, k, v, g, beta, cu, None, state_out, o, chunk=C, L_out=Lo, M_out=Mo,
                           fixed_out=F)
     torch.cuda.synchronize()
-    del Lo, Mo
 
-    def bits(t):
-        return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+    def host(t):
+        t = t.contiguous().cpu()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
 
     n = Nn - 1
     a, b = n * L, (n + 1) * L
@@ -190,14 +198,20 @@ def test_chunk_parallel_states_past_2_31_elements():
     for h in (0, Hh - 1):
         sl = (slice(a, b), slice(h, h + 1))
         o_ref, s_ref, cs_ref = oracle.recurrent(
-            bits(q[sl]), bits(k[sl]), bits(v[sl]), g[sl].contiguous().cpu().numpy(),
+            host(q[sl]), host(k[sl]), host(v[sl]), g[sl].contiguous().cpu().numpy(),
             beta[sl].contiguous().cpu().numpy(), np.array([0, L]), chunk=C)
         e_o = rel_err(host64(o[a:b, h]), o_ref[:, 0])
         e_s = rel_err(host64(state_out[n, h]), s_ref[0, 0])
         last = slice(c0 + nch - 8, c0 + nch)
         e_f = rel_err(host64(F[last, h]), cs_ref[nch - 8:nch, 0])
+        lo = b - C
+        loc = oracle.chunk_local(oracle.as_f64(host(k[lo:b, h])), oracle.as_f64(host(v[lo:b, h])),
+                                 g[lo:b, h].double().cpu().numpy(),
+                                 beta[lo:b, h].double().cpu().numpy())
+        e_l = rel_err(host64(Lo[c0 + nch - 1, h]), loc["L"])
+        e_m = rel_err(host64(Mo[c0 + nch - 1, h]), loc["M"])
         say(f"  pair ({n},{h}) last slot offset {((c0 + nch - 1) * Hh + h) * D * D:.3e}: "
-            f"o {e_o:.2e} state {e_s:.2e} fixed {e_f:.2e}")
-        assert max(e_o, e_s, e_f) <= BF16_TOL, (h, e_o, e_s, e_f)
-    del q, k, v, o, state_out, F
+            f"o {e_o:.2e} state {e_s:.2e} fixed {e_f:.2e} L {e_l:.2e} M {e_m:.2e}")
+        assert max(e_o, e_s, e_f, e_l, e_m) <= tol, (h, e_o, e_s, e_f, e_l, e_m)
+    del q, k, v, o, state_out, F, Lo, Mo
     torch.cuda.empty_cache()

@@ -8,11 +8,12 @@ is exercised.  Tolerance: max|gpu - ref| / max|ref| <= 1e-3 for bf16 inputs,
 1e-5 for fp32 inputs, on fp32 outputs; bf16 outputs must equal the
 round-to-nearest-even of the fp32 outputs bit for bit.
 
-Two schedules are covered: the chunk-parallel form (taken whenever L or M is
-requested) and the sequential chunk scan (taken for bf16 inputs at chunk 64
-when neither is requested, unless the sequences are long and few).  Each
-parity case runs both: "cp" asks for L, M and the chunk-end states, "scan"
-for the chunk-end states only, "none" for nothing optional."""
+Two schedules are covered: the chunk-parallel form (fp32 inputs, chunk 16)
+and the sequential chunk scan (bf16 inputs at chunk 64; segmented when the
+sequences are long and few), which also writes L and M through the
+chunk-local kernel when they are requested.  Each parity case runs with
+"cp": L, M and the chunk-end states requested, "scan": the chunk-end states
+only, and some with "none": nothing optional."""
 import numpy as np
 import pytest
 import torch
@@ -330,11 +331,11 @@ def test_split_prefill_resumes():
     assert rel_err(state.astype(np.float64), host64(full["state_out"])) <= 1e-3
 
 
-# Long sequences with few heads: with L and M requested ("cp") they take the
-# two-level fixup of the chunk-parallel form (fold segments of chunks, scan the
-# segments, apply the scanned starts); otherwise ("scan": with the chunk-end
-# states, "none": without) the segmented scan (local segment states, segment
-# transfer matrices, segment fixup, final pass from the true starts).
+# Long sequences with few heads: bf16 inputs take the segmented scan (local
+# segment states, segment transfer matrices, segment fixup, final pass from the
+# true starts), with L and M from the chunk-local kernel when requested ("cp");
+# fp32 inputs take the two-level fixup of the chunk-parallel form (fold
+# segments of chunks, scan the segments, apply the scanned starts).
 LONG_CASES = {
     "long-T32768-H1-slow": (4, dict(seqlens=[32768], H=1, gate="slow")),
     # fp32 inputs always take the chunk-parallel form: here its two-level fixup

@@ -19,6 +19,7 @@ SCRATCH_BYTES = 128 << 20
 
 
 def run(d, noalloc, keep_lm=False, keep_fixed=True):
+    """One prefill through either entry point; fp32 outputs and states."""
     import gated_delta_rule_100_amd as gdr
     di = dev_inputs(d)
     T, H, D, N, C = d["T"], d["H"], d["dk"], d["N"], d["chunk"]
@@ -35,7 +36,7 @@ def run(d, noalloc, keep_lm=False, keep_fixed=True):
         gdr.gdr_chunk_prefill_noalloc(di["q"], di["k"], di["v"], di["g"], di["beta"], di["cu"],
                                       di["state0"], sout, o, **kw)
     else:
-        need = gdr.gdr_chunk_prefill_workspace_bytes(T, N, H, D, D, C, gdr.GDR_BF16)
+        need = gdr.gdr_chunk_prefill_workspace_bytes(T, N, H, D, D, C, di["q"].dtype)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
         ws.view(torch.float16)[: ws.numel() // 2].fill_(float("nan"))
         gdr.gdr_chunk_prefill(di["q"], di["k"], di["v"], di["g"], di["beta"], di["cu"],
@@ -55,22 +56,27 @@ def same(a, b, what):
         assert torch.equal(a[key], b[key]), (what, key)
 
 
-# pairs of calls: (first, second), each (workload index, overrides, ask for L and M)
+# pairs of calls: (first, second), each (workload index, overrides, ask for L
+# and M, ask for the chunk-end states)
 SEQUENCES = {
-    "scan-then-smaller-scan": ((2, dict(seqlens=[700, 64, 1, 0, 300], H=8), False),
-                               (3, dict(seqlens=[130, 5], H=2), False)),
-    "segmented-then-smaller-chunk-parallel": ((4, dict(seqlens=[32768], H=1, state0=True), False),
-                                              (2, dict(seqlens=[200, 0, 65], H=2), True)),
+    "scan-then-smaller-scan": ((2, dict(seqlens=[700, 64, 1, 0, 300], H=8), False, True),
+                               (3, dict(seqlens=[130, 5], H=2), True, True)),
+    # fp32 inputs take the chunk-parallel form; without fixed_out its chunk-end
+    # states live in the scratch
+    "segmented-then-smaller-chunk-parallel": (
+        (4, dict(seqlens=[32768], H=1, state0=True), False, True),
+        (2, dict(seqlens=[200, 0, 65], H=2, dtype="f32"), False, False)),
 }
 
 
 @pytest.mark.parametrize("name", list(SEQUENCES))
 def test_noalloc_matches_workspace_entry_point(name):
-    for i, (idx, ov, lm) in enumerate(SEQUENCES[name]):
+    for i, (idx, ov, lm, fx) in enumerate(SEQUENCES[name]):
         d = workload(idx, seed=900 + i, **ov)
-        say(f"noalloc {name} call {i}: T={d['T']} N={d['N']} H={d['H']} L/M={lm}")
-        ref = run(d, noalloc=False, keep_lm=lm)
-        got = run(d, noalloc=True, keep_lm=lm)
+        say(f"noalloc {name} call {i}: T={d['T']} N={d['N']} H={d['H']} {d['dtype']} L/M={lm} "
+            f"fixed={fx}")
+        ref = run(d, noalloc=False, keep_lm=lm, keep_fixed=fx)
+        got = run(d, noalloc=True, keep_lm=lm, keep_fixed=fx)
         same(got, ref, f"{name} call {i}")
 
 
