@@ -113,7 +113,8 @@ def lm_request_bytes(idx):
     return io_min_bytes(idx) + chunk_heads * (2 * 65536 + PRE_FACTOR_W + PRE_FACTOR_R)
 
 
-ONLY = ("decode", "prefill", "varlen", "long", "prefill_cp", "long_cp", "fixup_long", "mtp")
+ONLY = ("decode", "prefill", "varlen", "long", "prefill_cp", "long_cp", "fixup_long", "mtp",
+        "copy")
 
 
 def parse(argv=None):
@@ -430,11 +431,26 @@ def prefill_line(r, idx, lm=False):
     return line
 
 
+def record_summary(name, keys=("avg_us", "per_launch", "hbm_bytes", "hbm_gbs", "l2_hit_rate",
+                                 "mfma_busy", "mean_waves_per_cu", "chain_steps",
+                                 "us_per_chain_step", "valu_per_compute_wave_step",
+                                 "mfma_per_compute_wave_step", "lds_per_compute_wave_step",
+                                 "lds_busy", "lds_bank_conflict_per_busy")):
+    """Per-kernel figures of a committed profile record (None when stale)."""
+    rec = load_record(name)
+    if rec is None:
+        return None, None
+    kern = {k: {f: v[f] for f in keys if f in v} for k, v in rec["kernels"].items()}
+    return rec, kern
+
+
 def prefill_roofline(pre_ms):
-    """The prefill's binding resource from the committed counter record: the
-    scan kernel is a chain of 64 dependent chunk steps per (sequence, head)."""
-    rec = load_record("prefill_B4_T4096_H16_counters.json")
-    out = {"kernel": "chunk_scan_kernel (after chunk_factors_kernel)",
+    """The prefill's roofline: the I/O-minimum bytes over the measured call
+    time, and what binds it from the committed counter record -- the scan
+    kernel is a chain of 64 dependent chunk steps per (sequence, head) that
+    keeps its compute units' matrix cores busy about a fifth of the time."""
+    rec, kern = record_summary("prefill_B4_T4096_H16_record.json")
+    out = {"kernel": "chunk_scan_kernel<128, 64, bf16, true, 2> after chunk_factors_kernel",
            "bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "achieved": round(PRE_IO_BYTES / (pre_ms / 1e3) / 1e9, 1),
            "frac": round(PRE_IO_BYTES / (pre_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -443,9 +459,10 @@ def prefill_roofline(pre_ms):
            "record": None, "traffic": None}
     if rec is None:
         return out
-    out["record"] = "profiles/prefill_B4_T4096_H16_counters.json"
+    out["record"] = "profiles/prefill_B4_T4096_H16_record.json"
     out["traffic"] = rec.get("hbm_bytes_per_launch")
-    out["kernels"] = rec.get("kernels")
+    out["kernel_us_per_launch"] = rec.get("kernel_us_per_launch")
+    out["kernels"] = kern
     return out
 
 
@@ -475,6 +492,10 @@ def main(argv=None):
             r = bench_mtp(torch, gdr, K, W)
         elif what == "fixup_long":
             r = bench_fixup_long(torch, gdr, K, W)
+        elif what == "copy":  # the counters' calibration: 1 GiB read and written per launch
+            src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+            dst = torch.empty_like(src)
+            r = per_launch(torch, lambda i: dst.copy_(src), K, torch.cuda.current_stream())
         else:
             idx = {"prefill": 2, "varlen": 3, "long": 4, "prefill_cp": 2, "long_cp": 4}[what]
             r = bench_prefill(torch, gdr, K, W, idx, cp_form=what.endswith("_cp"))
@@ -529,10 +550,20 @@ def main(argv=None):
             "prefill_ms": round(pre_w["ms"], 5),
             "prefill_tokens_per_s": round(PRE_TOKENS / (pre_w["ms"] / 1e3), 1),
         }
-        long_rec = load_record("prefill_long_T131072_H4_phases.json")
-        if long_rec is not None:
-            others["prefill_long"]["phases_us"] = long_rec.get("phases_us")
-            others["prefill_long"]["phases_record"] = "profiles/prefill_long_T131072_H4_phases.json"
+        for key, name in (("prefill_varlen", "prefill_varlen_32768tok_H32_record.json"),
+                          ("prefill_long", "prefill_long_T131072_H4_record.json"),
+                          ("prefill_cp", "prefill_B4_T4096_H16_LM_record.json"),
+                          ("prefill_long_cp", "prefill_long_T131072_H4_LM_record.json"),
+                          ("fixup_long", "fixup_long_2048chunks_H4_record.json"),
+                          ("decode_mtp", "decode_mtp_N64_T8_H32_d128_record.json")):
+            rec, kern = record_summary(name)
+            others[key]["record"] = None if rec is None else "profiles/" + name
+            if rec is not None:
+                others[key]["traffic"] = rec.get("hbm_bytes_per_launch")
+                others[key]["kernels"] = kern
+                for f in ("phases_us", "segment_fixup_us_per_step"):
+                    if f in rec:
+                        others[key][f] = rec[f]
     copy_gbs = copy_bandwidth(torch)
     log(f"device copy {copy_gbs:.1f} GB/s")
     cpu = None
@@ -544,7 +575,7 @@ def main(argv=None):
     pre_s = pre["ms"] / 1e3
     dec_gbs = DEC_STATE_BYTES / dec_s / 1e9
     achieved = DEC_ALG_BYTES / dec_s / 1e9
-    dec_rec = load_record("decode_N64_H32_d128_traffic.json")
+    dec_rec = load_record("decode_N64_H32_d128_record.json")
     out = {
         "metric": "GDR decode state GB/s (% HBM peak); chunked-prefill tokens/s at H=16,d=128",
         "value": round(dec_gbs, 2),
