@@ -142,10 +142,11 @@ size_t scan_workspace(int mc, int H, int chunk) {
 // per-chunk states; it takes bf16 inputs and chunk 64.  For long sequences at
 // low parallelism, where one dependent chain per (sequence, head) would leave
 // the GPU idle, the segmented scan cuts every sequence into segments of whole
-// chunks and runs three scan passes over all segments at once -- local end
-// states from zero, transfer matrices (identity start, v = 0), and the final
-// pass from the true segment starts -- with the segment-level fixup of the
-// chunk-parallel form between them.  When the caller asks for L or M, the
+// chunks and runs two scan passes over all segments at once -- one carrying
+// two state chains per segment (its local end state from zero, and its
+// transfer matrix from the identity with v = 0), and the final pass from the
+// true segment starts -- with the segment-level fixup of the chunk-parallel
+// form between them.  When the caller asks for L or M, the
 // chunk-local kernel writes them into the caller's buffers in parallel and
 // the chain still runs in factored form (reading 25.6 KB of factors per
 // chunk-head instead of L_c and M_c, 128 KiB).  The chunk-parallel form
@@ -301,7 +302,7 @@ gdr_status chunk_prefill(const char* who, const void* q, const void* k, const vo
     ws += align_up(z.gate);
     if (sched == kScan) {
       e = gdr::launch_chunk_scan(q, k, v, cu_seqlens, offs, f, state_in, state_out, fixed_out, o,
-                                 N, H, dk, chunk, mc, T_total, out_dtype, 0, st);
+                                 N, H, dk, chunk, mc, T_total, out_dtype, st);
       return hip_fail(e, who, "chunk scan");
     }
     // segmented scan
@@ -325,15 +326,11 @@ gdr_status chunk_prefill(const char* who, const void* q, const void* k, const vo
     if (e == hipSuccess)
       e = gdr::launch_segment_ranges(cu_seqlens, offs, seg_idx, N, ssz.seg, chunk, ms, cu_seg,
                                      offs_seg, st);
-    // local end state of every segment from zero
+    // local end state (from zero) and transfer matrix (identity start, v = 0)
+    // of every segment, both chains in one pass
     if (e == hipSuccess)
-      e = gdr::launch_chunk_scan(q, k, v, cu_seg, offs_seg, f, nullptr, seg_L, nullptr, nullptr,
-                                 ms, H, dk, chunk, mc, T_total, out_dtype, 0, st);
-    // transfer matrix of every segment: identity start, v = 0
-    if (e == hipSuccess)
-      e = gdr::launch_chunk_scan(q, k, nullptr, cu_seg, offs_seg, f, nullptr, seg_M, nullptr,
-                                 nullptr, ms, H, dk, chunk, mc, T_total, out_dtype,
-                                 gdr::kScanIdentityStart, st);
+      e = gdr::launch_chunk_scan_pair(k, v, cu_seg, offs_seg, f, nullptr, seg_L, seg_M, ms, H, dk,
+                                      chunk, mc, T_total, st);
     // segment-level fixup: the end state of every segment
     if (e == hipSuccess)
       e = gdr::launch_fixup_mode(0, seg_L, seg_M, state_in, seg_offs, nullptr, 0, nullptr,
@@ -343,7 +340,7 @@ gdr_status chunk_prefill(const char* who, const void* q, const void* k, const vo
     // outputs (and chunk-end states) from the true segment starts
     if (e == hipSuccess)
       e = gdr::launch_chunk_scan(q, k, v, cu_seg, offs_seg, f, seg_start, nullptr, fixed_out, o,
-                                 ms, H, dk, chunk, mc, T_total, out_dtype, 0, st);
+                                 ms, H, dk, chunk, mc, T_total, out_dtype, st);
     if (e != hipSuccess) return hip_fail(e, who, "segmented scan");
     e = gdr::launch_final_state(state_in, seg_end, seg_offs, N, H, dk, dv, ms, state_out, st);
     return hip_fail(e, who, "final state");

@@ -223,6 +223,11 @@ __global__ __launch_bounds__(D * 4) void fixup_mfma_kernel(
   }
 }
 
+// One state per (blockIdx.x, all blockIdx.y): blockIdx.y picks a slice of
+// kFinalSlices of the state, so that a few states still spread over many
+// compute units.
+constexpr int kFinalSlices = 16;
+
 __global__ __launch_bounds__(256) void final_state_kernel(const float* __restrict__ state_in,
                                                           const float* __restrict__ fixed,
                                                           const int32_t* __restrict__ offs,
@@ -243,7 +248,8 @@ __global__ __launch_bounds__(256) void final_state_kernel(const float* __restric
   }
   float4* dst = reinterpret_cast<float4*>(state_out + static_cast<size_t>(pair) * elems);
   if (src == reinterpret_cast<const float*>(dst)) return;  // in place, nothing to move
-  for (int e = threadIdx.x; e < elems / 4; e += blockDim.x)
+  const int per = elems / 4 / kFinalSlices;  // float4 per slice (elems is a multiple of 4096)
+  for (int e = blockIdx.y * per + threadIdx.x; e < (blockIdx.y + 1) * per; e += blockDim.x)
     dst[e] = src ? reinterpret_cast<const float4*>(src)[e] : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
@@ -302,8 +308,8 @@ hipError_t launch_fixup(const float* L, const float* M, const float* state_in,
 hipError_t launch_final_state(const float* state_in, const float* fixed,
                               const int32_t* chunk_offsets, int N, int H, int dk, int dv,
                               int n_chunks, float* state_out, hipStream_t stream) {
-  hipLaunchKernelGGL(final_state_kernel, dim3(N * H), dim3(256), 0, stream, state_in, fixed,
-                     chunk_offsets, H, dk * dv, n_chunks, state_out);
+  hipLaunchKernelGGL(final_state_kernel, dim3(N * H, kFinalSlices), dim3(256), 0, stream,
+                     state_in, fixed, chunk_offsets, H, dk * dv, n_chunks, state_out);
   return hipGetLastError();
 }
 

@@ -100,17 +100,23 @@ hipError_t launch_chunk_factors(const void* q, const void* k, const float* g, co
 // Sequential scan over the chunks of every sequence from the factors and the
 // q, k, v inputs: outputs o (skipped when o is NULL), final states (skipped
 // when state_out is NULL), and (when fixed != NULL) the state at every chunk
-// end.  v == NULL takes v as zero.  flags: kScanIdentityStart starts every
-// (sequence, head) from the identity instead of state_in (dv = dk), which with
-// v == NULL makes the final state the sequence's transfer matrix (the map
-// S -> S M of the recurrence without its v k^T terms, row a of the state
-// being row a of M).
-constexpr int kScanIdentityStart = 1;
+// end.  v == NULL takes v as zero.
 hipError_t launch_chunk_scan(const void* q, const void* k, const void* v,
                              const int32_t* cu_seqlens, const int32_t* chunk_offsets,
                              const ChunkFactors& f, const float* state_in, float* state_out,
                              float* fixed, void* o, int N, int H, int d, int chunk, int n_slots,
-                             int T_total, int out_dtype, int flags, hipStream_t stream);
+                             int T_total, int out_dtype, hipStream_t stream);
+
+// The scan without outputs carrying two state chains per (sequence, head):
+// the first from state_in (zero when NULL) with v, whose end state goes to
+// state_out, and one from the identity with v = 0, whose end state -- the
+// transfer matrix of the sequence's chunks -- goes to transfer_out (d = dk =
+// dv).  Both read the same chunk data once.
+hipError_t launch_chunk_scan_pair(const void* k, const void* v, const int32_t* cu_seqlens,
+                                  const int32_t* chunk_offsets, const ChunkFactors& f,
+                                  const float* state_in, float* state_out, float* transfer_out,
+                                  int N, int H, int d, int chunk, int n_slots, int T_total,
+                                  hipStream_t stream);
 
 // Segments of a chunk-parallel layout as pseudo-sequences for the scan: for
 // every segment slot m < max_segs with seg_idx[m] = (n, j), tokens

@@ -181,13 +181,21 @@ __device__ __forceinline__ void lead_interleave() {
   }
 }
 
-template <int D, int C, Dt OUTD, bool OUT, int NH>
+// NS = 2 (no outputs, whole tiles) carries a second state chain beside the
+// first: it starts from the identity and sees v = 0, so its end state is the
+// transfer matrix of the chunks walked (the map S -> S M of the recurrence
+// without its v k^T terms), written to state_out2, while the first chain (from
+// state_in, or zero) gives the local end state.  Both chains read the same K, T
+// and gate fragments from LDS, and the two independent chains fill each
+// other's latency in the compute waves.
+template <int D, int C, Dt OUTD, bool OUT, int NH, int NS = 1>
 __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ offs, ChunkFactors f, const float* state_in, float* state_out,
-    float* __restrict__ fixed, void* __restrict__ o, int N, int H, int n_slots, int T_total,
-    int flags) {
+    float* state_out2, float* __restrict__ fixed, void* __restrict__ o, int N, int H,
+    int n_slots, int T_total) {
+  static_assert(NS == 1 || (NS == 2 && !OUT && NH == 1), "two chains: no outputs, whole tiles");
   using Cfg = ScanCfg<D, C, NH>;
   constexpr int NT = Cfg::NT, KB = Cfg::KB, KH = Cfg::KH, CB = Cfg::CB, JT = Cfg::JT;
   constexpr int NO = Cfg::NO;
@@ -352,16 +360,20 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
     const int vrow = Cfg::ROWS * vb + 16 * rt + c16;  // state row held by this lane
     const int jt0 = hp * JT;                          // first column tile held
     const size_t sbase = (static_cast<size_t>(n) * H + h) * D * D + static_cast<size_t>(vrow) * D;
-    floatx4 S[JT];
+    floatx4 S[NS][JT];
 #pragma unroll
     for (int jl = 0; jl < JT; ++jl) {
       const int jt = jt0 + jl;
-      if (flags & kScanIdentityStart) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) S[jl][e] = vrow == 16 * jt + 4 * g4 + e ? 1.f : 0.f;
-      } else {
-        S[jl] = state_in ? *reinterpret_cast<const floatx4*>(state_in + sbase + 16 * jt + 4 * g4)
-                         : floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int ch = 0; ch < NS; ++ch) {
+        if (ch == 1) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S[ch][jl][e] = vrow == 16 * jt + 4 * g4 + e ? 1.f : 0.f;
+        } else {
+          S[ch][jl] = state_in
+                          ? *reinterpret_cast<const floatx4*>(state_in + sbase + 16 * jt + 4 * g4)
+                          : floatx4{0.f, 0.f, 0.f, 0.f};
+        }
       }
     }
     // Output token tiles of this wave: all of them when NH = 1; with NH = 2 the
@@ -403,26 +415,28 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
         // lane layout, so these registers serve as B (rows of S^T) in K S^T and
         // as A (rows of S) in S Q^T.
         constexpr int NCH = 2 / NH;  // column halves contracted by this wave
-        floatx4 Zh[NCH][NT], Yh[NCH][NT];
+        floatx4 Zh[NS][NCH][NT], Yh[NCH][NT];
 #pragma unroll
         for (int hc = 0; hc < NCH; ++hc) {
 #pragma unroll
           for (int a = 0; a < NT; ++a) {
-            Zh[hc][a] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ch = 0; ch < NS; ++ch) Zh[ch][hc][a] = floatx4{0.f, 0.f, 0.f, 0.f};
             if constexpr (OUT) Yh[hc][a] = floatx4{0.f, 0.f, 0.f, 0.f};
           }
 #pragma unroll
           for (int kl = 0; kl < KH; ++kl) {
             const int kbl = hc * KH + kl;  // block among this wave's columns
             const int kb = hp * (KB / NH) + kbl;
-            bf16x8 sbk[2];
-            {
+            bf16x8 sbk[NS][2];
+#pragma unroll
+            for (int ch = 0; ch < NS; ++ch) {
               float x[8];
 #pragma unroll
-              for (int e2 = 0; e2 < 8; ++e2) x[e2] = S[2 * kbl + e2 / 4][e2 & 3];
-              split8<2>(x, sbk);
+              for (int e2 = 0; e2 < 8; ++e2) x[e2] = S[ch][2 * kbl + e2 / 4][e2 & 3];
+              split8<2>(x, sbk[ch]);
 #pragma unroll
-              for (int p = 0; p < 2; ++p) sbk[p] = slot_to_natural(sbk[p]);
+              for (int p = 0; p < 2; ++p) sbk[ch][p] = slot_to_natural(sbk[ch][p]);
             }
             bf16x8 ka[NT], qa[NT];
 #pragma unroll
@@ -432,32 +446,40 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
               if constexpr (OUT)
                 qa[a] = *reinterpret_cast<const bf16x8*>(Ql + t * D + 8 * (n8 ^ swz(t, CHD)));
             }
-            // plane pairs, smallest terms first; the four token tiles are
-            // interleaved so that consecutive products are independent
+            // plane pairs, smallest terms first; the four token tiles (and the
+            // chains) are interleaved so that consecutive products are
+            // independent
 #pragma unroll
-            for (int a = 0; a < NT; ++a) Zh[hc][a] = mfma16x16x32(ka[a], sbk[1], Zh[hc][a]);
+            for (int a = 0; a < NT; ++a)
 #pragma unroll
-            for (int a = 0; a < NT; ++a) Zh[hc][a] = mfma16x16x32(ka[a], sbk[0], Zh[hc][a]);
+              for (int ch = 0; ch < NS; ++ch)
+                Zh[ch][hc][a] = mfma16x16x32(ka[a], sbk[ch][1], Zh[ch][hc][a]);
+#pragma unroll
+            for (int a = 0; a < NT; ++a)
+#pragma unroll
+              for (int ch = 0; ch < NS; ++ch)
+                Zh[ch][hc][a] = mfma16x16x32(ka[a], sbk[ch][0], Zh[ch][hc][a]);
             if constexpr (OUT) {
 #pragma unroll
-              for (int a = 0; a < NT; ++a) Yh[hc][a] = mfma16x16x32(sbk[1], qa[a], Yh[hc][a]);
+              for (int a = 0; a < NT; ++a) Yh[hc][a] = mfma16x16x32(sbk[0][1], qa[a], Yh[hc][a]);
 #pragma unroll
-              for (int a = 0; a < NT; ++a) Yh[hc][a] = mfma16x16x32(sbk[0], qa[a], Yh[hc][a]);
+              for (int a = 0; a < NT; ++a) Yh[hc][a] = mfma16x16x32(sbk[0][0], qa[a], Yh[hc][a]);
             }
           }
         }
-        floatx4 Z[NT], Yo[NO];  // Yo: Y^T of this wave's output tiles
+        floatx4 Z[NS][NT], Yo[NO];  // Yo: Y^T of this wave's output tiles
         if constexpr (NH == 1) {
 #pragma unroll
           for (int a = 0; a < NT; ++a) {
-            Z[a] = Zh[0][a] + Zh[1][a];
+#pragma unroll
+            for (int ch = 0; ch < NS; ++ch) Z[ch][a] = Zh[ch][0][a] + Zh[ch][1][a];
             if constexpr (OUT) Yo[a] = Yh[0][a] + Yh[1][a];
           }
         } else {
           // exchange with the wave holding the other column half (wave ^ 1):
           // all of its partial Z, and its partial Y^T of this wave's tiles
 #pragma unroll
-          for (int a = 0; a < NT; ++a) *xslot(wave, a) = Zh[0][a];
+          for (int a = 0; a < NT; ++a) *xslot(wave, a) = Zh[0][0][a];
           if constexpr (OUT) {
 #pragma unroll
             for (int u = 0; u < NO; ++u) {
@@ -472,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
           // does not wait for them at s_barrier)
           lds_barrier();  // exchange written
 #pragma unroll
-          for (int a = 0; a < NT; ++a) Z[a] = Zh[0][a] + *xslot(wave ^ 1, a);
+          for (int a = 0; a < NT; ++a) Z[0][a] = Zh[0][0][a] + *xslot(wave ^ 1, a);
           if constexpr (OUT) {
 #pragma unroll
             for (int u = 0; u < NO; ++u) {
@@ -491,7 +513,8 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
         // T rows are stored in slot order, so the T fragment of row 16 i + c and
         // 32-block m is one 16-byte read per plane.  Both column halves form
         // the same R and U.
-        floatx4 R[NT];
+        // (the second chain has v = 0)
+        floatx4 R[NS][NT];
 #pragma unroll
         for (int a = 0; a < NT; ++a) {
           const floatx4 gam = *reinterpret_cast<const floatx4*>(Gl + 16 * a + 4 * g4);
@@ -499,49 +522,61 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
           const shortx4 vv = v ? read_tr4(Vl, Cfg::ROWS, CHV, 16 * a, 16 * rt, c16, g4)
                                : shortx4{0, 0, 0, 0};
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            R[a][e] = bet[e] * (bf16_bits_to_f32(static_cast<uint16_t>(vv[e])) - gam[e] * Z[a][e]);
+          for (int e = 0; e < 4; ++e) {
+            R[0][a][e] =
+                bet[e] * (bf16_bits_to_f32(static_cast<uint16_t>(vv[e])) - gam[e] * Z[0][a][e]);
+            if constexpr (NS == 2) R[1][a][e] = bet[e] * (0.f - gam[e] * Z[1][a][e]);
+          }
         }
-        bf16x8 rb[CB][2];
+        bf16x8 rb[NS][CB][2];
 #pragma unroll
-        for (int m = 0; m < CB; ++m) {
-          float x[8];
+        for (int ch = 0; ch < NS; ++ch)
 #pragma unroll
-          for (int e2 = 0; e2 < 8; ++e2) x[e2] = R[2 * m + e2 / 4][e2 & 3];
-          split8<2>(x, rb[m]);
-        }
-        floatx4 U[NT];
+          for (int m = 0; m < CB; ++m) {
+            float x[8];
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) x[e2] = R[ch][2 * m + e2 / 4][e2 & 3];
+            split8<2>(x, rb[ch][m]);
+          }
+        floatx4 U[NS][NT];
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
-          const int t = 16 * i + c16, ch = t < C / 2 ? CHC / 2 : CHC;
-          U[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+          const int t = 16 * i + c16, cw16 = t < C / 2 ? CHC / 2 : CHC;
+#pragma unroll
+          for (int ch = 0; ch < NS; ++ch) U[ch][i] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int m = 0; m <= i / 2; ++m) {
             bf16x8 tf[2];
 #pragma unroll
             for (int p = 0; p < 2; ++p)
               tf[p] = *reinterpret_cast<const bf16x8*>(Tl + p * TL + tl_row<C>(t) +
-                                                       8 * ((4 * m + g4) ^ swz(t, ch)));
-            U[i] = mfma16x16x32(tf[1], rb[m][0], U[i]);
-            U[i] = mfma16x16x32(tf[0], rb[m][1], U[i]);
-            U[i] = mfma16x16x32(tf[0], rb[m][0], U[i]);
+                                                       8 * ((4 * m + g4) ^ swz(t, cw16)));
+#pragma unroll
+            for (int ch = 0; ch < NS; ++ch) {
+              U[ch][i] = mfma16x16x32(tf[1], rb[ch][m][0], U[ch][i]);
+              U[ch][i] = mfma16x16x32(tf[0], rb[ch][m][1], U[ch][i]);
+              U[ch][i] = mfma16x16x32(tf[0], rb[ch][m][0], U[ch][i]);
+            }
           }
         }
 
         // U as operand planes (32 tokens per block, slot order), plain and
         // scaled by D.
-        bf16x8 ub[CB][2], udb[CB][2];
+        bf16x8 ub[CB][2], udb[NS][CB][2];
 #pragma unroll
         for (int kb = 0; kb < CB; ++kb) {
-          float x[8], xd[8];
 #pragma unroll
-          for (int e2 = 0; e2 < 8; ++e2) {
-            const int a0 = 2 * kb + e2 / 4, e = e2 & 3;
-            x[e2] = U[a0][e];
-            xd[e2] = Gl[C + 16 * a0 + 4 * g4 + e] * U[a0][e];
+          for (int ch = 0; ch < NS; ++ch) {
+            float x[8], xd[8];
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) {
+              const int a0 = 2 * kb + e2 / 4, e = e2 & 3;
+              x[e2] = U[ch][a0][e];
+              xd[e2] = Gl[C + 16 * a0 + 4 * g4 + e] * U[ch][a0][e];
+            }
+            if constexpr (OUT) split8<2>(x, ub[kb]);
+            split8<2>(xd, udb[ch][kb]);
           }
-          if constexpr (OUT) split8<2>(x, ub[kb]);
-          split8<2>(xd, udb[kb]);
         }
 
         if constexpr (OUT) {
@@ -608,21 +643,24 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
           }
         const float gam_end = Gl[C - 1];
 #pragma unroll
-        for (int jl = 0; jl < JT; ++jl) S[jl] *= gam_end;
+        for (int ch = 0; ch < NS; ++ch)
+#pragma unroll
+          for (int jl = 0; jl < JT; ++jl) S[ch][jl] *= gam_end;
 #pragma unroll
         for (int kb = 0; kb < CB; ++kb)
 #pragma unroll
           for (int jl = 0; jl < JT; ++jl) {
             bf16x8 kk[1] = {kt[kb][jl]};
-            mma_planes<1, 2>(S[jl], kk, udb[kb]);
+#pragma unroll
+            for (int ch = 0; ch < NS; ++ch) mma_planes<1, 2>(S[ch][jl], kk, udb[ch][kb]);
           }
-        lead_interleave<8, 2 * CB * JT>();
+        lead_interleave<8, 2 * CB * JT * NS>();
         __builtin_amdgcn_sched_barrier(0);
         if (fixed) {
           float* fx = fixed + (static_cast<size_t>(s) * H + h) * D * D + static_cast<size_t>(vrow) * D;
 #pragma unroll
           for (int jl = 0; jl < JT; ++jl)
-            *reinterpret_cast<floatx4*>(fx + 16 * (jt0 + jl) + 4 * g4) = S[jl];
+            *reinterpret_cast<floatx4*>(fx + 16 * (jt0 + jl) + 4 * g4) = S[0][jl];
         }
         bare_barrier();  // chunk s is done with its buffer; chunk s + 1 is in LDS
       };
@@ -635,7 +673,14 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
     if (state_out) {
 #pragma unroll
       for (int jl = 0; jl < JT; ++jl)
-        *reinterpret_cast<floatx4*>(state_out + sbase + 16 * (jt0 + jl) + 4 * g4) = S[jl];
+        *reinterpret_cast<floatx4*>(state_out + sbase + 16 * (jt0 + jl) + 4 * g4) = S[0][jl];
+    }
+    if constexpr (NS == 2) {
+      if (state_out2) {
+#pragma unroll
+        for (int jl = 0; jl < JT; ++jl)
+          *reinterpret_cast<floatx4*>(state_out2 + sbase + 16 * (jt0 + jl) + 4 * g4) = S[1][jl];
+      }
     }
   };
   if constexpr (NH == 1) {
@@ -651,18 +696,19 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
 // has 256 compute units and one scan workgroup fills one (its LDS).
 constexpr int64_t kSplitMaxGroups = 256;
 
-template <int D, int C, Dt OUTD, bool OUT, int NH>
+template <int D, int C, Dt OUTD, bool OUT, int NH, int NS = 1>
 hipError_t scan_launch(const void* q, const void* k, const void* v, const int32_t* cu,
                        const int32_t* offs, const ChunkFactors& f, const float* state_in,
-                       float* state_out, float* fixed, void* o, int N, int H, int n_slots,
-                       int T_total, int flags, hipStream_t stream) {
+                       float* state_out, float* state_out2, float* fixed, void* o, int N, int H,
+                       int n_slots, int T_total, hipStream_t stream) {
   const int64_t pairs = static_cast<int64_t>(N) * H;
   const int64_t groups = (pairs + kXcds - 1) / kXcds * kXcds * ScanCfg<D, C, NH>::NVB;
   if (groups > INT32_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((chunk_scan_kernel<D, C, OUTD, OUT, NH>), dim3(static_cast<unsigned>(groups)),
-                     dim3(kThreads), 0, stream, static_cast<const uint16_t*>(q),
-                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), cu, offs, f,
-                     state_in, state_out, fixed, o, N, H, n_slots, T_total, flags);
+  hipLaunchKernelGGL((chunk_scan_kernel<D, C, OUTD, OUT, NH, NS>),
+                     dim3(static_cast<unsigned>(groups)), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), cu, offs, f, state_in, state_out, state_out2,
+                     fixed, o, N, H, n_slots, T_total);
   return hipGetLastError();
 }
 
@@ -677,13 +723,13 @@ template <int D, int C, Dt OUTD>
 hipError_t scan_t(const void* q, const void* k, const void* v, const int32_t* cu,
                   const int32_t* offs, const ChunkFactors& f, const float* state_in,
                   float* state_out, float* fixed, void* o, int N, int H, int n_slots, int T_total,
-                  int flags, hipStream_t stream) {
+                  hipStream_t stream) {
   const int64_t split_groups = (static_cast<int64_t>(N) * H + kXcds - 1) / kXcds * kXcds *
                                ScanCfg<D, C, 2>::NVB;
   const bool split = split_groups <= kSplitMaxGroups;
-#define GDR_SCAN_L(OUT_, NH_)                                                                      \
-  return scan_launch<D, C, OUTD, OUT_, NH_>(q, k, v, cu, offs, f, state_in, state_out, fixed, o,  \
-                                            N, H, n_slots, T_total, flags, stream)
+#define GDR_SCAN_L(OUT_, NH_)                                                                   \
+  return scan_launch<D, C, OUTD, OUT_, NH_>(q, k, v, cu, offs, f, state_in, state_out, nullptr, \
+                                            fixed, o, N, H, n_slots, T_total, stream)
   if (o) {
     if (split) GDR_SCAN_L(true, 2);
     GDR_SCAN_L(true, 1);
@@ -713,6 +759,10 @@ __global__ __launch_bounds__(256) void segment_ranges_kernel(
   offs_seg[m] = c;
 }
 
+// blockIdx.z picks one of kStartSlices slices of the state, so that the few
+// segment starts of a long sequence still spread over many compute units.
+constexpr int kStartSlices = 16;
+
 template <int D>
 __global__ __launch_bounds__(256) void segment_starts_kernel(const float* state_in,
                                                              const float* __restrict__ seg_end,
@@ -727,7 +777,9 @@ __global__ __launch_bounds__(256) void segment_starts_kernel(const float* state_
   else if (state_in)
     src = reinterpret_cast<const floatx4*>(state_in + (static_cast<size_t>(n) * H + h) * D * D);
   floatx4* dst = reinterpret_cast<floatx4*>(seg_start + (static_cast<size_t>(m) * H + h) * D * D);
-  for (int i = threadIdx.x; i < D * D / 4; i += blockDim.x)
+  constexpr int per = D * D / 4 / kStartSlices;
+  static_assert(per % 256 == 0 || per < 256, "slice");
+  for (int i = blockIdx.z * per + threadIdx.x; i < (blockIdx.z + 1) * per; i += blockDim.x)
     dst[i] = src ? src[i] : floatx4{0.f, 0.f, 0.f, 0.f};
 }
 
@@ -746,23 +798,38 @@ hipError_t launch_segment_starts(const float* state_in, const float* seg_end,
                                  float* seg_start, hipStream_t stream) {
   if (max_segs <= 0) return hipSuccess;
   if (d == 128)
-    hipLaunchKernelGGL(segment_starts_kernel<128>, dim3(max_segs, H), dim3(256), 0, stream,
-                       state_in, seg_end, seg_idx, H, seg_start);
+    hipLaunchKernelGGL(segment_starts_kernel<128>, dim3(max_segs, H, kStartSlices), dim3(256), 0,
+                       stream, state_in, seg_end, seg_idx, H, seg_start);
   else
-    hipLaunchKernelGGL(segment_starts_kernel<64>, dim3(max_segs, H), dim3(256), 0, stream,
-                       state_in, seg_end, seg_idx, H, seg_start);
+    hipLaunchKernelGGL(segment_starts_kernel<64>, dim3(max_segs, H, kStartSlices), dim3(256), 0,
+                       stream, state_in, seg_end, seg_idx, H, seg_start);
   return hipGetLastError();
+}
+
+hipError_t launch_chunk_scan_pair(const void* k, const void* v, const int32_t* cu_seqlens,
+                                  const int32_t* chunk_offsets, const ChunkFactors& f,
+                                  const float* state_in, float* state_out, float* transfer_out,
+                                  int N, int H, int d, int chunk, int n_slots, int T_total,
+                                  hipStream_t stream) {
+  if (chunk != 64) return hipErrorInvalidValue;
+  if (d == 128)
+    return scan_launch<128, 64, Dt::F32, false, 1, 2>(nullptr, k, v, cu_seqlens, chunk_offsets, f,
+                                                      state_in, state_out, transfer_out, nullptr,
+                                                      nullptr, N, H, n_slots, T_total, stream);
+  return scan_launch<64, 64, Dt::F32, false, 1, 2>(nullptr, k, v, cu_seqlens, chunk_offsets, f,
+                                                   state_in, state_out, transfer_out, nullptr,
+                                                   nullptr, N, H, n_slots, T_total, stream);
 }
 
 hipError_t launch_chunk_scan(const void* q, const void* k, const void* v,
                              const int32_t* cu_seqlens, const int32_t* chunk_offsets,
                              const ChunkFactors& f, const float* state_in, float* state_out,
                              float* fixed, void* o, int N, int H, int d, int chunk, int n_slots,
-                             int T_total, int out_dtype, int flags, hipStream_t stream) {
+                             int T_total, int out_dtype, hipStream_t stream) {
   if (chunk != 64) return hipErrorInvalidValue;
 #define GDR_SCAN(D_, OUT_)                                                                         \
   return scan_t<D_, 64, OUT_>(q, k, v, cu_seqlens, chunk_offsets, f, state_in, state_out, fixed, o, \
-                              N, H, n_slots, T_total, flags, stream)
+                              N, H, n_slots, T_total, stream)
   if (d == 128) {
     if (out_dtype == 0) GDR_SCAN(128, Dt::BF16);
     GDR_SCAN(128, Dt::F32);

@@ -207,10 +207,11 @@ size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int 
  *     (S M_c + L_c = gamma_C S + (diag(D) T diag(beta) (V - diag(gamma) K S^T))^T K,
  *     without forming M, L, W or Ut) and writes the outputs, the final states
  *     and, when given, fixed_out.  Taken for bf16 inputs at chunk 64; for long
- *     sequences at low parallelism as a segmented scan: the same pass over
- *     segments of whole chunks from zero (segment local states) and from the
- *     identity with v = 0 (segment transfer matrices), the segment-level
- *     fixup, and a final pass from every segment's true start.  When L_out or
+ *     sequences at low parallelism as a segmented scan: one pass over
+ *     segments of whole chunks carrying two chains per segment, from zero
+ *     (segment local states) and from the identity with v = 0 (segment
+ *     transfer matrices), the segment-level fixup, and a final pass from every
+ *     segment's true start.  When L_out or
  *     M_out is given, the chunk-local kernel of the chunk-parallel form writes
  *     them in parallel, before the scan.
  */
