@@ -563,12 +563,15 @@ struct ChunkWork {
     return t < C / 2 ? t * (C / 2) : (C / 2) * (C / 2) + (t - C / 2) * C;
   }
 
-  // T = (I + A)^{-1}, lower triangular, into the compact planes at Tl() (rows
+  // T = (I + A)^{-1}, lower triangular, into the compact plane at Tl() (rows
   // in operand-slot order, as P): wave j forms column block j by block
   // forward substitution,
   //   T_jj from the diagonal inversion,  T_ij = -T_ii sum_{j <= m < i} A_im T_mj,
   // every block in D-tile layout, which is the B operand of the next product.
-  // The blocks of the compact layout above the diagonal are zeroed.
+  // T is stored as one fp16 plane of kTScale T (round to nearest even; the
+  // unit diagonal is exact), the operand of the scan's U = T R with R / kTScale
+  // in two fp16 planes.  The blocks of the compact layout above the diagonal
+  // are zeroed.
   __device__ void solve_t() {
     static_assert(NT <= 4, "one column block per wave");
 #pragma unroll
@@ -607,20 +610,15 @@ struct ChunkWork {
       for (int i = j; i < NT; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          uint16_t sp[PT];
-          split_planes<PT>(X[i][e], sp);
           const int t = 16 * i + 4 * g4 + e;
-#pragma unroll
-          for (int p = 0; p < PT; ++p) Tl()[p * Cfg::TL_PLANE + tl_row(t) + col] = sp[p];
+          Tl()[tl_row(t) + col] = f16_bits(kTScale * X[i][e]);
         }
       // blocks above the diagonal that the compact layout stores: zeros
 #pragma unroll
       for (int i = 0; i < j; ++i) {
         if (i < NT / 2 && j >= NT / 2) continue;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int p = 0; p < PT; ++p) Tl()[p * Cfg::TL_PLANE + tl_row(16 * i + 4 * g4 + e) + col] = 0;
+        for (int e = 0; e < 4; ++e) Tl()[tl_row(16 * i + 4 * g4 + e) + col] = 0;
       }
     }
   }
@@ -945,14 +943,15 @@ __global__ __launch_bounds__(256, 2) void chunk_factors_kernel(
     float* gt = f.gate + slot * 4 * C;
     gt[w.tid] = w.sgam[w.tid];
     gt[C + w.tid] = w.sD[w.tid];
-    gt[2 * C + w.tid] = w.sb[w.tid];
+    gt[2 * C + w.tid] = w.sb[w.tid] * (1.f / kTScale);  // beta / kTScale (exact)
     gt[3 * C + w.tid] = 0.f;
   }
   __syncthreads();  // T and P planes complete
-  uint16_t* tg = f.t + slot * PT * TLP;
+  uint16_t* tg = f.t + slot * TLP;
   uint16_t* pg = f.p + slot * PT * TLP;
   for (int idx = w.tid; idx < PT * TLP / 8; idx += 256) {
-    *reinterpret_cast<uint4*>(tg + 8 * idx) = *reinterpret_cast<const uint4*>(w.Tl() + 8 * idx);
+    if (idx < TLP / 8)
+      *reinterpret_cast<uint4*>(tg + 8 * idx) = *reinterpret_cast<const uint4*>(w.Tl() + 8 * idx);
     *reinterpret_cast<uint4*>(pg + 8 * idx) = *reinterpret_cast<const uint4*>(w.Pp() + 8 * idx);
   }
 }

@@ -71,9 +71,14 @@ hipError_t launch_final_state(const float* state_in, const float* fixed,
 // rows t < C/2 keep their first C/2 columns, rows t >= C/2 all C (TL = 3 C^2 / 4
 // elements per plane); P rows store their contraction index in operand-slot
 // order (chunk.hip):
-//   t     [slots][H][2][TL]   T = (I + A)^{-1} as bf16 hi/lo planes
+//   t     [slots][H][TL]      kTScale T, T = (I + A)^{-1}, as one fp16 plane
 //   p     [slots][H][2][TL]   P = (Q K^T) (.) Gamma (s <= t) as bf16 hi/lo planes
-//   gate  [slots][H][4][C]    gamma_t, D_t, beta_t and zeros, fp32
+//   gate  [slots][H][4][C]    gamma_t, D_t, beta_t / kTScale and zeros, fp32
+// The scan forms U = T diag(beta) R as (kTScale T)(diag(beta / kTScale) R),
+// exactly the same product: the power-of-two scale moves the fp16 range of
+// the R planes up by kTScale (fp16 holds T with its unit diagonal exactly and
+// its other entries to 11 bits).
+constexpr float kTScale = 16.f;
 struct ChunkFactors {
   uint16_t* t;
   uint16_t* p;
@@ -88,7 +93,7 @@ inline ChunkFactorSizes chunk_factor_sizes(int slots, int H, int chunk) {
   const size_t n = static_cast<size_t>(slots) * H;
   const size_t c = static_cast<size_t>(chunk);
   const size_t tl = 3 * c * c / 4;
-  return {n * 2 * tl * 2, n * 2 * tl * 2, n * 4 * c * 4};
+  return {n * tl * 2, n * 2 * tl * 2, n * 4 * c * 4};
 }
 
 // Factors of every chunk slot < max_chunks (bf16 inputs, chunk 64).
@@ -100,7 +105,7 @@ hipError_t launch_chunk_factors(const void* q, const void* k, const float* g, co
 // Sequential scan over the chunks of every sequence from the factors and the
 // q, k, v inputs: outputs o (skipped when o is NULL), final states (skipped
 // when state_out is NULL), and (when fixed != NULL) the state at every chunk
-// end.  v == NULL takes v as zero.
+// end.
 hipError_t launch_chunk_scan(const void* q, const void* k, const void* v,
                              const int32_t* cu_seqlens, const int32_t* chunk_offsets,
                              const ChunkFactors& f, const float* state_in, float* state_out,

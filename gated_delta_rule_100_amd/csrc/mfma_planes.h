@@ -26,9 +26,21 @@ typedef unsigned short ushort8 __attribute__((ext_vector_type(8)));
 typedef unsigned short ushort4 __attribute__((ext_vector_type(4)));
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ floatx4 mfma16x16x32(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp16 operands (same lane layout): 11-bit significands for operands that are
+// not exact bf16 inputs and whose range fp16 holds.
+__device__ __forceinline__ floatx4 mfma16x16x32(halfx8 a, halfx8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// fp16 bit pattern of x (round to nearest even).
+__device__ __forceinline__ uint16_t f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
 }
 
 // 16x16x16 variant (lane (c, g): A[c][4g .. 4g+3], B[4g .. 4g+3][c]); its
@@ -140,6 +152,35 @@ __device__ __forceinline__ void split_planes(float x, uint16_t (&out)[P]) {
     out[p] = __builtin_bit_cast(uint16_t, hb);
     r = r - static_cast<float>(hb);
   }
+}
+
+// Two fp32 values as P planes of fp16 pairs (value a in the low half): each
+// plane rounds the residual of the planes before it to nearest even; two
+// planes keep ~22 significant bits.
+template <int P>
+__device__ __forceinline__ void split2_h(float a, float b, uint32_t (&out)[P]) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const f16x2 h = __builtin_convertvector(f32x2{a, b}, f16x2);
+    out[p] = __builtin_bit_cast(uint32_t, h);
+    if (p + 1 < P) {
+      a = a - static_cast<float>(h[0]);
+      b = b - static_cast<float>(h[1]);
+    }
+  }
+}
+
+// Split 8 fp32 values into P fp16x8 fragments.
+template <int P>
+__device__ __forceinline__ void split8_h(const float (&x)[8], halfx8 (&out)[P]) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  uint32_t w[4][P];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) split2_h<P>(x[2 * i], x[2 * i + 1], w[i]);
+#pragma unroll
+  for (int p = 0; p < P; ++p) out[p] = __builtin_bit_cast(halfx8, u32x4{w[0][p], w[1][p], w[2][p], w[3][p]});
 }
 
 // Split 8 fp32 values into P bf16x8 fragments.

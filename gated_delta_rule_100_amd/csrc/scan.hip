@@ -27,9 +27,11 @@
 // of S^T) in K S^T and as A (rows of S) in S Q^T.  Z, R and U are D tiles with
 // tokens as rows; two of them stacked are an operand fragment in slot order,
 // which is how R meets T (whose rows are stored in slot order) and U meets P
-// and K^T.  k, q, v are exact bf16; fp32 operands
-// are hi/lo planes.  The compute waves read only LDS and write their outputs
-// and states straight to global memory.
+// and K^T.  k, q, v are exact bf16; fp32 operands are hi/lo planes: bf16
+// planes, except in U = T R, where T is one fp16 plane and R two (fp16's
+// 11-bit significand holds T well enough for the 1e-3 budget, one bf16 plane
+// would not).  The compute waves read only LDS and write their outputs and
+// states straight to global memory.
 //
 // Copy waves.  Four more waves move each chunk's k, q, v rows, T, P and gates
 // into LDS with direct global-to-LDS loads, one chunk ahead: LDS holds two
@@ -72,13 +74,14 @@ struct ScanCfg {
   static constexpr int JT = ND / NH;                    // 16-wide column tiles per wave
   static constexpr int NO = NT / NH;                    // output token tiles per wave
   // T and P planes: rows t < C/2 keep their first C/2 columns (the rest is
-  // above the diagonal), rows t >= C/2 keep all C.
+  // above the diagonal), rows t >= C/2 keep all C.  T is one fp16 plane, P
+  // two bf16 planes.
   static constexpr int TL_LO = (C / 2) * (C / 2);
   static constexpr int TL = TL_LO + (C / 2) * C;
   // regions of one chunk buffer (bytes); each a whole number of 1 KiB blocks
   static constexpr int K_BYTES = C * D * 2;
   static constexpr int Q_BYTES = C * D * 2;
-  static constexpr int T_BYTES = 2 * TL * 2;
+  static constexpr int T_BYTES = TL * 2;
   static constexpr int P_BYTES = 2 * TL * 2;
   static constexpr int V_BYTES = C * ROWS * 2;
   static constexpr int G_BYTES = 4 * C * 4;  // gamma, D, beta, zeros
@@ -95,13 +98,16 @@ struct ScanCfg {
   static constexpr int OFF_X = 2 * BUF;
   static constexpr int BYTES = 2 * BUF + X_SLOTS * kComputeWaves * 64 * 16;
   // copy instructions (1 KiB each) per region, and each copy wave's share
-  static constexpr int NK = K_BYTES / 1024, NQ = Q_BYTES / 1024, NTL = T_BYTES / 1024;
-  static constexpr int NV = V_BYTES / 1024;
-  static constexpr int SK = NK / kCopyWaves, SQ = NQ / kCopyWaves, STL = NTL / kCopyWaves;
+  // (T: the first NTT % kCopyWaves copy waves issue one more)
+  static constexpr int NK = K_BYTES / 1024, NQ = Q_BYTES / 1024, NTT = T_BYTES / 1024;
+  static constexpr int NP = P_BYTES / 1024, NV = V_BYTES / 1024;
+  static constexpr int SK = NK / kCopyWaves, SQ = NQ / kCopyWaves, SP = NP / kCopyWaves;
+  static constexpr int STT = (NTT + kCopyWaves - 1) / kCopyWaves;
   static constexpr int SV = NV / kCopyWaves;
   static_assert(C == 64 && (D == 64 || D == 128) && (NH == 1 || NH == 2), "shape");
-  static_assert(K_BYTES % (1024 * kCopyWaves) == 0 && T_BYTES % (1024 * kCopyWaves) == 0 &&
-                    V_BYTES % (1024 * kCopyWaves) == 0 && G_BYTES == 1024,
+  static_assert(K_BYTES % (1024 * kCopyWaves) == 0 && P_BYTES % (1024 * kCopyWaves) == 0 &&
+                    T_BYTES % 1024 == 0 && V_BYTES % (1024 * kCopyWaves) == 0 &&
+                    G_BYTES == 1024,
                 "copy tiling");
   static_assert(BYTES <= 160 * 1024, "LDS");
 };
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
     int krow[Cfg::SK], qrow[Cfg::SQ], vrow[Cfg::SV];
     uint32_t kcol[Cfg::SK], qcol[Cfg::SQ], vcol[Cfg::SV];
     uint32_t kfull[Cfg::SK], qfull[Cfg::SQ], vfull[Cfg::SV];
-    uint32_t toff[Cfg::STL];
+    uint32_t toff[Cfg::STT], poff[Cfg::SP];
 #pragma unroll
     for (int x = 0; x < Cfg::SK; ++x) {
       const int p = 64 * (cw + kCopyWaves * x) + lane, t = p / CHD, pc = p % CHD;
@@ -265,9 +271,8 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
       vcol[x] = 2u * (Cfg::ROWS * vb) + 16u * (pc ^ swz_tr(t, CHV));
       vfull[x] = static_cast<uint32_t>(t) * row_bytes + vcol[x];
     }
-#pragma unroll
-    for (int x = 0; x < Cfg::STL; ++x) {
-      const int p = 64 * (cw + kCopyWaves * x) + lane;
+    // byte offset of the 16-byte piece p of a compact plane sequence
+    auto tl_piece = [&](int p) {
       const int pl = p / (TL / 8), rr = p % (TL / 8);
       int t, pc, ch;
       if (rr < Cfg::TL_LO / 8) {
@@ -279,8 +284,15 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
         pc = (rr - Cfg::TL_LO / 8) % CHC;
         ch = CHC;
       }
-      toff[x] = 2u * (pl * TL + tl_row<C>(t) + 8 * (pc ^ swz(t, ch)));
+      return 2u * (pl * TL + tl_row<C>(t) + 8 * (pc ^ swz(t, ch)));
+    };
+#pragma unroll
+    for (int x = 0; x < Cfg::STT; ++x) {
+      const int i = cw + kCopyWaves * x;
+      toff[x] = tl_piece(64 * (i < Cfg::NTT ? i : 0) + lane);
     }
+#pragma unroll
+    for (int x = 0; x < Cfg::SP; ++x) poff[x] = tl_piece(64 * (cw + kCopyWaves * x) + lane);
     const uint32_t goff = 16u * lane;
     // Chunk s into buffer (s - c0) & 1.  In a chunk shorter than C, rows past
     // its end repeat its last token (their beta is zero, so they leave U, O
@@ -296,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
       const char* qs = reinterpret_cast<const char*>(q + tbase);
       const char* vs = reinterpret_cast<const char*>(v + tbase);
       const size_t slot = static_cast<size_t>(s) * H + h;
-      const char* ts = reinterpret_cast<const char*>(f.t + slot * 2 * TL);
+      const char* ts = reinterpret_cast<const char*>(f.t + slot * TL);
       const char* ps = reinterpret_cast<const char*>(f.p + slot * 2 * TL);
       unsigned char* buf = smem + ((s - c0) & 1) * Cfg::BUF;
       if (last == C - 1) {
@@ -306,10 +318,8 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
 #pragma unroll
           for (int x = 0; x < Cfg::SQ; ++x) copy16(qs + qfull[x], buf + Cfg::OFF_Q + 1024 * (cw + kCopyWaves * x));
         }
-        if (v) {
 #pragma unroll
-          for (int x = 0; x < Cfg::SV; ++x) copy16(vs + vfull[x], buf + Cfg::OFF_V + 1024 * (cw + kCopyWaves * x));
-        }
+        for (int x = 0; x < Cfg::SV; ++x) copy16(vs + vfull[x], buf + Cfg::OFF_V + 1024 * (cw + kCopyWaves * x));
       } else {
 #pragma unroll
         for (int x = 0; x < Cfg::SK; ++x)
@@ -321,18 +331,18 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
             copy16(qs + static_cast<uint32_t>(qrow[x] < last ? qrow[x] : last) * row_bytes + qcol[x],
                    buf + Cfg::OFF_Q + 1024 * (cw + kCopyWaves * x));
         }
-        if (v) {
 #pragma unroll
-          for (int x = 0; x < Cfg::SV; ++x)
-            copy16(vs + static_cast<uint32_t>(vrow[x] < last ? vrow[x] : last) * row_bytes + vcol[x],
-                   buf + Cfg::OFF_V + 1024 * (cw + kCopyWaves * x));
-        }
+        for (int x = 0; x < Cfg::SV; ++x)
+          copy16(vs + static_cast<uint32_t>(vrow[x] < last ? vrow[x] : last) * row_bytes + vcol[x],
+                 buf + Cfg::OFF_V + 1024 * (cw + kCopyWaves * x));
       }
 #pragma unroll
-      for (int x = 0; x < Cfg::STL; ++x) copy16(ts + toff[x], buf + Cfg::OFF_T + 1024 * (cw + kCopyWaves * x));
+      for (int x = 0; x < Cfg::STT; ++x)
+        if (cw + kCopyWaves * x < Cfg::NTT)  // wave-uniform
+          copy16(ts + toff[x], buf + Cfg::OFF_T + 1024 * (cw + kCopyWaves * x));
       if constexpr (OUT) {
 #pragma unroll
-        for (int x = 0; x < Cfg::STL; ++x) copy16(ps + toff[x], buf + Cfg::OFF_P + 1024 * (cw + kCopyWaves * x));
+        for (int x = 0; x < Cfg::SP; ++x) copy16(ps + poff[x], buf + Cfg::OFF_P + 1024 * (cw + kCopyWaves * x));
       }
       if (cw == 0) copy16(reinterpret_cast<const char*>(f.gate + slot * 4 * C) + goff, buf + Cfg::OFF_G);
     };
@@ -507,20 +517,19 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
           }
         }
 
-        // R = diag(beta) (V - diag(gamma) Z) (v rows 16 a + 4 g + e at this
-        // lane's state row: a transpose read), as operand planes of 32 tokens
-        // (two stacked D tiles, slot order), then U = T R over the lower blocks:
-        // T rows are stored in slot order, so the T fragment of row 16 i + c and
-        // 32-block m is one 16-byte read per plane.  Both column halves form
-        // the same R and U.
+        // R = diag(beta / kTScale) (V - diag(gamma) Z) (v rows 16 a + 4 g + e
+        // at this lane's state row: a transpose read), as two fp16 operand
+        // planes of 32 tokens (two stacked D tiles, slot order), then
+        // U = (kTScale T) R over the lower blocks: T rows are stored in slot
+        // order, so the T fragment of row 16 i + c and 32-block m is one
+        // 16-byte read.  Both column halves form the same R and U.
         // (the second chain has v = 0)
         floatx4 R[NS][NT];
 #pragma unroll
         for (int a = 0; a < NT; ++a) {
           const floatx4 gam = *reinterpret_cast<const floatx4*>(Gl + 16 * a + 4 * g4);
           const floatx4 bet = *reinterpret_cast<const floatx4*>(Gl + 2 * C + 16 * a + 4 * g4);
-          const shortx4 vv = v ? read_tr4(Vl, Cfg::ROWS, CHV, 16 * a, 16 * rt, c16, g4)
-                               : shortx4{0, 0, 0, 0};
+          const shortx4 vv = read_tr4(Vl, Cfg::ROWS, CHV, 16 * a, 16 * rt, c16, g4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             R[0][a][e] =
@@ -528,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
             if constexpr (NS == 2) R[1][a][e] = bet[e] * (0.f - gam[e] * Z[1][a][e]);
           }
         }
-        bf16x8 rb[NS][CB][2];
+        halfx8 rb[NS][CB][2];
 #pragma unroll
         for (int ch = 0; ch < NS; ++ch)
 #pragma unroll
@@ -536,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
             float x[8];
 #pragma unroll
             for (int e2 = 0; e2 < 8; ++e2) x[e2] = R[ch][2 * m + e2 / 4][e2 & 3];
-            split8<2>(x, rb[ch][m]);
+            split8_h<2>(x, rb[ch][m]);
           }
         floatx4 U[NS][NT];
 #pragma unroll
@@ -546,16 +555,12 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
           for (int ch = 0; ch < NS; ++ch) U[ch][i] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int m = 0; m <= i / 2; ++m) {
-            bf16x8 tf[2];
-#pragma unroll
-            for (int p = 0; p < 2; ++p)
-              tf[p] = *reinterpret_cast<const bf16x8*>(Tl + p * TL + tl_row<C>(t) +
-                                                       8 * ((4 * m + g4) ^ swz(t, cw16)));
+            const halfx8 tf = *reinterpret_cast<const halfx8*>(Tl + tl_row<C>(t) +
+                                                               8 * ((4 * m + g4) ^ swz(t, cw16)));
 #pragma unroll
             for (int ch = 0; ch < NS; ++ch) {
-              U[ch][i] = mfma16x16x32(tf[1], rb[ch][m][0], U[ch][i]);
-              U[ch][i] = mfma16x16x32(tf[0], rb[ch][m][1], U[ch][i]);
-              U[ch][i] = mfma16x16x32(tf[0], rb[ch][m][0], U[ch][i]);
+              U[ch][i] = mfma16x16x32(tf, rb[ch][m][1], U[ch][i]);
+              U[ch][i] = mfma16x16x32(tf, rb[ch][m][0], U[ch][i]);
             }
           }
         }
