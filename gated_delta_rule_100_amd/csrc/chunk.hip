@@ -376,7 +376,8 @@ struct ChunkWork {
   //   P = (Q K^T) (.) Gamma (s <= t, zero elsewhere) as planes in the compact
   //     lower layout (rows t < C/2 keep C/2 columns), each row in operand-slot
   //     order: column 16 tj + c of 32-block tj/2 sits at slot
-  //     8 (c/4) + 4 (tj % 2) + c % 4.
+  //     8 (c/4) + 4 (tj % 2) + c % 4; in LDS the 16-byte pieces of a row are
+  //     permuted (tl_piece).
   __device__ void gram_t(const bf16x8 (&kf)[NT][KB][PI], const bf16x8 (&qf)[NT][KB][PI]) {
     static_assert(TF, "factors layout");
     int tcount = 0;
@@ -436,7 +437,7 @@ struct ChunkWork {
         uint32_t lo[PT], hi[PT];
         split2<PT>(x[0], x[1], lo);
         split2<PT>(x[2], x[3], hi);
-        uint16_t* dst = Pp() + tl_row(t) + 32 * (tj >> 1) + 8 * g4 + 4 * (tj & 1);
+        uint16_t* dst = Pp() + tl_piece(t, 4 * (tj >> 1) + g4) + 4 * (tj & 1);
 #pragma unroll
         for (int p = 0; p < PT; ++p)
           *reinterpret_cast<uint2*>(dst + p * Cfg::TL_PLANE) = make_uint2(lo[p], hi[p]);
@@ -562,6 +563,13 @@ struct ChunkWork {
   static __device__ __forceinline__ int tl_row(int t) {
     return t < C / 2 ? t * (C / 2) : (C / 2) * (C / 2) + (t - C / 2) * C;
   }
+  // LDS position of 16-byte piece pc of row t in the factors kernel's compact
+  // planes: pieces permuted by row so that the 16 rows one write touches fall
+  // into distinct banks (rows of 64 bytes: XOR (t/4) % 4; of 128: (t/2) % 8).
+  static __device__ __forceinline__ int tl_piece(int t, int pc) {
+    const int sw = t < C / 2 ? (t >> 2) & (C / 16 - 1) : (t >> 1) & (C / 8 - 1);
+    return tl_row(t) + 8 * (pc ^ sw);
+  }
 
   // T = (I + A)^{-1}, lower triangular, into the compact plane at Tl() (rows
   // in operand-slot order, as P): wave j forms column block j by block
@@ -611,14 +619,14 @@ struct ChunkWork {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 16 * i + 4 * g4 + e;
-          Tl()[tl_row(t) + col] = f16_bits(kTScale * X[i][e]);
+          Tl()[tl_piece(t, col >> 3) + (col & 7)] = f16_bits(kTScale * X[i][e]);
         }
       // blocks above the diagonal that the compact layout stores: zeros
 #pragma unroll
       for (int i = 0; i < j; ++i) {
         if (i < NT / 2 && j >= NT / 2) continue;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Tl()[tl_row(16 * i + 4 * g4 + e) + col] = 0;
+        for (int e = 0; e < 4; ++e) Tl()[tl_piece(16 * i + 4 * g4 + e, col >> 3) + (col & 7)] = 0;
       }
     }
   }
@@ -949,10 +957,17 @@ __global__ __launch_bounds__(256, 2) void chunk_factors_kernel(
   __syncthreads();  // T and P planes complete
   uint16_t* tg = f.t + slot * TLP;
   uint16_t* pg = f.p + slot * PT * TLP;
+  // global piece idx (the compact layout, unpermuted) from its LDS position
   for (int idx = w.tid; idx < PT * TLP / 8; idx += 256) {
+    const int pl = idx / (TLP / 8), r = idx % (TLP / 8);
+    constexpr int LO = (C / 2) * (C / 2) / 8;  // pieces of the rows t < C/2
+    const int t = r < LO ? r / (C / 16) : C / 2 + (r - LO) / (C / 8);
+    const int pc = r < LO ? r % (C / 16) : (r - LO) % (C / 8);
+    const int src = W_::tl_piece(t, pc);
     if (idx < TLP / 8)
-      *reinterpret_cast<uint4*>(tg + 8 * idx) = *reinterpret_cast<const uint4*>(w.Tl() + 8 * idx);
-    *reinterpret_cast<uint4*>(pg + 8 * idx) = *reinterpret_cast<const uint4*>(w.Pp() + 8 * idx);
+      *reinterpret_cast<uint4*>(tg + 8 * idx) = *reinterpret_cast<const uint4*>(w.Tl() + src);
+    *reinterpret_cast<uint4*>(pg + 8 * idx) =
+        *reinterpret_cast<const uint4*>(w.Pp() + pl * TLP + src);
   }
 }
 
