@@ -213,7 +213,11 @@ size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int 
  *     transfer matrices), the segment-level fixup, and a final pass from every
  *     segment's true start.  When L_out or
  *     M_out is given, the chunk-local kernel of the chunk-parallel form writes
- *     them in parallel, before the scan.
+ *     them in parallel, before the scan.  The scan holds T as one fp16 plane
+ *     (scaled by 16) and beta (V - diag(gamma) K S^T) / 16 as two fp16 planes:
+ *     entries of beta (v - gamma S k) beyond about 1e6 in magnitude overflow
+ *     to non-finite results (keys are expected L2-normalised, as the method
+ *     assumes).
  */
 gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v,
                              const float* g, const float* beta,

@@ -120,6 +120,21 @@ def test_prefill_matches_oracle(name, schedule):
     check_against_oracle(d, res, d["chunk"], check_locals=d["T"] <= 20000)
 
 
+@pytest.mark.parametrize("seqlens", [[256, 130, 1], [16384]])
+def test_prefill_large_values(seqlens):
+    # v and the initial state 4096 times the recipe's (exact in bf16 and fp32):
+    # the scan's fp16 operand planes of R / 16 in U = T R then reach several
+    # hundred, and the errors stay within the tolerance relative to max|ref|;
+    # [16384] takes the segmented scan
+    from gdr_synth import bf16_bits_from_f32
+    d = workload(2, seed=120, seqlens=seqlens, H=2, gate="slow")
+    d["v"] = bf16_bits_from_f32((oracle.bf16_to_f64(d["v"]) * 4096.0).astype(np.float32))
+    d["state0"] = (d["state0"] * np.float32(4096.0)).astype(np.float32)
+    say(f"prefill with 4096-fold v and state: T={d['T']} N={d['N']} H={d['H']}")
+    res = run_prefill(d, schedule="scan")
+    check_against_oracle(d, res, d["chunk"], check_locals=False)
+
+
 @pytest.mark.parametrize("schedule", SCHEDULES)
 def test_prefill_without_initial_state(schedule):
     d = workload(2, seed=110, seqlens=[130, 64, 0, 5], H=2, gate="slow")
