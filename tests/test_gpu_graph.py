@@ -110,3 +110,41 @@ def test_decode_in_graph():
         di["g"].copy_(gb if r % 2 == 0 else gb * 0.5)
 
     _check_replays(g, refill, (o, st), expected)
+
+
+@pytest.mark.parametrize("T, inter", [(8, False), (3, True)])
+def test_decode_mtp_in_graph(T, inter):
+    # T = 8 without per-token states takes the chunked kernel, T = 3 with them
+    # the token-by-token one
+    import gated_delta_rule_100_amd as gdr
+    from gdr_synth import generate
+    N, H, D = 8, 4, 128
+    data = generate([T] * N, H, D, D, dtype="bf16", state0=True, seed=952, gate="slow")
+    di = dev_inputs(data)
+    q, k, v = (di[x].view(N, T, H, D) for x in ("q", "k", "v"))
+    g, b = di["g"].view(N, T, H), di["beta"].view(N, T, H)
+    say(f"multi-token decode T={T} captured in a graph, {REPLAYS} replays")
+    s0 = di["state0"].clone()
+    st = s0.clone()
+    o = torch.empty(N, T, H, D, device="cuda")
+    I = torch.empty(N, T, H, D, D, device="cuda") if inter else None
+    gb = g.clone()
+    expected = []
+    for gg in (gb, gb * 0.5):
+        st.copy_(s0)
+        g.copy_(gg)
+        gdr.gdr_decode_mtp(q, k, v, g, b, st, st, o, I)
+        torch.cuda.synchronize()
+        expected.append((o.clone(), st.clone()) + ((I.clone(),) if inter else ()))
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=s):
+        gdr.gdr_decode_mtp(q, k, v, g, b, st, st, o, I, stream=s)
+    torch.cuda.synchronize()
+
+    def refill(r):
+        st.copy_(s0)  # updated in place: restart it
+        g.copy_(gb if r % 2 == 0 else gb * 0.5)
+
+    _check_replays(graph, refill, (o, st) + ((I,) if inter else ()), expected)
