@@ -277,6 +277,8 @@ __global__ __launch_bounds__(64 * kMtpWaves, 5) void mtp_chunk_kernel(
   __shared__ __align__(16) float sKQ[16 * LDK];  // rows 0-7: k_t, rows 8-15: q_t (zero past T)
   __shared__ __align__(16) float sF[F_N];
   __shared__ __align__(16) float sX[NW][16 * XLD];
+  constexpr int TLD = 36;  // padded row of the per-wave store staging (floats)
+  __shared__ __align__(16) float sT[NW][16 * TLD];
 
   const int pair = blockIdx.x / WPP, r0 = (blockIdx.x % WPP) * kMtpRows;
   if (pair >= NH) return;
@@ -448,10 +450,25 @@ __global__ __launch_bounds__(64 * kMtpWaves, 5) void mtp_chunk_kernel(
     st[kt] = acc;
   }
   if (state_out) {
+    // The state leaves in 128-byte row pieces: the wave's rows pass through
+    // its own LDS region two column tiles at a time, so that each store
+    // instruction covers 8 rows x 128 B where the matrix-core layout covers
+    // 16 rows x 64 B (which writes at about 60% of the rate, in-place copy of
+    // the same bytes).  The region is the wave's alone and LDS accesses of a
+    // wave complete in order, so no barrier is needed.
     floatx4* Sout = reinterpret_cast<floatx4*>(state_out + static_cast<size_t>(pair) * DV * DK);
+    float* W = sT[wave];
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-      __builtin_nontemporal_store(st[kt], &Sout[((rbase + c) * DK + 16 * kt + 4 * gq) / 4]);
+    for (int p = 0; p < KT / 2; ++p) {
+      *reinterpret_cast<floatx4*>(W + c * TLD + 4 * gq) = st[2 * p];
+      *reinterpret_cast<floatx4*>(W + c * TLD + 16 + 4 * gq) = st[2 * p + 1];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int row = 8 * hh + (lane >> 3), col = 4 * (lane & 7);
+        const floatx4 x = *reinterpret_cast<const floatx4*>(W + row * TLD + col);
+        __builtin_nontemporal_store(x, &Sout[((rbase + row) * DK + 32 * p + col) / 4]);
+      }
+    }
   }
 }
 
