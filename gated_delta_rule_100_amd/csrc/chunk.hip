@@ -686,10 +686,22 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
   // keeps every operand of order one, so M keeps fp32 precision when gamma_C
   // is near the bottom of the fp32 range (operands of that size would have
   // their last bf16 plane below the normal range, where the matrix cores
-  // flush it).  Rows of this wave's feature tiles; 16 lanes store 64
-  // contiguous bytes of a row.
+  // flush it).  Rows of this wave's feature tiles.
+  //
+  // The tiles leave in 256-byte row pieces: a wave stages four column tiles
+  // (16 rows x 64 columns of L and of M) in LDS that the V rows and the A
+  // blocks no longer need, and each store instruction then covers 4 rows x
+  // 256 B instead of the D-tile layout's 4 rows x 64 B (which writes at about
+  // 60% of the rate in an in-place copy of the same bytes).  Each wave owns
+  // its staging rows and LDS accesses of a wave complete in order, so only the
+  // barrier that retires V and A is needed.
+  constexpr int SLD = 68;                      // padded staging row (floats)
+  constexpr int STAGE = 2 * 16 * SLD;          // floats per wave: L, then M
+  constexpr bool STAGED = Cfg::OFF_GATE - Cfg::OFF_VR >= 4 * STAGE * 4 && Cfg::ND % 4 == 0;
   const float gam_end = w.sgam[C - 1];
   const size_t base = (static_cast<size_t>(cid) * H + h) * D * D;
+  if constexpr (STAGED) __syncthreads();  // V rows and A blocks are dead
+  float* stg = reinterpret_cast<float*>(smem + Cfg::OFF_VR) + w.wave * STAGE;
 #pragma unroll
   for (int bb = 0; bb < Cfg::DPW; ++bb) {
     const int b = w.wave + 4 * bb;
@@ -709,11 +721,33 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
         mma_planes<Cfg::PT, Cfg::PI>(m, AW[kb], kf);
       }
       const int i0 = 16 * b + 4 * w.g4, j = 16 * bj + w.c16;
+      if constexpr (STAGED) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const size_t at = base + static_cast<size_t>(i0 + e) * D + j;
-        if (Lout) Lout[at] = l[e];
-        if (Mout) Mout[at] = gam_end * ((i0 + e == j ? 1.f : 0.f) - m[e]);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * w.g4 + e, cc = 16 * (bj & 3) + w.c16;
+          stg[r * SLD + cc] = l[e];
+          stg[16 * SLD + r * SLD + cc] = gam_end * ((i0 + e == j ? 1.f : 0.f) - m[e]);
+        }
+        if ((bj & 3) == 3) {  // four column tiles staged: 16 rows x 256 B of each
+          const int lane = w.tid & 63;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * i + (lane >> 4), cc = 4 * (lane & 15);
+            const size_t at = base + static_cast<size_t>(16 * b + r) * D + 64 * (bj >> 2) + cc;
+            if (Lout)
+              *reinterpret_cast<floatx4*>(Lout + at) = *reinterpret_cast<const floatx4*>(stg + r * SLD + cc);
+            if (Mout)
+              *reinterpret_cast<floatx4*>(Mout + at) =
+                  *reinterpret_cast<const floatx4*>(stg + 16 * SLD + r * SLD + cc);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const size_t at = base + static_cast<size_t>(i0 + e) * D + j;
+          if (Lout) Lout[at] = l[e];
+          if (Mout) Mout[at] = gam_end * ((i0 + e == j ? 1.f : 0.f) - m[e]);
+        }
       }
     }
   }
