@@ -277,7 +277,7 @@ __global__ __launch_bounds__(64 * kMtpWaves, 5) void mtp_chunk_kernel(
   __shared__ __align__(16) float sKQ[16 * LDK];  // rows 0-7: k_t, rows 8-15: q_t (zero past T)
   __shared__ __align__(16) float sF[F_N];
   __shared__ __align__(16) float sX[NW][16 * XLD];
-  constexpr int TLD = 36;  // padded row of the per-wave store staging (floats)
+  constexpr int TLD = 68;  // padded row of the per-wave state staging (floats)
   __shared__ __align__(16) float sT[NW][16 * TLD];
 
   const int pair = blockIdx.x / WPP, r0 = (blockIdx.x % WPP) * kMtpRows;
@@ -307,12 +307,17 @@ __global__ __launch_bounds__(64 * kMtpWaves, 5) void mtp_chunk_kernel(
     for (int e = 0; e < 4; ++e)
       vv[e] = load_scalar<IN>(v, ((tok0 + c) * H + h) * DV + rbase + 4 * gq + e);
   }
-  // this lane's state row, 16-column tiles: S[row c][16 kt + 4 gq + e]
+  // The state arrives in 256-byte row pieces (an instruction covers 4 rows x
+  // 256 B: register j holds row 4 (j % 4) + lane / 16, columns
+  // 64 (j / 4) + 4 (lane % 16)); the wave's own LDS rows turn it into the
+  // matrix-core layout below, S[row c][16 kt + 4 gq + e], which read straight
+  // from memory covers only 16 rows x 64 B per instruction.
   const floatx4* Sin = reinterpret_cast<const floatx4*>(state_in + static_cast<size_t>(pair) * DV * DK);
-  floatx4 st[KT];
+  floatx4 ld[KT];
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt)
-    st[kt] = __builtin_nontemporal_load(&Sin[((rbase + c) * DK + 16 * kt + 4 * gq) / 4]);
+  for (int j = 0; j < KT; ++j)
+    ld[j] = __builtin_nontemporal_load(
+        &Sin[((rbase + 4 * (j & 3) + (lane >> 4)) * DK + 64 * (j >> 2) + 4 * (lane & 15)) / 4]);
 
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
@@ -377,6 +382,20 @@ __global__ __launch_bounds__(64 * kMtpWaves, 5) void mtp_chunk_kernel(
     for (int t = 0; t < kMtpMaxT; ++t) sF[F_TINV + 8 * t + j] = x[t];
   }
   lds_barrier();
+
+  // 64 columns at a time through the wave's staging rows (its own; LDS
+  // accesses of a wave complete in order)
+  float* W = sT[wave];
+  floatx4 st[KT];
+#pragma unroll
+  for (int v = 0; v < KT / 4; ++v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<floatx4*>(W + (4 * i + (lane >> 4)) * TLD + 4 * (lane & 15)) = ld[4 * v + i];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      st[4 * v + t] = *reinterpret_cast<const floatx4*>(W + c * TLD + 16 * t + 4 * gq);
+  }
 
   // [Z | Y] = S [K; Q]^T: lane (c, gq) ends with row 4 gq + e of the wave and
   // column c (token c of Z for c < 8, token c - 8 of Y for c >= 8).
@@ -450,23 +469,21 @@ __global__ __launch_bounds__(64 * kMtpWaves, 5) void mtp_chunk_kernel(
     st[kt] = acc;
   }
   if (state_out) {
-    // The state leaves in 128-byte row pieces: the wave's rows pass through
-    // its own LDS region two column tiles at a time, so that each store
-    // instruction covers 8 rows x 128 B where the matrix-core layout covers
-    // 16 rows x 64 B (which writes at about 60% of the rate, in-place copy of
-    // the same bytes).  The region is the wave's alone and LDS accesses of a
-    // wave complete in order, so no barrier is needed.
+    // back through the staging rows, leaving as it arrived: each store
+    // instruction covers 4 rows x 256 B, where the matrix-core layout covers
+    // 16 rows x 64 B (about 60% of the write rate in an in-place copy of the
+    // same bytes)
     floatx4* Sout = reinterpret_cast<floatx4*>(state_out + static_cast<size_t>(pair) * DV * DK);
-    float* W = sT[wave];
 #pragma unroll
-    for (int p = 0; p < KT / 2; ++p) {
-      *reinterpret_cast<floatx4*>(W + c * TLD + 4 * gq) = st[2 * p];
-      *reinterpret_cast<floatx4*>(W + c * TLD + 16 + 4 * gq) = st[2 * p + 1];
+    for (int v = 0; v < KT / 4; ++v) {
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int row = 8 * hh + (lane >> 3), col = 4 * (lane & 7);
+      for (int t = 0; t < 4; ++t)
+        *reinterpret_cast<floatx4*>(W + c * TLD + 16 * t + 4 * gq) = st[4 * v + t];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * i + (lane >> 4), col = 4 * (lane & 15);
         const floatx4 x = *reinterpret_cast<const floatx4*>(W + row * TLD + col);
-        __builtin_nontemporal_store(x, &Sout[((rbase + row) * DK + 32 * p + col) / 4]);
+        __builtin_nontemporal_store(x, &Sout[((rbase + row) * DK + 64 * v + col) / 4]);
       }
     }
   }
