@@ -272,16 +272,20 @@ struct ChunkWork {
     *(tid < C ? sb + tid : spare + 1) = bv * keep;
     lds_barrier();  // row loads may stay in flight
     if (tid < C) {
-      // Sequential prefix in a fixed order, so every thread forms the same
-      // G_C, accumulated in fp64: the decays e^{G} have a relative error equal
-      // to the absolute error of G, and an fp32 prefix over 64 gates carries
-      // about |G| 2^-24 per step (about 1e-5 at G = -55), which would show in
-      // gamma_C and so in M.  gamma and D come from the fp64 sums, rounded once.
-      double G = 0.0, Gt = 0.0;
-      for (int s = 0; s < C; ++s) {
-        G += static_cast<double>(sg[s]);
-        if (s == tid) Gt = G;
+      // Inclusive prefix over the chunk's lanes (one wave; a fixed shuffle
+      // tree, so the result is deterministic), accumulated in fp64: the decays
+      // e^{G} have a relative error equal to the absolute error of G, and an
+      // fp32 prefix over 64 gates carries about |G| 2^-24 per step (about 1e-5
+      // at G = -55), which would show in gamma_C and so in M.  Every lane takes
+      // G_C from the last lane.  gamma and D come from the fp64 sums, rounded
+      // once.
+      double Gt = static_cast<double>(sg[tid]);
+#pragma unroll
+      for (int off = 1; off < C; off <<= 1) {
+        const double y = __shfl_up(Gt, off, C);
+        if ((tid & (C - 1)) >= off) Gt += y;
       }
+      const double G = __shfl(Gt, C - 1, C);
       const float gam = static_cast<float>(exp(Gt));
       sG[tid] = static_cast<float>(Gt);
       sgam[tid] = gam;

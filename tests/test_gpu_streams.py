@@ -20,8 +20,9 @@ def _prefill(gdr, d, di, lm, stream=None):
     o = torch.empty(T, H, D, device="cuda")
     so = torch.empty(N, H, D, D, device="cuda")
     mc = gdr.gdr_max_chunks(T, N, C)
-    L = torch.empty(mc, H, D, D, device="cuda") if lm else None
-    M = torch.empty(mc, H, D, D, device="cuda") if lm else None
+    # zero-filled: chunk slots past the batch's chunks are not written
+    L = torch.zeros(mc, H, D, D, device="cuda") if lm else None
+    M = torch.zeros(mc, H, D, D, device="cuda") if lm else None
     ws = torch.empty(gdr.gdr_chunk_prefill_workspace_bytes(T, N, H, D, D, C, gdr.GDR_BF16),
                      dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
