@@ -46,7 +46,7 @@ def test_prefill_in_graph(entry):
     o = torch.empty(T, H, D, device="cuda")
     sout = torch.empty(N, H, D, D, device="cuda")
     mc = gdr.gdr_max_chunks(T, N, C)
-    F = torch.empty(mc, H, D, D, device="cuda")
+    F = torch.zeros(mc, H, D, D, device="cuda")  # slots past the batch's chunks stay zero
     ws = torch.empty(gdr.gdr_chunk_prefill_workspace_bytes(T, N, H, D, D, C, gdr.GDR_BF16),
                      dtype=torch.uint8, device="cuda")
     q0, v0 = di["q"].clone(), di["v"].clone()

@@ -83,6 +83,10 @@ CASES = {
     "varlen-skewed-H32": (3, dict(seqlens=[4000, 50, 300, 64, 1, 0, 700, 129], H=32)),
     "varlen-skewed-H32-slow": (3, dict(seqlens=[70, 3100, 0, 1100, 64, 640, 1, 9], H=32,
                                        gate="slow")),
+    # 64 sequences (the most whose chunk layout the scan kernels form
+    # themselves) and 65 (the layout kernel runs first), with empty ones
+    "varlen-64-sequences": (3, dict(seqlens=[(37 * i) % 150 for i in range(64)], H=2)),
+    "varlen-65-sequences": (3, dict(seqlens=[(41 * i) % 170 for i in range(65)], H=2)),
     # in-chunk decays far below e^-87: decay factors and gamma underflow
     "steep-gates-ragged": (2, dict(seqlens=[200, 130, 64, 5], H=2, gate="steep")),
     "d64-C64-bf16": (2, dict(seqlens=[150, 64, 3], H=3, dk=64, dv=64, gate="slow")),
