@@ -278,15 +278,8 @@ gdr_status chunk_prefill(const char* who, const void* q, const void* k, const vo
   int32_t* cidx = reinterpret_cast<int32_t*>(ws);
   ws += align_up(sizeof(int32_t) * 2 * static_cast<size_t>(mc));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // The plain scan of a batch of at most 64 sequences forms the chunk layout
-  // inside its two kernels from cu_seqlens; every other schedule runs the
-  // layout kernel first.
-  const bool own_layout = sched == kScan && !L_out && !M_out && N <= gdr::kSmallLayoutMaxN;
-  hipError_t e = hipSuccess;
-  if (!own_layout) {
-    e = gdr::launch_layout(cu_seqlens, N, chunk, offs, cidx, mc, st);
-    if (e != hipSuccess) return hip_fail(e, who, "layout");
-  }
+  hipError_t e = gdr::launch_layout(cu_seqlens, N, chunk, offs, cidx, mc, st);
+  if (e != hipSuccess) return hip_fail(e, who, "layout");
 
   if (scan) {
     const gdr::ChunkFactorSizes z = gdr::chunk_factor_sizes(mc, H, chunk);
@@ -302,15 +295,14 @@ gdr_status chunk_prefill(const char* who, const void* q, const void* k, const vo
                                     dk, dv, chunk, in_dtype, st);
         if (e != hipSuccess) return hip_fail(e, who, "chunk_local");
       }
-      e = gdr::launch_chunk_factors(q, k, g, beta, cu_seqlens, own_layout ? nullptr : cidx, f, mc,
-                                    T_total, N, H, dk, chunk, st);
+      e = gdr::launch_chunk_factors(q, k, g, beta, cu_seqlens, cidx, f, mc, T_total, H, dk, chunk,
+                                    st);
       if (e != hipSuccess) return hip_fail(e, who, "chunk factors");
     }
     ws += align_up(z.gate);
     if (sched == kScan) {
-      e = gdr::launch_chunk_scan(q, k, v, cu_seqlens, own_layout ? nullptr : offs, f, state_in,
-                                 state_out, fixed_out, o, N, H, dk, chunk, mc, T_total, out_dtype,
-                                 st);
+      e = gdr::launch_chunk_scan(q, k, v, cu_seqlens, offs, f, state_in, state_out, fixed_out, o,
+                                 N, H, dk, chunk, mc, T_total, out_dtype, st);
       return hip_fail(e, who, "chunk scan");
     }
     // segmented scan

@@ -110,30 +110,6 @@ __device__ __forceinline__ ChunkTokens chunk_tokens(const int32_t* cu, const int
   return r;
 }
 
-// chunk_tokens for a batch of at most 64 sequences without the layout kernel's
-// chunk indices: the wave forms the layout from cu_seqlens (every lane of the
-// wave must take part).
-__device__ __forceinline__ ChunkTokens chunk_tokens_small(const int32_t* cu, int N, int cid, int C,
-                                                          int T_total) {
-  ChunkTokens r{0, 0, -1, -1};
-  const int lane = threadIdx.x & 63;
-  const SmallLayout sl = small_layout(cu, N, C, lane);
-  const unsigned long long hit = __ballot(lane < N && sl.excl <= cid && cid < sl.incl);
-  if (hit == 0) return r;
-  // (the shuffles give every lane the same values: scalar registers)
-  const int n = __builtin_ctzll(hit);
-  const int j = cid - __builtin_amdgcn_readfirstlane(__shfl(sl.excl, n, 64));
-  const int a = __builtin_amdgcn_readfirstlane(__shfl(sl.cu_lo, n, 64)) + j * C;
-  int b = __builtin_amdgcn_readfirstlane(__shfl(sl.cu_hi, n, 64));
-  b = b < a + C ? b : a + C;
-  if (a < 0 || b > T_total || b <= a) return r;
-  r.tok0 = a;
-  r.c = b - a;
-  r.n = n;
-  r.j = j;
-  return r;
-}
-
 template <int D, int C, Dt IN, bool OUT, bool TF = false>
 struct ChunkWork {
   using Cfg = ChunkCfg<D, C, IN, OUT, TF>;
@@ -944,7 +920,7 @@ template <int D, int C>
 __global__ __launch_bounds__(256, 2) void chunk_factors_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, const int32_t* __restrict__ cu, const int32_t* __restrict__ cidx,
-    ChunkFactors f, int N, int H, int T_total, int max_chunks) {
+    ChunkFactors f, int H, int T_total, int max_chunks) {
   using W_ = ChunkWork<D, C, Dt::BF16, false, true>;
   using Cfg = typename W_::Cfg;
   constexpr int PT = Cfg::PT, NT = Cfg::NT, KB = Cfg::KB, TLP = Cfg::TL_PLANE, CHD = Cfg::CHD;
@@ -962,10 +938,8 @@ __global__ __launch_bounds__(256, 2) void chunk_factors_kernel(
   // head's 256-byte slice of rows H * 256 bytes apart.  Chunks are produced
   // last-first: the scan reads them first-first, so the earliest chunks are
   // the most recently written (and still cache-resident) when it starts.
-  // (cidx NULL: at most 64 sequences, the layout formed here from cu_seqlens)
   const int h = blockIdx.x % H, cid = max_chunks - 1 - static_cast<int>(blockIdx.x / H);
-  const ChunkTokens ct = cidx ? chunk_tokens(cu, cidx, cid, C, T_total)
-                              : chunk_tokens_small(cu, N, cid, C, T_total);
+  const ChunkTokens ct = chunk_tokens(cu, cidx, cid, C, T_total);
   if (ct.c <= 0) return;
 
   W_ w;
@@ -1039,12 +1013,11 @@ __global__ __launch_bounds__(256, 2) void chunk_factors_kernel(
 template <int D, int C>
 hipError_t factors_t(const void* q, const void* k, const float* g, const float* beta,
                      const int32_t* cu, const int32_t* cidx, const ChunkFactors& f,
-                     int max_chunks, int T_total, int N, int H, hipStream_t stream) {
+                     int max_chunks, int T_total, int H, hipStream_t stream) {
   const int64_t groups = static_cast<int64_t>(max_chunks) * H;
   if (groups > INT32_MAX) return hipErrorInvalidConfiguration;
-  if (!cidx && (N < 1 || N > kSmallLayoutMaxN)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((chunk_factors_kernel<D, C>), dim3(static_cast<unsigned>(groups)), dim3(256), 0,
-                     stream, q, k, g, beta, cu, cidx, f, N, H, T_total, max_chunks);
+                     stream, q, k, g, beta, cu, cidx, f, H, T_total, max_chunks);
   return hipGetLastError();
 }
 
@@ -1137,14 +1110,14 @@ hipError_t launch_chunk_out(const void* q, const void* k, const void* v, const f
 
 hipError_t launch_chunk_factors(const void* q, const void* k, const float* g, const float* beta,
                                 const int32_t* cu_seqlens, const int32_t* chunk_indices,
-                                const ChunkFactors& f, int max_chunks, int T_total, int N, int H,
-                                int d, int chunk, hipStream_t stream) {
+                                const ChunkFactors& f, int max_chunks, int T_total, int H, int d,
+                                int chunk, hipStream_t stream) {
   if (max_chunks <= 0) return hipSuccess;
   if (chunk != 64) return hipErrorInvalidValue;
   if (d == 128)
-    return factors_t<128, 64>(q, k, g, beta, cu_seqlens, chunk_indices, f, max_chunks, T_total, N,
-                              H, stream);
-  return factors_t<64, 64>(q, k, g, beta, cu_seqlens, chunk_indices, f, max_chunks, T_total, N, H,
+    return factors_t<128, 64>(q, k, g, beta, cu_seqlens, chunk_indices, f, max_chunks, T_total, H,
+                              stream);
+  return factors_t<64, 64>(q, k, g, beta, cu_seqlens, chunk_indices, f, max_chunks, T_total, H,
                            stream);
 }
 

@@ -23,34 +23,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-// Chunk layout of a batch of at most 64 sequences, formed by one whole wave
-// from cu_seqlens (what the layout kernel writes, without a launch): lane
-// n < N gets the first chunk slot of sequence n (excl), the slot past its last
-// (incl) and its token range [cu_lo, cu_hi).  Every lane of the wave must take
-// part (shuffles).
-struct SmallLayout {
-  int excl, incl, cu_lo, cu_hi;
-};
-__device__ __forceinline__ SmallLayout small_layout(const int32_t* cu, int N, int C, int lane) {
-  SmallLayout r{0, 0, 0, 0};
-  int cnt = 0;
-  if (lane < N) {
-    r.cu_lo = cu[lane];
-    r.cu_hi = cu[lane + 1];
-    const int len = r.cu_hi - r.cu_lo;
-    cnt = len > 0 ? (len + C - 1) / C : 0;
-  }
-  int incl = cnt;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
-  r.incl = incl;
-  r.excl = incl - cnt;
-  return r;
-}
-
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
 // (lgkmcnt) but not for global loads still in flight, which __syncthreads()
 // also drains (its release fence covers global memory).  The s_waitcnt

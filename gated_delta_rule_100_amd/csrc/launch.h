@@ -96,23 +96,16 @@ inline ChunkFactorSizes chunk_factor_sizes(int slots, int H, int chunk) {
   return {n * tl * 2, n * 2 * tl * 2, n * 4 * c * 4};
 }
 
-// Batches of at most this many sequences may skip the layout kernel: one
-// wave forms their chunk layout from cu_seqlens (small_layout, gdr_device.h).
-constexpr int kSmallLayoutMaxN = 64;
-
 // Factors of every chunk slot < max_chunks (bf16 inputs, chunk 64).
-// chunk_indices NULL (N <= kSmallLayoutMaxN): every workgroup forms the layout
-// from cu_seqlens itself.
 hipError_t launch_chunk_factors(const void* q, const void* k, const float* g, const float* beta,
                                 const int32_t* cu_seqlens, const int32_t* chunk_indices,
-                                const ChunkFactors& f, int max_chunks, int T_total, int N, int H,
-                                int d, int chunk, hipStream_t stream);
+                                const ChunkFactors& f, int max_chunks, int T_total, int H, int d,
+                                int chunk, hipStream_t stream);
 
 // Sequential scan over the chunks of every sequence from the factors and the
 // q, k, v inputs: outputs o (skipped when o is NULL), final states (skipped
 // when state_out is NULL), and (when fixed != NULL) the state at every chunk
-// end.  chunk_offsets NULL (N <= kSmallLayoutMaxN): every workgroup forms the
-// layout from cu_seqlens itself.
+// end.
 hipError_t launch_chunk_scan(const void* q, const void* k, const void* v,
                              const int32_t* cu_seqlens, const int32_t* chunk_offsets,
                              const ChunkFactors& f, const float* state_in, float* state_out,

@@ -220,23 +220,11 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, g4 = lane >> 4;
 
-  int c0, c1, tb, te;
-  if (offs) {
-    c0 = offs[n];
-    c1 = offs[n + 1];
-    tb = cu[n];
-    te = cu[n + 1];
-  } else {  // at most 64 sequences: the layout formed here from cu_seqlens
-    // (the shuffles give every lane the same values: scalar registers)
-    const SmallLayout sl = small_layout(cu, N, C, lane);
-    c0 = __builtin_amdgcn_readfirstlane(__shfl(sl.excl, n, 64));
-    c1 = __builtin_amdgcn_readfirstlane(__shfl(sl.incl, n, 64));
-    tb = __builtin_amdgcn_readfirstlane(__shfl(sl.cu_lo, n, 64));
-    te = __builtin_amdgcn_readfirstlane(__shfl(sl.cu_hi, n, 64));
-  }
+  int c0 = offs[n], c1 = offs[n + 1];
   c0 = c0 < 0 ? 0 : (c0 > n_slots ? n_slots : c0);
   c1 = c1 < c0 ? c0 : (c1 > n_slots ? n_slots : c1);
   if (T_total <= 0) c1 = c0;  // no token to read, whatever the offsets claim
+  int tb = cu[n], te = cu[n + 1];
   tb = tb < 0 ? 0 : (tb > T_total ? T_total : tb);
   te = te < tb ? tb : (te > T_total ? T_total : te);
 
@@ -844,7 +832,6 @@ hipError_t launch_chunk_scan(const void* q, const void* k, const void* v,
                              float* fixed, void* o, int N, int H, int d, int chunk, int n_slots,
                              int T_total, int out_dtype, hipStream_t stream) {
   if (chunk != 64) return hipErrorInvalidValue;
-  if (!chunk_offsets && (N < 1 || N > kSmallLayoutMaxN)) return hipErrorInvalidValue;
 #define GDR_SCAN(D_, OUT_)                                                                         \
   return scan_t<D_, 64, OUT_>(q, k, v, cu_seqlens, chunk_offsets, f, state_in, state_out, fixed, o, \
                               N, H, n_slots, T_total, stream)
