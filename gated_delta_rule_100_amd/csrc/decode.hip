@@ -21,6 +21,7 @@
 // o = S' q written out per row.
 #include "gdr_device.h"
 #include "launch.h"
+#include "mfma_planes.h"
 
 namespace gdr {
 namespace {
@@ -400,13 +401,40 @@ __global__ __launch_bounds__(64 * kMtpWaves, 5) void mtp_chunk_kernel(
   // [Z | Y] = S [K; Q]^T: lane (c, gq) ends with row 4 gq + e of the wave and
   // column c (token c of Z for c < 8, token c - 8 of Y for c >= 8).
   floatx4 zy0 = {0.f, 0.f, 0.f, 0.f}, zy1 = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (IN == Dt::BF16) {
+    // bf16 inputs: S as two bf16 planes against the exact bf16 rows of K and
+    // Q on the 16x16x32 matrix cores (8 products instead of 32 fp32 ones).
+    // Block kb contracts columns 32 kb + 4 gq + e and 32 kb + 16 + 4 gq + e in
+    // the slots of lane group gq, the same order in both operands, which is
+    // where the state already is (st[2 kb], st[2 kb + 1]).
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    const floatx4 kc = *reinterpret_cast<const floatx4*>(sKQ + c * LDK + 16 * kt + 4 * gq);
+    for (int kb = 0; kb < KT / 2; ++kb) {
+      const floatx4 k0 = *reinterpret_cast<const floatx4*>(sKQ + c * LDK + 32 * kb + 4 * gq);
+      const floatx4 k1 = *reinterpret_cast<const floatx4*>(sKQ + c * LDK + 32 * kb + 16 + 4 * gq);
+      float xs[8], xk[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (kt & 1) zy1 = mfma4(st[kt][e], kc[e], zy1);
-      else zy0 = mfma4(st[kt][e], kc[e], zy0);
+      for (int e = 0; e < 4; ++e) {
+        xs[e] = st[2 * kb][e];
+        xs[4 + e] = st[2 * kb + 1][e];
+        xk[e] = k0[e];
+        xk[4 + e] = k1[e];
+      }
+      bf16x8 sp[2], kp[1];
+      split8<2>(xs, sp);
+      split8<1>(xk, kp);  // exact: the rows are bf16 inputs
+      floatx4& acc = (kb & 1) ? zy1 : zy0;
+      acc = mfma16x16x32(sp[1], kp[0], acc);  // the low plane first
+      acc = mfma16x16x32(sp[0], kp[0], acc);
+    }
+  } else {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const floatx4 kc = *reinterpret_cast<const floatx4*>(sKQ + c * LDK + 16 * kt + 4 * gq);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (kt & 1) zy1 = mfma4(st[kt][e], kc[e], zy1);
+        else zy0 = mfma4(st[kt][e], kc[e], zy0);
+      }
     }
   }
   const floatx4 zy = zy0 + zy1;
@@ -458,15 +486,42 @@ __global__ __launch_bounds__(64 * kMtpWaves, 5) void mtp_chunk_kernel(
   // B[t][row c] = D_t U[c][t]; the output lands on lane (c, gq), element e =
   // S[row c][16 kt + 4 gq + e], where the state already is.
   const float gam_end = sF[F_GAM + kMtpMaxT - 1];
-  float ub[2];
+  if constexpr (IN == Dt::BF16) {
+    // 16x16x16 products over the tokens (8, padded to 16 with zeros in lane
+    // groups 2 and 3): A[j][t] = K[t][16 kt + j] (exact bf16), B[t][row c] =
+    // D_t U[c][t] as two bf16 planes (lane group gq: tokens 4 gq .. 4 gq + 3)
+    shortx4 ubp[2] = {shortx4{0, 0, 0, 0}, shortx4{0, 0, 0, 0}};
+    if (gq < 2) {
+      floatx4 du;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) ub[ks] = sF[F_D + 4 * ks + gq] * ua[ks];
+      for (int e = 0; e < 4; ++e) du[e] = sF[F_D + 4 * gq + e] * X[c * XLD + 4 * gq + e];
+      split4<2>(du, ubp);
+    }
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    floatx4 acc = st[kt] * gam_end;
+    for (int kt = 0; kt < KT; ++kt) {
+      shortx4 ka[1] = {shortx4{0, 0, 0, 0}};
+      if (gq < 2) {
+        floatx4 kk;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) acc = mfma4(sKQ[(4 * ks + gq) * LDK + 16 * kt + c], ub[ks], acc);
-    st[kt] = acc;
+        for (int e = 0; e < 4; ++e) kk[e] = sKQ[(4 * gq + e) * LDK + 16 * kt + c];
+        split4<1>(kk, ka);  // exact
+      }
+      floatx4 acc = st[kt] * gam_end;
+      acc = mfma16x16x16(ka[0], ubp[1], acc);
+      acc = mfma16x16x16(ka[0], ubp[0], acc);
+      st[kt] = acc;
+    }
+  } else {
+    float ub[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) ub[ks] = sF[F_D + 4 * ks + gq] * ua[ks];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      floatx4 acc = st[kt] * gam_end;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) acc = mfma4(sKQ[(4 * ks + gq) * LDK + 16 * kt + c], ub[ks], acc);
+      st[kt] = acc;
+    }
   }
   if (state_out) {
     // back through the staging rows, leaving as it arrived: each store
