@@ -224,16 +224,21 @@ __global__ __launch_bounds__(kDecodeThreads) void mtp_kernel(
   }
 }
 
-// Multi-token decode on the matrix cores (5 <= T <= 8 tokens, no per-token
-// states; the kernel itself takes any 1 <= T <= 8).  The T tokens of a (sequence, head) are one chunk of the chunked
-// form of the recurrence (derived from it: G_t = g_1 + ... + g_t,
-// gamma_t = e^{G_t}, D_t = e^{G_T - G_t}, A_ts = beta_t e^{G_t - G_s} k_t.k_s for
-// s < t, Tinv = (I + A)^{-1}, P_ts = e^{G_t - G_s} q_t.k_s for s <= t):
+// Multi-token decode on the matrix cores (T >= 5 tokens, no per-token states;
+// the kernel itself takes any T >= 1).  The tokens of a (sequence, head) go in
+// chunks of 8 (the last may be shorter), each one chunk of the chunked form of
+// the recurrence applied to the state, which stays in registers from the
+// first chunk to the last.  For a chunk of T tokens (derived from the
+// recurrence: G_t = g_1 + ... + g_t, gamma_t = e^{G_t}, D_t = e^{G_T - G_t},
+// A_ts = beta_t e^{G_t - G_s} k_t.k_s for s < t, Tinv = (I + A)^{-1},
+// P_ts = e^{G_t - G_s} q_t.k_s for s <= t):
 //   Z = S K^T, Y = S Q^T                         (one product: [K; Q] stacked)
 //   U = (diag(beta) (V - diag(gamma) Z)) Tinv^T  per state row
 //   O = diag(gamma) Y + U P^T                    (o_t = S_t q_t for every t)
 //   S <- gamma_T S + U diag(D) K
-// all in fp32 on v_mfma_f32_16x16x4_f32.  A workgroup holds 64 state rows, a
+// in fp32 on v_mfma_f32_16x16x4_f32 (with bf16 inputs, [Z | Y] and the state
+// update on the bf16 matrix cores, their fp32 operand as two bf16 planes).
+// A workgroup holds 64 state rows, a
 // wave 16: lane (c, g) holds S[row c][16 kt + 4 g + e], which is at once the A
 // operand of S K^T (the contraction index permuted the same way in both
 // operands) and the accumulator layout of S^T <- gamma_T S^T + K^T diag(D) U^T,
@@ -257,10 +262,13 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int DK, int DV, Dt IN, Dt OUT>
+// MULTI: T > 8 (more than one chunk; the next chunk's inputs are loaded while
+// the current one is applied, which needs registers for four waves per SIMD
+// instead of five).
+template <int DK, int DV, Dt IN, Dt OUT, bool MULTI>
 // (at least 5 waves per SIMD: 84 VGPRs and no accumulation registers, against
 // 4 waves and a 32-register accumulator copy by default; 62 against 66 us)
-__global__ __launch_bounds__(64 * kMtpWaves, 5) void mtp_chunk_kernel(
+__global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 3 : 5) void mtp_chunk_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* state_in,
     float* state_out, void* __restrict__ o, int NH, int H, int T) {
@@ -287,27 +295,31 @@ __global__ __launch_bounds__(64 * kMtpWaves, 5) void mtp_chunk_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c = lane & 15, gq = lane >> 4;
   const int rbase = r0 + 16 * wave;  // first state row of this wave
-  const size_t tok0 = static_cast<size_t>(n) * T;
+  const size_t seq0 = static_cast<size_t>(n) * T;  // the sequence's first token
 
-  // Token inputs first (a wait for them then does not wait for the state).
-  float tk[TPT];
+  // The inputs of the Tc tokens from token tok0 on (a chunk of at most 8):
+  // k and q rows, gates, and v of this lane's four rows at token c (lanes
+  // c < Tc of the first 8).
+  float tk[TPT], gv, bv, vv[4];
+  auto load_tokens = [&](size_t tok0, int Tc) {
 #pragma unroll
-  for (int i = 0; i < TPT; ++i) {
-    const int idx = tid + kMtpThreads * i, rr = idx / DK, col = idx % DK, t = rr & 7;
-    tk[i] = t < T ? load_scalar<IN>(rr < 8 ? k : q, ((tok0 + t) * H + h) * DK + col) : 0.f;
-  }
-  float gv = 0.f, bv = 0.f;
-  if (tid < kMtpMaxT && tid < T) {
-    gv = g[(tok0 + tid) * H + h];
-    bv = beta[(tok0 + tid) * H + h];
-  }
-  // v of this lane's four rows at token c (lanes c < T of the first 8)
-  float vv[4] = {0.f, 0.f, 0.f, 0.f};
-  if (c < T) {
+    for (int i = 0; i < TPT; ++i) {
+      const int idx = tid + kMtpThreads * i, rr = idx / DK, col = idx % DK, t = rr & 7;
+      tk[i] = t < Tc ? load_scalar<IN>(rr < 8 ? k : q, ((tok0 + t) * H + h) * DK + col) : 0.f;
+    }
+    gv = 0.f;
+    bv = 0.f;
+    if (tid < kMtpMaxT && tid < Tc) {
+      gv = g[(tok0 + tid) * H + h];
+      bv = beta[(tok0 + tid) * H + h];
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      vv[e] = load_scalar<IN>(v, ((tok0 + c) * H + h) * DV + rbase + 4 * gq + e);
-  }
+      vv[e] = c < Tc ? load_scalar<IN>(v, ((tok0 + c) * H + h) * DV + rbase + 4 * gq + e) : 0.f;
+  };
+  // The first chunk's inputs first (a wait for them then does not wait for
+  // the state).
+  load_tokens(seq0, T < kMtpMaxT ? T : kMtpMaxT);
   // The state arrives in 256-byte row pieces (an instruction covers 4 rows x
   // 256 B: register j holds row 4 (j % 4) + lane / 16, columns
   // 64 (j / 4) + 4 (lane % 16)); the wave's own LDS rows turn it into the
@@ -320,74 +332,80 @@ __global__ __launch_bounds__(64 * kMtpWaves, 5) void mtp_chunk_kernel(
     ld[j] = __builtin_nontemporal_load(
         &Sin[((rbase + 4 * (j & 3) + (lane >> 4)) * DK + 64 * (j >> 2) + 4 * (lane & 15)) / 4]);
 
-#pragma unroll
-  for (int i = 0; i < TPT; ++i) {
-    const int idx = tid + kMtpThreads * i;
-    sKQ[(idx / DK) * LDK + idx % DK] = tk[i];
-  }
-  if (tid < kMtpMaxT) {
-    sF[F_GRAW + tid] = gv;
-    sF[F_B + tid] = bv;
-  }
-  lds_barrier();  // the state loads stay in flight
-
-  // Gate prefix (fixed order; padding adds g = 0, so G_7 = G_T) and the dot
-  // products k_t.k_s (threads 0-63) and q_t.k_s (64-127), t, s < 8.
-  if (tid < kMtpMaxT) {
-    float G = 0.f, Gt = 0.f;
-    for (int s = 0; s < kMtpMaxT; ++s) {
-      G += sF[F_GRAW + s];
-      if (s == tid) Gt = G;
-    }
-    sF[F_G + tid] = Gt;
-    sF[F_GAM + tid] = expf(Gt);
-    sF[F_D + tid] = tid < T ? expf(G - Gt) : 0.f;
-  }
-  if (tid < 128) {
-    const int t = (tid >> 3) & 7, s = tid & 7;
-    const float* a = sKQ + ((tid >> 6) ? 8 + t : t) * LDK;
-    const float* b = sKQ + s * LDK;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependent chains
-#pragma unroll 8
-    for (int j = 0; j < DK; j += 4) {
-      const floatx4 x = *reinterpret_cast<const floatx4*>(a + j);
-      const floatx4 y = *reinterpret_cast<const floatx4*>(b + j);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(x[e], y[e], acc[e]);
-    }
-    sF[F_DOT + tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  }
-  lds_barrier();
-  // A (threads 0-63) and P (64-127), one element each
-  if (tid < 128) {
-    const int t = (tid >> 3) & 7, s = tid & 7;
-    const float decay = expf(sF[F_G + t] - sF[F_G + s]);
-    if (tid < 64)
-      sF[F_A + 8 * t + s] = s < t ? sF[F_B + t] * decay * sF[F_DOT + tid] : 0.f;
-    else
-      sF[F_P + 8 * t + s] = s <= t ? decay * sF[F_DOT + tid] : 0.f;
-  }
-  lds_barrier();
-  // Tinv = (I + A)^{-1} by forward substitution (thread j: column j)
-  if (tid < kMtpMaxT) {
-    const int j = tid;
-    float x[kMtpMaxT];
-#pragma unroll
-    for (int t = 0; t < kMtpMaxT; ++t) {
-      float acc = t == j ? 1.f : 0.f;
-#pragma unroll
-      for (int s = 0; s < t; ++s) acc = fmaf(-sF[F_A + 8 * t + s], x[s], acc);
-      x[t] = acc;
-    }
-#pragma unroll
-    for (int t = 0; t < kMtpMaxT; ++t) sF[F_TINV + 8 * t + j] = x[t];
-  }
-  lds_barrier();
-
-  // 64 columns at a time through the wave's staging rows (its own; LDS
-  // accesses of a wave complete in order)
   float* W = sT[wave];
   floatx4 st[KT];
+  // The chunk of Tc tokens from token tok0 on: its k and q rows and gates into
+  // LDS (from the registers load_tokens filled), its gate prefix, dots, A, P
+  // and Tinv.
+  auto setup_chunk = [&](int Tc) {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int idx = tid + kMtpThreads * i;
+      sKQ[(idx / DK) * LDK + idx % DK] = tk[i];
+    }
+    if (tid < kMtpMaxT) {
+      sF[F_GRAW + tid] = gv;
+      sF[F_B + tid] = bv;
+    }
+    lds_barrier();  // the state loads stay in flight
+
+    // Gate prefix (fixed order; padding adds g = 0, so G_7 = G_T) and the dot
+    // products k_t.k_s (threads 0-63) and q_t.k_s (64-127), t, s < 8.
+    if (tid < kMtpMaxT) {
+      float G = 0.f, Gt = 0.f;
+      for (int s = 0; s < kMtpMaxT; ++s) {
+        G += sF[F_GRAW + s];
+        if (s == tid) Gt = G;
+      }
+      sF[F_G + tid] = Gt;
+      sF[F_GAM + tid] = expf(Gt);
+      sF[F_D + tid] = tid < Tc ? expf(G - Gt) : 0.f;
+    }
+    if (tid < 128) {
+      const int t = (tid >> 3) & 7, s = tid & 7;
+      const float* a = sKQ + ((tid >> 6) ? 8 + t : t) * LDK;
+      const float* b = sKQ + s * LDK;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependent chains
+#pragma unroll 8
+      for (int j = 0; j < DK; j += 4) {
+        const floatx4 x = *reinterpret_cast<const floatx4*>(a + j);
+        const floatx4 y = *reinterpret_cast<const floatx4*>(b + j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(x[e], y[e], acc[e]);
+      }
+      sF[F_DOT + tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    }
+    lds_barrier();
+    // A (threads 0-63) and P (64-127), one element each
+    if (tid < 128) {
+      const int t = (tid >> 3) & 7, s = tid & 7;
+      const float decay = expf(sF[F_G + t] - sF[F_G + s]);
+      if (tid < 64)
+        sF[F_A + 8 * t + s] = s < t ? sF[F_B + t] * decay * sF[F_DOT + tid] : 0.f;
+      else
+        sF[F_P + 8 * t + s] = s <= t ? decay * sF[F_DOT + tid] : 0.f;
+    }
+    lds_barrier();
+    // Tinv = (I + A)^{-1} by forward substitution (thread j: column j)
+    if (tid < kMtpMaxT) {
+      const int j = tid;
+      float x[kMtpMaxT];
+#pragma unroll
+      for (int t = 0; t < kMtpMaxT; ++t) {
+        float acc = t == j ? 1.f : 0.f;
+#pragma unroll
+        for (int s = 0; s < t; ++s) acc = fmaf(-sF[F_A + 8 * t + s], x[s], acc);
+        x[t] = acc;
+      }
+#pragma unroll
+      for (int t = 0; t < kMtpMaxT; ++t) sF[F_TINV + 8 * t + j] = x[t];
+    }
+    lds_barrier();
+  };
+  int t0 = 0;
+  setup_chunk(T < kMtpMaxT ? T : kMtpMaxT);
+  // 64 columns at a time through the wave's staging rows (its own; LDS
+  // accesses of a wave complete in order)
 #pragma unroll
   for (int v = 0; v < KT / 4; ++v) {
 #pragma unroll
@@ -397,131 +415,146 @@ __global__ __launch_bounds__(64 * kMtpWaves, 5) void mtp_chunk_kernel(
     for (int t = 0; t < 4; ++t)
       st[4 * v + t] = *reinterpret_cast<const floatx4*>(W + c * TLD + 16 * t + 4 * gq);
   }
+  // The tokens in chunks of 8 (the last may be shorter); the state stays in
+  // registers from the first chunk to the last.
+  for (;;) {
+    const int Tc = T - t0 < kMtpMaxT ? T - t0 : kMtpMaxT;
+    const size_t tok0 = seq0 + t0;
 
-  // [Z | Y] = S [K; Q]^T: lane (c, gq) ends with row 4 gq + e of the wave and
-  // column c (token c of Z for c < 8, token c - 8 of Y for c >= 8).
-  floatx4 zy0 = {0.f, 0.f, 0.f, 0.f}, zy1 = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (IN == Dt::BF16) {
-    // bf16 inputs: S as two bf16 planes against the exact bf16 rows of K and
-    // Q on the 16x16x32 matrix cores (8 products instead of 32 fp32 ones).
-    // Block kb contracts columns 32 kb + 4 gq + e and 32 kb + 16 + 4 gq + e in
-    // the slots of lane group gq, the same order in both operands, which is
-    // where the state already is (st[2 kb], st[2 kb + 1]).
+    // [Z | Y] = S [K; Q]^T: lane (c, gq) ends with row 4 gq + e of the wave and
+    // column c (token c of Z for c < 8, token c - 8 of Y for c >= 8).
+    floatx4 zy0 = {0.f, 0.f, 0.f, 0.f}, zy1 = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (IN == Dt::BF16) {
+      // bf16 inputs: S as two bf16 planes against the exact bf16 rows of K and
+      // Q on the 16x16x32 matrix cores (8 products instead of 32 fp32 ones).
+      // Block kb contracts columns 32 kb + 4 gq + e and 32 kb + 16 + 4 gq + e in
+      // the slots of lane group gq, the same order in both operands, which is
+      // where the state already is (st[2 kb], st[2 kb + 1]).
 #pragma unroll
-    for (int kb = 0; kb < KT / 2; ++kb) {
-      const floatx4 k0 = *reinterpret_cast<const floatx4*>(sKQ + c * LDK + 32 * kb + 4 * gq);
-      const floatx4 k1 = *reinterpret_cast<const floatx4*>(sKQ + c * LDK + 32 * kb + 16 + 4 * gq);
-      float xs[8], xk[8];
+      for (int kb = 0; kb < KT / 2; ++kb) {
+        const floatx4 k0 = *reinterpret_cast<const floatx4*>(sKQ + c * LDK + 32 * kb + 4 * gq);
+        const floatx4 k1 = *reinterpret_cast<const floatx4*>(sKQ + c * LDK + 32 * kb + 16 + 4 * gq);
+        float xs[8], xk[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xs[e] = st[2 * kb][e];
-        xs[4 + e] = st[2 * kb + 1][e];
-        xk[e] = k0[e];
-        xk[4 + e] = k1[e];
+        for (int e = 0; e < 4; ++e) {
+          xs[e] = st[2 * kb][e];
+          xs[4 + e] = st[2 * kb + 1][e];
+          xk[e] = k0[e];
+          xk[4 + e] = k1[e];
+        }
+        bf16x8 sp[2], kp[1];
+        split8<2>(xs, sp);
+        split8<1>(xk, kp);  // exact: the rows are bf16 inputs
+        floatx4& acc = (kb & 1) ? zy1 : zy0;
+        acc = mfma16x16x32(sp[1], kp[0], acc);  // the low plane first
+        acc = mfma16x16x32(sp[0], kp[0], acc);
       }
-      bf16x8 sp[2], kp[1];
-      split8<2>(xs, sp);
-      split8<1>(xk, kp);  // exact: the rows are bf16 inputs
-      floatx4& acc = (kb & 1) ? zy1 : zy0;
-      acc = mfma16x16x32(sp[1], kp[0], acc);  // the low plane first
-      acc = mfma16x16x32(sp[0], kp[0], acc);
-    }
-  } else {
+    } else {
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      const floatx4 kc = *reinterpret_cast<const floatx4*>(sKQ + c * LDK + 16 * kt + 4 * gq);
+      for (int kt = 0; kt < KT; ++kt) {
+        const floatx4 kc = *reinterpret_cast<const floatx4*>(sKQ + c * LDK + 16 * kt + 4 * gq);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (kt & 1) zy1 = mfma4(st[kt][e], kc[e], zy1);
-        else zy0 = mfma4(st[kt][e], kc[e], zy0);
+        for (int e = 0; e < 4; ++e) {
+          if (kt & 1) zy1 = mfma4(st[kt][e], kc[e], zy1);
+          else zy0 = mfma4(st[kt][e], kc[e], zy0);
+        }
       }
     }
-  }
-  const floatx4 zy = zy0 + zy1;
+    const floatx4 zy = zy0 + zy1;
 
-  // R = beta (v - gamma Z) on lanes c < 8, exchanged through LDS as [row][t]
-  float* X = sX[wave];
-  if (c < kMtpMaxT) {
-    const float bt = sF[F_B + c], gt = sF[F_GAM + c];
+    // R = beta (v - gamma Z) on lanes c < 8, exchanged through LDS as [row][t]
+    float* X = sX[wave];
+    if (c < kMtpMaxT) {
+      const float bt = sF[F_B + c], gt = sF[F_GAM + c];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) X[(4 * gq + e) * XLD + c] = bt * (vv[e] - gt * zy[e]);
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  // U = R Tinv^T: A[row c][t] = R, B[t][t' = c] = Tinv[c][t]
-  floatx4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int t = 4 * ks + gq;
-    const float a = X[c * XLD + t];
-    const float b = c < kMtpMaxT ? sF[F_TINV + 8 * c + t] : 0.f;
-    u = mfma4(a, b, u);
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  if (c < kMtpMaxT) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) X[(4 * gq + e) * XLD + c] = u[e];
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  // U in the A layout (row c, token 4 ks + gq), for O and (scaled by D) the update
-  float ua[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) ua[ks] = X[c * XLD + 4 * ks + gq];
-
-  // O = gamma Y + U P^T on lanes c >= 8 (token c - 8, rows 4 gq + e)
-  floatx4 pu = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const float b = c >= kMtpMaxT ? sF[F_P + 8 * (c - kMtpMaxT) + 4 * ks + gq] : 0.f;
-    pu = mfma4(ua[ks], b, pu);
-  }
-  if (c >= kMtpMaxT && c - kMtpMaxT < T) {
-    const int t = c - kMtpMaxT;
-    const float gt = sF[F_GAM + t];
-    const size_t ob = ((tok0 + t) * H + h) * DV + rbase + 4 * gq;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) store_scalar<OUT>(o, ob + e, fmaf(gt, zy[e], pu[e]));
-  }
-
-  // S^T <- gamma_T S^T + K^T diag(D) U^T, tile by tile: A[j][t] = K[t][16 kt + j],
-  // B[t][row c] = D_t U[c][t]; the output lands on lane (c, gq), element e =
-  // S[row c][16 kt + 4 gq + e], where the state already is.
-  const float gam_end = sF[F_GAM + kMtpMaxT - 1];
-  if constexpr (IN == Dt::BF16) {
-    // 16x16x16 products over the tokens (8, padded to 16 with zeros in lane
-    // groups 2 and 3): A[j][t] = K[t][16 kt + j] (exact bf16), B[t][row c] =
-    // D_t U[c][t] as two bf16 planes (lane group gq: tokens 4 gq .. 4 gq + 3)
-    shortx4 ubp[2] = {shortx4{0, 0, 0, 0}, shortx4{0, 0, 0, 0}};
-    if (gq < 2) {
-      floatx4 du;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) du[e] = sF[F_D + 4 * gq + e] * X[c * XLD + 4 * gq + e];
-      split4<2>(du, ubp);
+      for (int e = 0; e < 4; ++e) X[(4 * gq + e) * XLD + c] = bt * (vv[e] - gt * zy[e]);
     }
+    // the next chunk's inputs, in flight through the rest of this one
+    if constexpr (MULTI) {
+      if (t0 + kMtpMaxT < T)
+        load_tokens(tok0 + kMtpMaxT, T - t0 - kMtpMaxT < kMtpMaxT ? T - t0 - kMtpMaxT : kMtpMaxT);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    // U = R Tinv^T: A[row c][t] = R, B[t][t' = c] = Tinv[c][t]
+    floatx4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      shortx4 ka[1] = {shortx4{0, 0, 0, 0}};
+    for (int ks = 0; ks < 2; ++ks) {
+      const int t = 4 * ks + gq;
+      const float a = X[c * XLD + t];
+      const float b = c < kMtpMaxT ? sF[F_TINV + 8 * c + t] : 0.f;
+      u = mfma4(a, b, u);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    if (c < kMtpMaxT) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) X[(4 * gq + e) * XLD + c] = u[e];
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    // U in the A layout (row c, token 4 ks + gq), for O and (scaled by D) the update
+    float ua[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) ua[ks] = X[c * XLD + 4 * ks + gq];
+
+    // O = gamma Y + U P^T on lanes c >= 8 (token c - 8, rows 4 gq + e)
+    floatx4 pu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const float b = c >= kMtpMaxT ? sF[F_P + 8 * (c - kMtpMaxT) + 4 * ks + gq] : 0.f;
+      pu = mfma4(ua[ks], b, pu);
+    }
+    if (c >= kMtpMaxT && c - kMtpMaxT < Tc) {
+      const int t = c - kMtpMaxT;
+      const float gt = sF[F_GAM + t];
+      const size_t ob = ((tok0 + t) * H + h) * DV + rbase + 4 * gq;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_scalar<OUT>(o, ob + e, fmaf(gt, zy[e], pu[e]));
+    }
+
+    // S^T <- gamma_T S^T + K^T diag(D) U^T, tile by tile: A[j][t] = K[t][16 kt + j],
+    // B[t][row c] = D_t U[c][t]; the output lands on lane (c, gq), element e =
+    // S[row c][16 kt + 4 gq + e], where the state already is.
+    const float gam_end = sF[F_GAM + kMtpMaxT - 1];
+    if constexpr (IN == Dt::BF16) {
+      // 16x16x16 products over the tokens (8, padded to 16 with zeros in lane
+      // groups 2 and 3): A[j][t] = K[t][16 kt + j] (exact bf16), B[t][row c] =
+      // D_t U[c][t] as two bf16 planes (lane group gq: tokens 4 gq .. 4 gq + 3)
+      shortx4 ubp[2] = {shortx4{0, 0, 0, 0}, shortx4{0, 0, 0, 0}};
       if (gq < 2) {
-        floatx4 kk;
+        floatx4 du;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) kk[e] = sKQ[(4 * gq + e) * LDK + 16 * kt + c];
-        split4<1>(kk, ka);  // exact
+        for (int e = 0; e < 4; ++e) du[e] = sF[F_D + 4 * gq + e] * X[c * XLD + 4 * gq + e];
+        split4<2>(du, ubp);
       }
-      floatx4 acc = st[kt] * gam_end;
-      acc = mfma16x16x16(ka[0], ubp[1], acc);
-      acc = mfma16x16x16(ka[0], ubp[0], acc);
-      st[kt] = acc;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        shortx4 ka[1] = {shortx4{0, 0, 0, 0}};
+        if (gq < 2) {
+          floatx4 kk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kk[e] = sKQ[(4 * gq + e) * LDK + 16 * kt + c];
+          split4<1>(kk, ka);  // exact
+        }
+        floatx4 acc = st[kt] * gam_end;
+        acc = mfma16x16x16(ka[0], ubp[1], acc);
+        acc = mfma16x16x16(ka[0], ubp[0], acc);
+        st[kt] = acc;
+      }
+    } else {
+      float ub[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) ub[ks] = sF[F_D + 4 * ks + gq] * ua[ks];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        floatx4 acc = st[kt] * gam_end;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) acc = mfma4(sKQ[(4 * ks + gq) * LDK + 16 * kt + c], ub[ks], acc);
+        st[kt] = acc;
+      }
     }
-  } else {
-    float ub[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) ub[ks] = sF[F_D + 4 * ks + gq] * ua[ks];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      floatx4 acc = st[kt] * gam_end;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) acc = mfma4(sKQ[(4 * ks + gq) * LDK + 16 * kt + c], ub[ks], acc);
-      st[kt] = acc;
-    }
+    t0 += kMtpMaxT;
+    if (!MULTI || t0 >= T) break;
+    lds_barrier();  // every wave is done with this chunk's K, Q and factors
+    setup_chunk(T - t0 < kMtpMaxT ? T - t0 : kMtpMaxT);
   }
   if (state_out) {
     // back through the staging rows, leaving as it arrived: each store
@@ -550,9 +583,14 @@ hipError_t launch_mtp_chunk_t(const void* q, const void* k, const void* v, const
                               int NH, int H, int T, hipStream_t stream) {
   const int64_t groups = static_cast<int64_t>(NH) * (DV / (16 * mtp_waves<DV>()));
   if (groups > INT32_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((mtp_chunk_kernel<DK, DV, IN, OUT>), dim3(static_cast<unsigned>(groups)),
-                     dim3(64 * mtp_waves<DV>()), 0, stream, q, k, v, g, beta, state_in, state_out, o,
-                     NH, H, T);
+  if (T > kMtpMaxT)
+    hipLaunchKernelGGL((mtp_chunk_kernel<DK, DV, IN, OUT, true>), dim3(static_cast<unsigned>(groups)),
+                       dim3(64 * mtp_waves<DV>()), 0, stream, q, k, v, g, beta, state_in, state_out,
+                       o, NH, H, T);
+  else
+    hipLaunchKernelGGL((mtp_chunk_kernel<DK, DV, IN, OUT, false>),
+                       dim3(static_cast<unsigned>(groups)), dim3(64 * mtp_waves<DV>()), 0, stream, q,
+                       k, v, g, beta, state_in, state_out, o, NH, H, T);
   return hipGetLastError();
 }
 
@@ -610,10 +648,10 @@ hipError_t launch_mtp(const void* q, const void* k, const void* v, const float* 
                       int out_dtype, hipStream_t stream) {
   (void)dv;
   const int NH = N * H;
-  // 5..8 tokens without per-token states: the chunked form on the matrix
+  // 5 or more tokens without per-token states: the chunked form on the matrix
   // cores; otherwise (and for T = 1, which then equals the decode step bit for
   // bit) the token-by-token kernel.
-  const bool chunked = inter == nullptr && T >= kMtpChunkMinT && T <= kMtpMaxT;
+  const bool chunked = inter == nullptr && T >= kMtpChunkMinT;
 #define GDR_MTP(D_, IN_, OUT_)                                                                \
   return chunked ? launch_mtp_chunk_t<D_, D_, IN_, OUT_>(q, k, v, g, beta, state_in, state_out, \
                                                          o, NH, H, T, stream)                    \

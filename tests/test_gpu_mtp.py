@@ -85,9 +85,11 @@ def test_mtp_T1_equals_decode_step_bitwise():
         assert torch.equal(s1, s2)
 
 
-# Without per-token states, 5 <= T <= 8 tokens take the chunked kernel (the T
-# tokens as one chunk of the chunked form, on fp32 matrix products); the last
-# two cases take the token-by-token kernel without per-token states.
+# Without per-token states, T >= 5 tokens take the chunked kernel (every 8
+# tokens one chunk of the chunked form on the matrix cores, the state kept in
+# registers across the chunks; T > 8 ends on a shorter chunk unless T is a
+# multiple of 8); the T = 3 case takes the token-by-token kernel without
+# per-token states.
 CHUNKED_CASES = {
     "N3-T6-H2-d128-bf16": (3, 6, 2, 128, "bf16", "std"),
     "N2-T8-H3-d64-f32": (2, 8, 3, 64, "f32", "std"),
@@ -95,9 +97,14 @@ CHUNKED_CASES = {
     "N3-T7-H2-d128-bf16-slow": (3, 7, 2, 128, "bf16", "slow"),
     "N2-T5-H2-d64-bf16-steep": (2, 5, 2, 64, "bf16", "steep"),
     "N2-T8-H2-d128-f32-unit": (2, 8, 2, 128, "f32", "unit"),
-    # outside 5..8 the token-by-token kernel runs without per-token states
+    "N2-T12-H2-d64-bf16-slow": (2, 12, 2, 64, "bf16", "slow"),
+    "N3-T16-H2-d128-bf16": (3, 16, 2, 128, "bf16", "std"),
+    "N2-T17-H2-d128-f32": (2, 17, 2, 128, "f32", "std"),
+    "N2-T33-H1-d64-f32-steep": (2, 33, 1, 64, "f32", "steep"),
+    "N2-T64-H2-d128-bf16-unit": (2, 64, 2, 128, "bf16", "unit"),
+    "N1-T64-H3-d128-f32-slow": (1, 64, 3, 128, "f32", "slow"),
+    # below 5 tokens the token-by-token kernel runs without per-token states
     "N3-T3-H2-d128-bf16-token": (3, 3, 2, 128, "bf16", "std"),
-    "N2-T12-H2-d64-bf16-token": (2, 12, 2, 64, "bf16", "slow"),
 }
 
 
@@ -128,7 +135,7 @@ def test_mtp_in_place_and_uncommitted():
     assert so is None and torch.equal(x["state0"], before)
     assert torch.equal(o, ref_o) and torch.equal(I, ref_i)
     assert torch.equal(I[:, -1], ref_s)
-    # without intermediates (5 <= T <= 8: the chunked kernel): a new final state
+    # without intermediates (T >= 5: the chunked kernel): a new final state
     # and in place give the same bits, and both agree with the token-by-token
     # kernel to rounding
     o2, so2, _ = run_mtp(x, inter=False)
@@ -185,11 +192,13 @@ def test_mtp_full_size_sampled():
         assert max(e) <= 1e-3
 
 
-def test_mtp_chunked_full_size_sampled():
-    # the decode workload's shape with 8 draft tokens, without per-token states
-    N, T, H, d = 64, 8, 32, 128
-    say("mtp chunked full size N=64 T=8 H=32 d=128 bf16")
-    data, _, x = mtp_inputs(N, T, H, d, "bf16", seed=315)
+@pytest.mark.parametrize("T", [8, 32])
+def test_mtp_chunked_full_size_sampled(T):
+    # the decode workload's shape with 8 (one chunk) or 32 (four chunks) draft
+    # tokens, without per-token states
+    N, H, d = 64, 32, 128
+    say(f"mtp chunked full size N=64 T={T} H=32 d=128 bf16")
+    data, _, x = mtp_inputs(N, T, H, d, "bf16", seed=315 + T)
     o, so, _ = run_mtp(x, torch.bfloat16, inter=False)
     o32, so32, _ = run_mtp(x, inter=False)
     assert torch.equal(o, o32.to(torch.bfloat16)) and torch.equal(so, so32)
