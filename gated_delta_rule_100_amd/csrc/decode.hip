@@ -262,13 +262,13 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// MULTI: T > 8 (more than one chunk; the next chunk's inputs are loaded while
-// the current one is applied, which needs registers for four waves per SIMD
-// instead of five).
+// MULTI: T > 8 (more than one chunk; the chunk loop holds the state in
+// registers through the factor phase of every later chunk, which needs
+// registers for four waves per SIMD instead of five).
 template <int DK, int DV, Dt IN, Dt OUT, bool MULTI>
 // (at least 5 waves per SIMD: 84 VGPRs and no accumulation registers, against
 // 4 waves and a 32-register accumulator copy by default; 62 against 66 us)
-__global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 3 : 5) void mtp_chunk_kernel(
+__global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 4 : 5) void mtp_chunk_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* state_in,
     float* state_out, void* __restrict__ o, int NH, int H, int T) {
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 3 : 5) void mtp_chunk_kerne
   // The chunk of Tc tokens from token tok0 on: its k and q rows and gates into
   // LDS (from the registers load_tokens filled), its gate prefix, dots, A, P
   // and Tinv.
-  auto setup_chunk = [&](int Tc) {
+  auto setup_chunk = [&](int Tc, auto lean) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int idx = tid + kMtpThreads * i;
@@ -366,12 +366,19 @@ __global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 3 : 5) void mtp_chunk_kerne
       const float* a = sKQ + ((tid >> 6) ? 8 + t : t) * LDK;
       const float* b = sKQ + s * LDK;
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependent chains
-#pragma unroll 8
-      for (int j = 0; j < DK; j += 4) {
+      auto step4 = [&](int j) {
         const floatx4 x = *reinterpret_cast<const floatx4*>(a + j);
         const floatx4 y = *reinterpret_cast<const floatx4*>(b + j);
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] = fmaf(x[e], y[e], acc[e]);
+      };
+      if constexpr (decltype(lean)::value) {
+        // later chunks: the state's registers are live, so fewer reads in flight
+#pragma unroll 2
+        for (int j = 0; j < DK; j += 4) step4(j);
+      } else {
+#pragma unroll 8
+        for (int j = 0; j < DK; j += 4) step4(j);
       }
       sF[F_DOT + tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     }
@@ -392,6 +399,8 @@ __global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 3 : 5) void mtp_chunk_kerne
       float x[kMtpMaxT];
 #pragma unroll
       for (int t = 0; t < kMtpMaxT; ++t) {
+        // later chunks: row t's reads are not hoisted above the rows before it
+        if constexpr (decltype(lean)::value) __builtin_amdgcn_sched_barrier(0);
         float acc = t == j ? 1.f : 0.f;
 #pragma unroll
         for (int s = 0; s < t; ++s) acc = fmaf(-sF[F_A + 8 * t + s], x[s], acc);
@@ -403,7 +412,7 @@ __global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 3 : 5) void mtp_chunk_kerne
     lds_barrier();
   };
   int t0 = 0;
-  setup_chunk(T < kMtpMaxT ? T : kMtpMaxT);
+  setup_chunk(T < kMtpMaxT ? T : kMtpMaxT, std::false_type{});
   // 64 columns at a time through the wave's staging rows (its own; LDS
   // accesses of a wave complete in order)
 #pragma unroll
@@ -468,11 +477,6 @@ __global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 3 : 5) void mtp_chunk_kerne
       const float bt = sF[F_B + c], gt = sF[F_GAM + c];
 #pragma unroll
       for (int e = 0; e < 4; ++e) X[(4 * gq + e) * XLD + c] = bt * (vv[e] - gt * zy[e]);
-    }
-    // the next chunk's inputs, in flight through the rest of this one
-    if constexpr (MULTI) {
-      if (t0 + kMtpMaxT < T)
-        load_tokens(tok0 + kMtpMaxT, T - t0 - kMtpMaxT < kMtpMaxT ? T - t0 - kMtpMaxT : kMtpMaxT);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);
     // U = R Tinv^T: A[row c][t] = R, B[t][t' = c] = Tinv[c][t]
@@ -553,8 +557,11 @@ __global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 3 : 5) void mtp_chunk_kerne
     }
     t0 += kMtpMaxT;
     if (!MULTI || t0 >= T) break;
+    // the next chunk's inputs (loading them earlier, while this chunk's products
+    // run, takes registers that cost more than the wait)
+    load_tokens(seq0 + t0, T - t0 < kMtpMaxT ? T - t0 : kMtpMaxT);
     lds_barrier();  // every wave is done with this chunk's K, Q and factors
-    setup_chunk(T - t0 < kMtpMaxT ? T - t0 : kMtpMaxT);
+    setup_chunk(T - t0 < kMtpMaxT ? T - t0 : kMtpMaxT, std::true_type{});
   }
   if (state_out) {
     // back through the staging rows, leaving as it arrived: each store
