@@ -350,7 +350,7 @@ __global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 4 : 5) void mtp_chunk_kerne
     lds_barrier();  // the state loads stay in flight
 
     // Gate prefix (fixed order; padding adds g = 0, so G_7 = G_T) and the dot
-    // products k_t.k_s (threads 0-63) and q_t.k_s (64-127), t, s < 8.
+    // products k_t.k_s (slots 8 t + s) and q_t.k_s (slots 64 + 8 t + s), t, s < 8.
     if (tid < kMtpMaxT) {
       float G = 0.f, Gt = 0.f;
       for (int s = 0; s < kMtpMaxT; ++s) {
@@ -361,26 +361,42 @@ __global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 4 : 5) void mtp_chunk_kerne
       sF[F_GAM + tid] = expf(Gt);
       sF[F_D + tid] = tid < Tc ? expf(G - Gt) : 0.f;
     }
-    if (tid < 128) {
-      const int t = (tid >> 3) & 7, s = tid & 7;
-      const float* a = sKQ + ((tid >> 6) ? 8 + t : t) * LDK;
-      const float* b = sKQ + s * LDK;
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependent chains
-      auto step4 = [&](int j) {
-        const floatx4 x = *reinterpret_cast<const floatx4*>(a + j);
-        const floatx4 y = *reinterpret_cast<const floatx4*>(b + j);
+    if (wave == 1) {
+      // [K; Q] K^T on the matrix cores (one wave, beside the gate prefix):
+      // D[r][s] = k_r.k_s (r < 8) or q_{r-8}.k_s, s < 8; B is A's first eight
+      // rows (zero beyond), the contraction index in the same order in both.
+      const float* row = sKQ + c * LDK;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (IN == Dt::BF16) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = fmaf(x[e], y[e], acc[e]);
-      };
-      if constexpr (decltype(lean)::value) {
-        // later chunks: the state's registers are live, so fewer reads in flight
-#pragma unroll 2
-        for (int j = 0; j < DK; j += 4) step4(j);
+        for (int kb = 0; kb < DK / 32; ++kb) {
+          const floatx4 x0 = *reinterpret_cast<const floatx4*>(row + 32 * kb + 8 * gq);
+          const floatx4 x1 = *reinterpret_cast<const floatx4*>(row + 32 * kb + 8 * gq + 4);
+          float xs[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xs[e] = x0[e];
+            xs[4 + e] = x1[e];
+          }
+          bf16x8 a[1];
+          split8<1>(xs, a);  // exact: bf16 inputs
+          const bf16x8 b = c < kMtpMaxT ? a[0] : bf16x8{};
+          acc = mfma16x16x32(a[0], b, acc);
+        }
       } else {
-#pragma unroll 8
-        for (int j = 0; j < DK; j += 4) step4(j);
+#pragma unroll
+        for (int kk = 0; kk < DK / 16; ++kk) {
+          const floatx4 x = *reinterpret_cast<const floatx4*>(row + 16 * kk + 4 * gq);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = mfma4(x[e], c < kMtpMaxT ? x[e] : 0.f, acc);
+        }
       }
-      sF[F_DOT + tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      // lane (c, gq) holds D[4 gq + e][c]; the dot of row r and token s goes to
+      // slot 8 r + s
+      if (c < kMtpMaxT) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sF[F_DOT + 8 * (4 * gq + e) + c] = acc[e];
+      }
     }
     lds_barrier();
     // A (threads 0-63) and P (64-127), one element each
