@@ -288,6 +288,13 @@ __global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 4 : 5) void mtp_chunk_kerne
   __shared__ __align__(16) float sX[NW][16 * XLD];
   constexpr int TLD = 68;  // padded row of the per-wave state staging (floats)
   __shared__ __align__(16) float sT[NW][16 * TLD];
+  // MULTI: the next chunk's k and q rows ([16][DK]) and v rows of this
+  // workgroup ([8 tokens][kMtpRows]) as stored in memory, copied in while the
+  // current chunk is applied (1 KiB per copy instruction)
+  constexpr int ESZ = IN == Dt::BF16 ? 2 : 4;
+  constexpr int KQ_BYTES = 16 * DK * ESZ, V_BYTES = kMtpMaxT * kMtpRows * ESZ;
+  static_assert(KQ_BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "copy tiling");
+  __shared__ __align__(1024) unsigned char sStage[MULTI ? KQ_BYTES + V_BYTES : 1024];
 
   const int pair = blockIdx.x / WPP, r0 = (blockIdx.x % WPP) * kMtpRows;
   if (pair >= NH) return;
@@ -332,16 +339,66 @@ __global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 4 : 5) void mtp_chunk_kerne
     ld[j] = __builtin_nontemporal_load(
         &Sin[((rbase + 4 * (j & 3) + (lane >> 4)) * DK + 64 * (j >> 2) + 4 * (lane & 15)) / 4]);
 
+  // MULTI: the rows of the Tc tokens from token tok0 on into sStage (rows of
+  // tokens t >= Tc repeat the last token; they are zeroed on the way to sKQ),
+  // and their gates into gv, bv.
+  auto stage_tokens = [&](size_t tok0, int Tc) {
+    constexpr int NI = (KQ_BYTES + V_BYTES) / 1024;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+    for (int x = 0; x < (NI + NW - 1) / NW; ++x) {
+      const int i = wv + NW * x;
+      if (i >= NI) break;  // wave-uniform
+      const int b = 1024 * i + 16 * lane;
+      const char* src;
+      if (b < KQ_BYTES) {
+        const int r = b / (DK * ESZ), cb = b % (DK * ESZ), t = r & 7;
+        const size_t tt = tok0 + (t < Tc ? t : Tc - 1);
+        src = static_cast<const char*>(r < 8 ? k : q) + (tt * H + h) * DK * ESZ + cb;
+      } else {
+        const int bv_ = b - KQ_BYTES, t = bv_ / (kMtpRows * ESZ), cb = bv_ % (kMtpRows * ESZ);
+        const size_t tt = tok0 + (t < Tc ? t : Tc - 1);
+        src = static_cast<const char*>(v) + (tt * H + h) * DV * ESZ + r0 * ESZ + cb;
+      }
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                       (__attribute__((address_space(3))) void*)(sStage + 1024 * i),
+                                       16, 0, 0);
+    }
+    gv = 0.f;
+    bv = 0.f;
+    if (tid < kMtpMaxT && tid < Tc) {
+      gv = g[(tok0 + tid) * H + h];
+      bv = beta[(tok0 + tid) * H + h];
+    }
+  };
+  auto staged = [&](int byte) -> float {
+    if constexpr (IN == Dt::BF16)
+      return bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sStage + byte));
+    else
+      return *reinterpret_cast<const float*>(sStage + byte);
+  };
+
   float* W = sT[wave];
   floatx4 st[KT];
   // The chunk of Tc tokens from token tok0 on: its k and q rows and gates into
-  // LDS (from the registers load_tokens filled), its gate prefix, dots, A, P
-  // and Tinv.
+  // LDS (from the registers load_tokens filled, or for later chunks from
+  // sStage), its gate prefix, dots, A, P and Tinv.
   auto setup_chunk = [&](int Tc, auto lean) {
+    if constexpr (decltype(lean)::value) {
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int idx = tid + kMtpThreads * i;
-      sKQ[(idx / DK) * LDK + idx % DK] = tk[i];
+      for (int i = 0; i < TPT; ++i) {
+        const int idx = tid + kMtpThreads * i, rr = idx / DK, col = idx % DK;
+        sKQ[rr * LDK + col] = (rr & 7) < Tc ? staged((rr * DK + col) * ESZ) : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        vv[e] = c < Tc ? staged(KQ_BYTES + (c * kMtpRows + 16 * wave + 4 * gq + e) * ESZ) : 0.f;
+    } else {
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        const int idx = tid + kMtpThreads * i;
+        sKQ[(idx / DK) * LDK + idx % DK] = tk[i];
+      }
     }
     if (tid < kMtpMaxT) {
       sF[F_GRAW + tid] = gv;
@@ -429,6 +486,10 @@ __global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 4 : 5) void mtp_chunk_kerne
   };
   int t0 = 0;
   setup_chunk(T < kMtpMaxT ? T : kMtpMaxT, std::false_type{});
+  // the next chunk's rows, in flight while this one is applied
+  if constexpr (MULTI) {
+    if (kMtpMaxT < T) stage_tokens(seq0 + kMtpMaxT, T - kMtpMaxT < kMtpMaxT ? T - kMtpMaxT : kMtpMaxT);
+  }
   // 64 columns at a time through the wave's staging rows (its own; LDS
   // accesses of a wave complete in order)
 #pragma unroll
@@ -573,11 +634,12 @@ __global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 4 : 5) void mtp_chunk_kerne
     }
     t0 += kMtpMaxT;
     if (!MULTI || t0 >= T) break;
-    // the next chunk's inputs (loading them earlier, while this chunk's products
-    // run, takes registers that cost more than the wait)
-    load_tokens(seq0 + t0, T - t0 < kMtpMaxT ? T - t0 : kMtpMaxT);
-    lds_barrier();  // every wave is done with this chunk's K, Q and factors
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next chunk
+    lds_barrier();  // every wave's have landed, and is done with this chunk's K, Q and factors
     setup_chunk(T - t0 < kMtpMaxT ? T - t0 : kMtpMaxT, std::true_type{});
+    if (t0 + kMtpMaxT < T)
+      stage_tokens(seq0 + t0 + kMtpMaxT,
+                   T - t0 - kMtpMaxT < kMtpMaxT ? T - t0 - kMtpMaxT : kMtpMaxT);
   }
   if (state_out) {
     // back through the staging rows, leaving as it arrived: each store
