@@ -555,7 +555,7 @@ __global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 4 : 5) void mtp_chunk_kerne
 #pragma unroll
       for (int e = 0; e < 4; ++e) X[(4 * gq + e) * XLD + c] = bt * (vv[e] - gt * zy[e]);
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);
+    wave_lds_sync();
     // U = R Tinv^T: A[row c][t] = R, B[t][t' = c] = Tinv[c][t]
     floatx4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -565,12 +565,12 @@ __global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 4 : 5) void mtp_chunk_kerne
       const float b = c < kMtpMaxT ? sF[F_TINV + 8 * c + t] : 0.f;
       u = mfma4(a, b, u);
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);
+    wave_lds_sync();
     if (c < kMtpMaxT) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) X[(4 * gq + e) * XLD + c] = u[e];
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);
+    wave_lds_sync();
     // U in the A layout (row c, token 4 ks + gq), for O and (scaled by D) the update
     float ua[2];
 #pragma unroll

@@ -36,6 +36,18 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Exchange point for the lanes of one wave through LDS, with no barrier:
+// waits for the wave's LDS accesses (in order, so another lane's earlier
+// write is then visible) and keeps the compiler from carrying a value read
+// before the point past it -- for a lane whose own write was skipped, reusing
+// its earlier read of the same address would be legal for threads that do
+// not synchronise, and wrong here.
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+}
+
 // Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15); every lane of the
 // row receives the same bits.  Each stage adds the value of a partner lane
 // whose partner is the lane itself (quad_perm [1,0,3,2] and [2,3,0,1] within
