@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kDecodeThreads) void mtp_kernel(
   }
 }
 
-// Multi-token decode on the matrix cores (T >= 5 tokens, no per-token states;
+// Multi-token decode on the matrix cores (T >= 2 tokens, no per-token states;
 // the kernel itself takes any T >= 1).  The tokens of a (sequence, head) go in
 // chunks of 8 (the last may be shorter), each one chunk of the chunked form of
 // the recurrence applied to the state, which stays in registers from the
@@ -246,11 +246,12 @@ __global__ __launch_bounds__(kDecodeThreads) void mtp_kernel(
 // every workgroup of a head (they are small).
 constexpr int kMtpWaves = 4;               // 16 state rows each
 constexpr int kMtpMaxT = 8;
-// Below this many tokens the token-by-token kernel is faster: the chunked one
-// costs about the same for any T <= 8 (on 64 sequences x 32 heads, d = 128,
-// cold: about 59 us at T = 2 and 4, 60 at T = 6, 62 at T = 8, against 48, 58,
-// about 68 and 78 token by token).
-constexpr int kMtpChunkMinT = 5;
+// From this many tokens on the chunked kernel is the faster: it costs about
+// the same for any T <= 8 (on 64 sequences x 32 heads, d = 128, bf16, four
+// states in rotation: 47-48 us at T = 2 to 6, against 48, 53, 60 and 49 us
+// token by token at T = 2, 3, 4 and 5); T = 1 stays token by token, which is
+// the decode step bit for bit.
+constexpr int kMtpChunkMinT = 2;
 
 // Waves (16 state rows each) of a workgroup at dv.
 template <int DV>
@@ -733,7 +734,7 @@ hipError_t launch_mtp(const void* q, const void* k, const void* v, const float* 
                       int out_dtype, hipStream_t stream) {
   (void)dv;
   const int NH = N * H;
-  // 5 or more tokens without per-token states: the chunked form on the matrix
+  // 2 or more tokens without per-token states: the chunked form on the matrix
   // cores; otherwise (and for T = 1, which then equals the decode step bit for
   // bit) the token-by-token kernel.
   const bool chunked = inter == nullptr && T >= kMtpChunkMinT;

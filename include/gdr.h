@@ -104,7 +104,7 @@ gdr_status gdr_decode_step(const void* q, const void* k, const void* v,
  * (state_in for t = 0), and its output uses the updated state.  The result is
  * that of gdr_chunk_prefill over N packed sequences of T tokens, and T = 1 is
  * gdr_decode_step (bit for bit).  The state is read once and written once
- * whatever T is.  Without `inter`, T >= 5 tokens are applied in chunks of 8
+ * whatever T is.  Without `inter`, T >= 2 tokens are applied in chunks of 8
  * (the last may be shorter) of the chunked form on the matrix cores, other T
  * token by token; the two agree to rounding (1e-3 for bf16 inputs, 1e-5 for
  * fp32 inputs, against the token-by-token recurrence), and each is

@@ -85,11 +85,11 @@ def test_mtp_T1_equals_decode_step_bitwise():
         assert torch.equal(s1, s2)
 
 
-# Without per-token states, T >= 5 tokens take the chunked kernel (every 8
+# Without per-token states, T >= 2 tokens take the chunked kernel (every 8
 # tokens one chunk of the chunked form on the matrix cores, the state kept in
 # registers across the chunks; T > 8 ends on a shorter chunk unless T is a
-# multiple of 8); the T = 3 case takes the token-by-token kernel without
-# per-token states.
+# multiple of 8); T = 1 takes the token-by-token kernel (the decode step,
+# tested below).
 CHUNKED_CASES = {
     "N3-T6-H2-d128-bf16": (3, 6, 2, 128, "bf16", "std"),
     "N2-T8-H3-d64-f32": (2, 8, 3, 64, "f32", "std"),
@@ -103,8 +103,8 @@ CHUNKED_CASES = {
     "N2-T33-H1-d64-f32-steep": (2, 33, 1, 64, "f32", "steep"),
     "N2-T64-H2-d128-bf16-unit": (2, 64, 2, 128, "bf16", "unit"),
     "N1-T64-H3-d128-f32-slow": (1, 64, 3, 128, "f32", "slow"),
-    # below 5 tokens the token-by-token kernel runs without per-token states
-    "N3-T3-H2-d128-bf16-token": (3, 3, 2, 128, "bf16", "std"),
+    "N3-T3-H2-d128-bf16": (3, 3, 2, 128, "bf16", "std"),
+    "N4-T2-H2-d64-f32-slow": (4, 2, 2, 64, "f32", "slow"),
 }
 
 
@@ -135,7 +135,7 @@ def test_mtp_in_place_and_uncommitted():
     assert so is None and torch.equal(x["state0"], before)
     assert torch.equal(o, ref_o) and torch.equal(I, ref_i)
     assert torch.equal(I[:, -1], ref_s)
-    # without intermediates (T >= 5: the chunked kernel): a new final state
+    # without intermediates (T >= 2: the chunked kernel): a new final state
     # and in place give the same bits, and both agree with the token-by-token
     # kernel to rounding
     o2, so2, _ = run_mtp(x, inter=False)
