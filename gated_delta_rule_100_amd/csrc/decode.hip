@@ -267,8 +267,8 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
 // registers through the factor phase of every later chunk, which needs
 // registers for four waves per SIMD instead of five).
 template <int DK, int DV, Dt IN, Dt OUT, bool MULTI>
-// (at least 5 waves per SIMD: 84 VGPRs and no accumulation registers, against
-// 4 waves and a 32-register accumulator copy by default; 62 against 66 us)
+// (one chunk: at least 5 waves per SIMD, which keeps the accumulators out of
+// a second register file; 4 waves by default were slower)
 __global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 4 : 5) void mtp_chunk_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* state_in,
@@ -283,8 +283,8 @@ __global__ __launch_bounds__(64 * kMtpWaves, MULTI ? 4 : 5) void mtp_chunk_kerne
   constexpr int F_GRAW = 0, F_B = 8, F_G = 16, F_GAM = 24, F_D = 32, F_TINV = 40, F_P = 104,
                 F_DOT = 168, F_A = 296, F_N = 360;
   static_assert(DV % kMtpRows == 0 && DK % 16 == 0, "shape");
-  static_assert(kMtpThreads >= 128, "the factor step gives one thread to each of the 2 x 64 dots");
-  __shared__ __align__(16) float sKQ[16 * LDK];  // rows 0-7: k_t, rows 8-15: q_t (zero past T)
+  static_assert(kMtpThreads >= 128, "the factor step gives one thread to each entry of A and P");
+  __shared__ __align__(16) float sKQ[16 * LDK];  // rows 0-7: k_t, rows 8-15: q_t (zero past the chunk)
   __shared__ __align__(16) float sF[F_N];
   __shared__ __align__(16) float sX[NW][16 * XLD];
   constexpr int TLD = 68;  // padded row of the per-wave state staging (floats)
