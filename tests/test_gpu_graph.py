@@ -112,10 +112,11 @@ def test_decode_in_graph():
     _check_replays(g, refill, (o, st), expected)
 
 
-@pytest.mark.parametrize("T, inter", [(8, False), (3, True)])
+@pytest.mark.parametrize("T, inter", [(8, False), (20, False), (3, True)])
 def test_decode_mtp_in_graph(T, inter):
-    # T = 8 without per-token states takes the chunked kernel, T = 3 with them
-    # the token-by-token one
+    # without per-token states the chunked kernel (T = 20: three chunks, the
+    # next chunk's rows copied in while one is applied), with them (T = 3) the
+    # token-by-token one
     import gated_delta_rule_100_amd as gdr
     from gdr_synth import generate
     N, H, D = 8, 4, 128
