@@ -194,29 +194,37 @@ __device__ __forceinline__ void lead_interleave() {
 // state_in, or zero) gives the local end state.  Both chains read the same K, T
 // and gate fragments from LDS, and the two independent chains fill each
 // other's latency in the compute waves.
-template <int D, int C, Dt OUTD, bool OUT, int NH, int NS = 1>
-__global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ offs, ChunkFactors f, const float* state_in, float* state_out,
-    float* state_out2, float* __restrict__ fixed, void* __restrict__ o, int N, int H,
-    int n_slots, int T_total) {
+// The LDS of a scan kernel, one array per kernel (Tag names the kernel and
+// holds its size): both forms in the mixed kernel share one.  The body below
+// names the array directly rather than through a pointer variable, which
+// keeps its addresses compile-time constants.
+template <class Tag>
+__shared__ __align__(1024) unsigned char scan_lds[Tag::BYTES];
+
+template <int D, int C, Dt OUTD, bool OUT, int NH, int NS, bool MIXED>
+struct ScanLds {
+  static constexpr int BYTES = MIXED ? (ScanCfg<D, C, 1>::BYTES > ScanCfg<D, C, 2>::BYTES
+                                            ? ScanCfg<D, C, 1>::BYTES
+                                            : ScanCfg<D, C, 2>::BYTES)
+                                     : ScanCfg<D, C, NH>::BYTES;
+};
+
+// The work of one workgroup: state rows ROWS vb .. ROWS vb + ROWS - 1 of
+// (sequence n, head h), in the LDS array scan_lds<Lds>.
+template <int D, int C, Dt OUTD, bool OUT, int NH, int NS, class Lds>
+__device__ __forceinline__ void scan_workgroup(
+    int n, int h, int vb, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ offs, const ChunkFactors& f,
+    const float* state_in, float* state_out, float* state_out2, float* __restrict__ fixed,
+    void* __restrict__ o, int H, int n_slots, int T_total) {
   static_assert(NS == 1 || (NS == 2 && !OUT && NH == 1), "two chains: no outputs, whole tiles");
   using Cfg = ScanCfg<D, C, NH>;
   constexpr int NT = Cfg::NT, KB = Cfg::KB, KH = Cfg::KH, CB = Cfg::CB, JT = Cfg::JT;
   constexpr int NO = Cfg::NO;
-  constexpr int CHD = Cfg::CHD, CHC = Cfg::CHC, TL = Cfg::TL, NVB = Cfg::NVB;
+  constexpr int CHD = Cfg::CHD, CHC = Cfg::CHC, TL = Cfg::TL;
   constexpr int CHV = Cfg::ROWS / 8;  // 16-byte chunks per staged v row
-  __shared__ __align__(1024) unsigned char smem[Cfg::BYTES];
-
-  // XCD-aware placement: linear ids with the same residue mod 8 share an XCD,
-  // so the workgroups of one (sequence, head) share its L2.
-  const int lin = blockIdx.x;
-  const int xcd = lin % kXcds, r = lin / kXcds;
-  const int vb = r % NVB;
-  const int pair = (r / NVB) * kXcds + xcd;
-  if (pair >= N * H) return;
-  const int n = pair / H, h = pair % H;
+  static_assert(Lds::BYTES >= Cfg::BYTES, "LDS");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, g4 = lane >> 4;
 
@@ -310,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
       const size_t slot = static_cast<size_t>(s) * H + h;
       const char* ts = reinterpret_cast<const char*>(f.t + slot * TL);
       const char* ps = reinterpret_cast<const char*>(f.p + slot * 2 * TL);
-      unsigned char* buf = smem + ((s - c0) & 1) * Cfg::BUF;
+      unsigned char* buf = scan_lds<Lds> + ((s - c0) & 1) * Cfg::BUF;
       if (last == C - 1) {
 #pragma unroll
         for (int x = 0; x < Cfg::SK; ++x) copy16(ks + kfull[x], buf + Cfg::OFF_K + 1024 * (cw + kCopyWaves * x));
@@ -391,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
     // U^T P^T: half 0 takes tiles 0 and 3, half 1 tiles 1 and 2 (tile a needs
     // blocks kb <= a / 2; four token tiles, C = 64).  Tile u of half x (NH = 2):
     auto otile = [](int x, int u) { return u == 0 ? x : 3 - x; };
-    float* xch = reinterpret_cast<float*>(smem + Cfg::OFF_X);
+    float* xch = reinterpret_cast<float*>(scan_lds<Lds> + Cfg::OFF_X);
     auto xslot = [&](int w, int x) {
       return reinterpret_cast<floatx4*>(xch) + (x * kComputeWaves + w) * 64 + lane;
     };
@@ -408,7 +416,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
       // copies of the step below reads LDS at loop-invariant addresses.
       auto step = [&](int s, auto bsel) {
         using B = decltype(bsel);
-        const unsigned char* buf = smem + B::value * Cfg::BUF;
+        const unsigned char* buf = scan_lds<Lds> + B::value * Cfg::BUF;
         const uint16_t* Kl = reinterpret_cast<const uint16_t*>(buf + Cfg::OFF_K);
         const uint16_t* Ql = reinterpret_cast<const uint16_t*>(buf + Cfg::OFF_Q);
         const uint16_t* Tl = reinterpret_cast<const uint16_t*>(buf + Cfg::OFF_T);
@@ -697,9 +705,114 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
   }
 }
 
-// Workgroups of the column-split form (NH = 2) that fit the GPU at once: MI355X
-// has 256 compute units and one scan workgroup fills one (its LDS).
-constexpr int64_t kSplitMaxGroups = 256;
+template <int D, int C, Dt OUTD, bool OUT, int NH, int NS = 1>
+__global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ offs, ChunkFactors f, const float* state_in, float* state_out,
+    float* state_out2, float* __restrict__ fixed, void* __restrict__ o, int N, int H,
+    int n_slots, int T_total) {
+  using Cfg = ScanCfg<D, C, NH>;
+  // XCD-aware placement: linear ids with the same residue mod 8 share an XCD,
+  // so the workgroups of one (sequence, head) share its L2.
+  const int lin = blockIdx.x;
+  const int xcd = lin % kXcds, r = lin / kXcds;
+  const int vb = r % Cfg::NVB;
+  const int pair = (r / Cfg::NVB) * kXcds + xcd;
+  if (pair >= N * H) return;
+  scan_workgroup<D, C, OUTD, OUT, NH, NS, ScanLds<D, C, OUTD, OUT, NH, NS, false>>(
+      pair / H, pair % H, vb, q, k, v, cu, offs, f, state_in, state_out, state_out2, fixed, o, H,
+      n_slots, T_total);
+}
+
+// MI355X has 256 compute units and one scan workgroup fills one (its LDS).
+constexpr int kCus = 256;
+// Workgroups of the column-split form (NH = 2) that fit the GPU at once.
+constexpr int64_t kSplitMaxGroups = kCus;
+
+// Mixed launch: when the column split of every sequence does not fit the GPU
+// at once, the sequence with the most chunks may still take it while the
+// others run in whole tiles.  A chunk step of the split form takes about
+// 0.887 of the whole-tile step on a busy GPU (2.27 against 2.56 us at
+// d = 128, both measured with every compute unit running a scan workgroup).
+constexpr int64_t kStepSplit = 887, kStepWhole = 1000;
+constexpr int kMixedMaxN = 63;  // one lane per chunk offset
+
+// The sequence that the mixed launch runs in the split form, or -1 for none.
+// Every wave of every workgroup reaches the same answer from the chunk
+// offsets.  The candidate is the sequence with the most chunks (the first of
+// equal ones).  It is split when the modelled time of the launch falls:
+//   whole tiles: max(its chain, all workgroup-steps / compute units),
+//   mixed:       max(its chain at the split step, the longest other chain,
+//                    the other workgroup-steps / the compute units left).
+template <int NVB1, int NVB2>
+__device__ __forceinline__ int mixed_split_choice(const int32_t* __restrict__ offs, int N, int H,
+                                                  int n_slots) {
+  const int lane = threadIdx.x & 63;
+  int a = lane <= N ? offs[lane] : 0;
+  a = a < 0 ? 0 : (a > n_slots ? n_slots : a);
+  const int b = __shfl_down(a, 1);
+  const int cnt = lane < N && b > a ? b - a : 0;  // < 2^25 chunks: the key fits 31 bits
+  int key = (cnt << 6) | (63 - lane), sum = cnt;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const int ok = __shfl_xor(key, m);
+    key = ok > key ? ok : key;
+    sum += __shfl_xor(sum, m);
+  }
+  const int star = 63 - (key & 63);
+  const int64_t lmax = key >> 6;
+  int other = lane != star ? cnt : 0;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const int oo = __shfl_xor(other, m);
+    other = oo > other ? oo : other;
+  }
+  const int64_t all_steps = static_cast<int64_t>(sum) * H * NVB1;
+  const int64_t rest_steps = (sum - lmax) * H * NVB1;
+  const int64_t free_cus = kCus - static_cast<int64_t>(H) * NVB2;
+  const int64_t spread_all = (all_steps + kCus - 1) / kCus;
+  const int64_t spread_rest = (rest_steps + free_cus - 1) / free_cus;
+  const int64_t t_whole = kStepWhole * (lmax > spread_all ? lmax : spread_all);
+  const int64_t t_rest = kStepWhole * (other > spread_rest ? other : spread_rest);
+  const int64_t t_mixed = kStepSplit * lmax > t_rest ? kStepSplit * lmax : t_rest;
+  return __builtin_amdgcn_readfirstlane(lmax > 0 && t_mixed < t_whole ? star : -1);
+}
+
+// Linear ids [0, split_groups) are the split form's workgroups of the chosen
+// sequence (XCD-aware as above, over its heads); the rest are the whole-tile
+// workgroups of every (sequence, head) pair, of which the chosen sequence's
+// exit at once.  When no sequence is chosen, the first part exits instead.
+// Both forms give identical bits, so the choice changes no result.
+template <int D, int C, Dt OUTD, bool OUT>
+__global__ __launch_bounds__(kThreads) void chunk_scan_mixed_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ offs, ChunkFactors f, const float* state_in, float* state_out,
+    float* __restrict__ fixed, void* __restrict__ o, int N, int H, int n_slots, int T_total,
+    int split_groups) {
+  using C1 = ScanCfg<D, C, 1>;
+  using C2 = ScanCfg<D, C, 2>;
+  using Lds = ScanLds<D, C, OUTD, OUT, 1, 1, true>;
+  const int star = mixed_split_choice<C1::NVB, C2::NVB>(offs, N, H, n_slots);
+  const int lin = blockIdx.x;
+  const int xcd = lin % kXcds;
+  if (lin < split_groups) {
+    if (star < 0) return;
+    const int r = lin / kXcds, vb = r % C2::NVB;
+    const int h = (r / C2::NVB) * kXcds + xcd;
+    if (h >= H) return;
+    scan_workgroup<D, C, OUTD, OUT, 2, 1, Lds>(star, h, vb, q, k, v, cu, offs, f, state_in,
+                                                state_out, nullptr, fixed, o, H, n_slots, T_total);
+    return;
+  }
+  const int r = (lin - split_groups) / kXcds, vb = r % C1::NVB;
+  const int pair = (r / C1::NVB) * kXcds + xcd;
+  if (pair >= N * H || pair / H == star) return;
+  scan_workgroup<D, C, OUTD, OUT, 1, 1, Lds>(pair / H, pair % H, vb, q, k, v, cu, offs, f,
+                                              state_in, state_out, nullptr, fixed, o, H, n_slots,
+                                              T_total);
+}
 
 template <int D, int C, Dt OUTD, bool OUT, int NH, int NS = 1>
 hipError_t scan_launch(const void* q, const void* k, const void* v, const int32_t* cu,
@@ -729,9 +842,26 @@ hipError_t scan_t(const void* q, const void* k, const void* v, const int32_t* cu
                   const int32_t* offs, const ChunkFactors& f, const float* state_in,
                   float* state_out, float* fixed, void* o, int N, int H, int n_slots, int T_total,
                   hipStream_t stream) {
-  const int64_t split_groups = (static_cast<int64_t>(N) * H + kXcds - 1) / kXcds * kXcds *
-                               ScanCfg<D, C, 2>::NVB;
+  constexpr int NVB1 = ScanCfg<D, C, 1>::NVB, NVB2 = ScanCfg<D, C, 2>::NVB;
+  const int64_t split_groups = (static_cast<int64_t>(N) * H + kXcds - 1) / kXcds * kXcds * NVB2;
   const bool split = split_groups <= kSplitMaxGroups;
+  if (!split && N <= kMixedMaxN && static_cast<int64_t>(H) * NVB2 <= kCus / 2) {
+    // the split part covers the heads of one sequence
+    const int64_t head_groups = (static_cast<int64_t>(H) + kXcds - 1) / kXcds * kXcds * NVB2;
+    const int64_t groups =
+        head_groups + (static_cast<int64_t>(N) * H + kXcds - 1) / kXcds * kXcds * NVB1;
+    if (groups > INT32_MAX) return hipErrorInvalidConfiguration;
+#define GDR_SCAN_M(OUT_)                                                                        \
+  hipLaunchKernelGGL((chunk_scan_mixed_kernel<D, C, OUTD, OUT_>),                               \
+                     dim3(static_cast<unsigned>(groups)), dim3(kThreads), 0, stream,            \
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),          \
+                     static_cast<const uint16_t*>(v), cu, offs, f, state_in, state_out, fixed, o, \
+                     N, H, n_slots, T_total, static_cast<int>(head_groups))
+    if (o) GDR_SCAN_M(true);
+    else GDR_SCAN_M(false);
+#undef GDR_SCAN_M
+    return hipGetLastError();
+  }
 #define GDR_SCAN_L(OUT_, NH_)                                                                   \
   return scan_launch<D, C, OUTD, OUT_, NH_>(q, k, v, cu, offs, f, state_in, state_out, nullptr, \
                                             fixed, o, N, H, n_slots, T_total, stream)

@@ -217,6 +217,35 @@ def test_prefill_scan_forms_agree_bitwise():
         assert torch.equal(single["fixed"][:nc], packed["fixed"][c0:c0 + nc])
 
 
+@pytest.mark.parametrize("dk", [128, 64])
+def test_prefill_mixed_scan_agrees_bitwise(dk):
+    # A batch whose column-split workgroups do not all fit the GPU at once but
+    # whose longest sequence dominates: the scan runs that sequence in the
+    # split form and the others in whole tiles, in one launch.  Each sequence
+    # run alone takes the split form; both agree bit for bit, wherever the long
+    # sequence sits in the batch.
+    lens = [37, 0, 64, 5, 1, 650, 20, 129]
+    d = workload(3, seed=131, seqlens=lens, H=32, dk=dk, dv=dk)
+    say(f"prefill mixed scan: N={len(lens)} H=32 d={dk} T={d['T']} (long sequence 5)")
+    packed = run_prefill(d, schedule="scan")
+    check_against_oracle(d, packed, d["chunk"], check_locals=False)
+    cu = d["cu_seqlens"]
+    for n in range(len(lens)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        sub = dict(d)
+        for key in ("q", "k", "v", "g", "beta"):
+            sub[key] = np.ascontiguousarray(d[key][a:b])
+        sub["state0"] = np.ascontiguousarray(d["state0"][n:n + 1])
+        sub["cu_seqlens"] = np.array([0, b - a], dtype=np.int32)
+        sub["N"], sub["T"] = 1, b - a
+        single = run_prefill(sub, schedule="scan")
+        assert torch.equal(single["o"], packed["o"][a:b])
+        assert torch.equal(single["state_out"][0], packed["state_out"][n])
+        c0 = int(np.sum((np.array(lens[:n]) + 63) // 64))
+        nc = (b - a + 63) // 64
+        assert torch.equal(single["fixed"][:nc], packed["fixed"][c0:c0 + nc])
+
+
 def test_prefill_workspace_on_side_stream():
     """With no workspace given, the binding allocates one on the launch stream:
     a prefill on a side stream followed at once by allocations and writes on
