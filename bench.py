@@ -70,12 +70,12 @@ PRE_IO_BYTES = PRE_TOKENS * PRE_H * (3 * PRE_D * 2 + PRE_D * 2 + 8) \
 PRE_CHUNK_HEADS = PRE_B * (PRE_T // PRE_C) * PRE_H
 PRE_CP_BYTES = PRE_IO_BYTES + PRE_CHUNK_HEADS * 393216
 # The sequential-scan schedule (taken for this workload) moves per chunk-head
-# the factors the chunk kernel writes (T and P compact lower-triangular: T as
-# one fp16 plane, 6 KiB, P as a bf16 plane pair, 12 KiB, and 1 KiB of gates),
+# the factors the chunk kernel writes (T and P compact lower-triangular, each
+# one fp16 plane of 6 KiB, and 1 KiB of gates),
 # which the scan reads back once, together with a second read of the chunk's
 # q and k rows (16 KiB each; the factors kernel and the scan both read them),
 # on top of the unavoidable input/output.
-PRE_FACTOR_W = 6144 + 12288 + 1024
+PRE_FACTOR_W = 6144 + 6144 + 1024
 PRE_FACTOR_R = PRE_FACTOR_W + 2 * 16384
 PRE_SCAN_BYTES = PRE_IO_BYTES + PRE_CHUNK_HEADS * (PRE_FACTOR_W + PRE_FACTOR_R)
 # long workload: one sequence of 131072 tokens, 4 heads: 2048 chunks per head

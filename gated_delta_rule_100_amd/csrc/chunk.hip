@@ -69,7 +69,7 @@ struct ChunkCfg {
   static constexpr int AOFF_BYTES = r16(mx(NOFF, 1) * PT * BLK_PS * 2);
   static constexpr int LDA = 20;                          // row stride of A_ii (16-byte rows)
   static constexpr int DIAG_BLK = r16(mx(16 * LDA * 4, PT * BLK_PS * 2));  // A_ii fp32, then T_ii planes
-  static constexpr int P_BYTES = TF ? r16(PT * TL_PLANE * 2) : OUT ? r16(PT * P_PS * 2) : 0;
+  static constexpr int P_BYTES = TF ? r16(TL_PLANE * 2) : OUT ? r16(PT * P_PS * 2) : 0;
   static constexpr int GATE_BYTES = (6 * C + 4) * 4;  // six vectors and a spare slot
   static constexpr int OFF_KR = 0;
   static constexpr int OFF_VR = KT_BYTES;
@@ -377,8 +377,8 @@ struct ChunkWork {
   // 16 tj + 4 g .. +3), which go to LDS as one 8-byte write per plane:
   //   A_ts = beta_t Gamma_ts (k_t . k_s), s < t: diagonal blocks fp32 (zero on
   //     and above the diagonal), strictly lower blocks as planes;
-  //   P = (Q K^T) (.) Gamma (s <= t, zero elsewhere) as planes in the compact
-  //     lower layout (rows t < C/2 keep C/2 columns), each row in operand-slot
+  //   P = (Q K^T) (.) Gamma (s <= t, zero elsewhere) as one fp16 plane of
+  //     kPScale P (round to nearest even) in the compact lower layout (rows t < C/2 keep C/2 columns), each row in operand-slot
   //     order: column 16 tj + c of 32-block tj/2 sits at slot
   //     8 (c/4) + 4 (tj % 2) + c % 4; in LDS the 16-byte pieces of a row are
   //     permuted (tl_piece).
@@ -438,13 +438,11 @@ struct ChunkWork {
           const float y = acc[e] * decay(Gt, Gs[e]);
           x[e] = s <= t ? y : 0.f;
         }
-        uint32_t lo[PT], hi[PT];
-        split2<PT>(x[0], x[1], lo);
-        split2<PT>(x[2], x[3], hi);
+        uint32_t lo[1], hi[1];
+        split2_h<1>(kPScale * x[0], kPScale * x[1], lo);
+        split2_h<1>(kPScale * x[2], kPScale * x[3], hi);
         uint16_t* dst = Pp() + tl_piece(t, 4 * (tj >> 1) + g4) + 4 * (tj & 1);
-#pragma unroll
-        for (int p = 0; p < PT; ++p)
-          *reinterpret_cast<uint2*>(dst + p * Cfg::TL_PLANE) = make_uint2(lo[p], hi[p]);
+        *reinterpret_cast<uint2*>(dst) = make_uint2(lo[0], hi[0]);
       }
     }
   }
@@ -995,18 +993,15 @@ __global__ __launch_bounds__(256, 2) void chunk_factors_kernel(
   }
   __syncthreads();  // T and P planes complete
   uint16_t* tg = f.t + slot * TLP;
-  uint16_t* pg = f.p + slot * PT * TLP;
+  uint16_t* pg = f.p + slot * TLP;
   // global piece idx (the compact layout, unpermuted) from its LDS position
-  for (int idx = w.tid; idx < PT * TLP / 8; idx += 256) {
-    const int pl = idx / (TLP / 8), r = idx % (TLP / 8);
+  for (int idx = w.tid; idx < TLP / 8; idx += 256) {
     constexpr int LO = (C / 2) * (C / 2) / 8;  // pieces of the rows t < C/2
-    const int t = r < LO ? r / (C / 16) : C / 2 + (r - LO) / (C / 8);
-    const int pc = r < LO ? r % (C / 16) : (r - LO) % (C / 8);
+    const int t = idx < LO ? idx / (C / 16) : C / 2 + (idx - LO) / (C / 8);
+    const int pc = idx < LO ? idx % (C / 16) : (idx - LO) % (C / 8);
     const int src = W_::tl_piece(t, pc);
-    if (idx < TLP / 8)
-      *reinterpret_cast<uint4*>(tg + 8 * idx) = *reinterpret_cast<const uint4*>(w.Tl() + src);
-    *reinterpret_cast<uint4*>(pg + 8 * idx) =
-        *reinterpret_cast<const uint4*>(w.Pp() + pl * TLP + src);
+    *reinterpret_cast<uint4*>(tg + 8 * idx) = *reinterpret_cast<const uint4*>(w.Tl() + src);
+    *reinterpret_cast<uint4*>(pg + 8 * idx) = *reinterpret_cast<const uint4*>(w.Pp() + src);
   }
 }
 

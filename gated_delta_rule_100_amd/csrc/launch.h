@@ -72,13 +72,16 @@ hipError_t launch_final_state(const float* state_in, const float* fixed,
 // elements per plane); P rows store their contraction index in operand-slot
 // order (chunk.hip):
 //   t     [slots][H][TL]      kTScale T, T = (I + A)^{-1}, as one fp16 plane
-//   p     [slots][H][2][TL]   P = (Q K^T) (.) Gamma (s <= t) as bf16 hi/lo planes
+//   p     [slots][H][TL]      kPScale P, P = (Q K^T) (.) Gamma (s <= t), as one
+//                             fp16 plane
 //   gate  [slots][H][4][C]    gamma_t, D_t, beta_t / kTScale and zeros, fp32
-// The scan forms U = T diag(beta) R as (kTScale T)(diag(beta / kTScale) R),
-// exactly the same product: the power-of-two scale moves the fp16 range of
-// the R planes up by kTScale (fp16 holds T with its unit diagonal exactly and
-// its other entries to 11 bits).
+// The scan forms U = T diag(beta) R as (kTScale T)(diag(beta / kTScale) R)
+// and P U as (kPScale P)(U / kPScale), exactly the same products: the
+// power-of-two scales move the fp16 range of the R and U planes up by 16
+// (fp16 holds T with its unit diagonal exactly and its other entries, and P,
+// to 11 bits).
 constexpr float kTScale = 16.f;
+constexpr float kPScale = 16.f;
 struct ChunkFactors {
   uint16_t* t;
   uint16_t* p;
@@ -93,7 +96,7 @@ inline ChunkFactorSizes chunk_factor_sizes(int slots, int H, int chunk) {
   const size_t n = static_cast<size_t>(slots) * H;
   const size_t c = static_cast<size_t>(chunk);
   const size_t tl = 3 * c * c / 4;
-  return {n * tl * 2, n * 2 * tl * 2, n * 4 * c * 4};
+  return {n * tl * 2, n * tl * 2, n * 4 * c * 4};
 }
 
 // Factors of every chunk slot < max_chunks (bf16 inputs, chunk 64).

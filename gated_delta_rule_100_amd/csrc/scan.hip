@@ -28,10 +28,11 @@
 // tokens as rows; two of them stacked are an operand fragment in slot order,
 // which is how R meets T (whose rows are stored in slot order) and U meets P
 // and K^T.  k, q, v are exact bf16; fp32 operands are hi/lo planes: bf16
-// planes, except in U = T R, where T is one fp16 plane and R two (fp16's
-// 11-bit significand holds T well enough for the 1e-3 budget, one bf16 plane
-// would not).  The compute waves read only LDS and write their outputs and
-// states straight to global memory.
+// planes, except in U = T R, where T is one fp16 plane and R two, and in
+// P U, where P is one fp16 plane and U two (fp16's 11-bit significand holds
+// T and P well enough for the 1e-3 budget, one bf16 plane would not).  The
+// compute waves read only LDS and write their outputs and states straight to
+// global memory.
 //
 // Copy waves.  Four more waves move each chunk's k, q, v rows, T, P and gates
 // into LDS with direct global-to-LDS loads, one chunk ahead: LDS holds two
@@ -74,15 +75,15 @@ struct ScanCfg {
   static constexpr int JT = ND / NH;                    // 16-wide column tiles per wave
   static constexpr int NO = NT / NH;                    // output token tiles per wave
   // T and P planes: rows t < C/2 keep their first C/2 columns (the rest is
-  // above the diagonal), rows t >= C/2 keep all C.  T is one fp16 plane, P
-  // two bf16 planes.
+  // above the diagonal), rows t >= C/2 keep all C.  T and P are one fp16
+  // plane each.
   static constexpr int TL_LO = (C / 2) * (C / 2);
   static constexpr int TL = TL_LO + (C / 2) * C;
   // regions of one chunk buffer (bytes); each a whole number of 1 KiB blocks
   static constexpr int K_BYTES = C * D * 2;
   static constexpr int Q_BYTES = C * D * 2;
   static constexpr int T_BYTES = TL * 2;
-  static constexpr int P_BYTES = 2 * TL * 2;
+  static constexpr int P_BYTES = TL * 2;
   static constexpr int V_BYTES = C * ROWS * 2;
   static constexpr int G_BYTES = 4 * C * 4;  // gamma, D, beta, zeros
   static constexpr int OFF_K = 0;
@@ -98,14 +99,14 @@ struct ScanCfg {
   static constexpr int OFF_X = 2 * BUF;
   static constexpr int BYTES = 2 * BUF + X_SLOTS * kComputeWaves * 64 * 16;
   // copy instructions (1 KiB each) per region, and each copy wave's share
-  // (T: the first NTT % kCopyWaves copy waves issue one more)
+  // (T and P: the first NTT % kCopyWaves copy waves issue one more)
   static constexpr int NK = K_BYTES / 1024, NQ = Q_BYTES / 1024, NTT = T_BYTES / 1024;
   static constexpr int NP = P_BYTES / 1024, NV = V_BYTES / 1024;
-  static constexpr int SK = NK / kCopyWaves, SQ = NQ / kCopyWaves, SP = NP / kCopyWaves;
-  static constexpr int STT = (NTT + kCopyWaves - 1) / kCopyWaves;
+  static constexpr int SK = NK / kCopyWaves, SQ = NQ / kCopyWaves;
+  static constexpr int STT = (NTT + kCopyWaves - 1) / kCopyWaves, SP = STT;
   static constexpr int SV = NV / kCopyWaves;
   static_assert(C == 64 && (D == 64 || D == 128) && (NH == 1 || NH == 2), "shape");
-  static_assert(K_BYTES % (1024 * kCopyWaves) == 0 && P_BYTES % (1024 * kCopyWaves) == 0 &&
+  static_assert(K_BYTES % (1024 * kCopyWaves) == 0 && P_BYTES == T_BYTES &&
                     T_BYTES % 1024 == 0 && V_BYTES % (1024 * kCopyWaves) == 0 &&
                     G_BYTES == 1024,
                 "copy tiling");
@@ -253,11 +254,11 @@ __device__ __forceinline__ void scan_workgroup(
     const uint32_t row_bytes = 2u * static_cast<uint32_t>(H) * D;  // one token row of q, k, v
     // per-lane source offsets of this wave's copies: chunk row and byte offset
     // inside the row (k, q, v), the two combined for a full chunk, and the
-    // byte offset in a T or P slot
+    // byte offset in a T or P slot (the same compact layout)
     int krow[Cfg::SK], qrow[Cfg::SQ], vrow[Cfg::SV];
     uint32_t kcol[Cfg::SK], qcol[Cfg::SQ], vcol[Cfg::SV];
     uint32_t kfull[Cfg::SK], qfull[Cfg::SQ], vfull[Cfg::SV];
-    uint32_t toff[Cfg::STT], poff[Cfg::SP];
+    uint32_t toff[Cfg::STT];
 #pragma unroll
     for (int x = 0; x < Cfg::SK; ++x) {
       const int p = 64 * (cw + kCopyWaves * x) + lane, t = p / CHD, pc = p % CHD;
@@ -299,8 +300,6 @@ __device__ __forceinline__ void scan_workgroup(
       const int i = cw + kCopyWaves * x;
       toff[x] = tl_piece(64 * (i < Cfg::NTT ? i : 0) + lane);
     }
-#pragma unroll
-    for (int x = 0; x < Cfg::SP; ++x) poff[x] = tl_piece(64 * (cw + kCopyWaves * x) + lane);
     const uint32_t goff = 16u * lane;
     // Chunk s into buffer (s - c0) & 1.  In a chunk shorter than C, rows past
     // its end repeat its last token (their beta is zero, so they leave U, O
@@ -317,7 +316,7 @@ __device__ __forceinline__ void scan_workgroup(
       const char* vs = reinterpret_cast<const char*>(v + tbase);
       const size_t slot = static_cast<size_t>(s) * H + h;
       const char* ts = reinterpret_cast<const char*>(f.t + slot * TL);
-      const char* ps = reinterpret_cast<const char*>(f.p + slot * 2 * TL);
+      const char* ps = reinterpret_cast<const char*>(f.p + slot * TL);
       unsigned char* buf = scan_lds<Lds> + ((s - c0) & 1) * Cfg::BUF;
       if (last == C - 1) {
 #pragma unroll
@@ -350,7 +349,9 @@ __device__ __forceinline__ void scan_workgroup(
           copy16(ts + toff[x], buf + Cfg::OFF_T + 1024 * (cw + kCopyWaves * x));
       if constexpr (OUT) {
 #pragma unroll
-        for (int x = 0; x < Cfg::SP; ++x) copy16(ps + poff[x], buf + Cfg::OFF_P + 1024 * (cw + kCopyWaves * x));
+        for (int x = 0; x < Cfg::SP; ++x)
+          if (cw + kCopyWaves * x < Cfg::NP)  // wave-uniform
+            copy16(ps + toff[x], buf + Cfg::OFF_P + 1024 * (cw + kCopyWaves * x));
       }
       if (cw == 0) copy16(reinterpret_cast<const char*>(f.gate + slot * 4 * C) + goff, buf + Cfg::OFF_G);
     };
@@ -573,9 +574,11 @@ __device__ __forceinline__ void scan_workgroup(
           }
         }
 
-        // U as operand planes (32 tokens per block, slot order), plain and
-        // scaled by D.
-        bf16x8 ub[CB][2], udb[NS][CB][2];
+        // U as operand planes (32 tokens per block, slot order): U / kPScale
+        // as two fp16 planes against the fp16 plane of kPScale P, and
+        // diag(D) U as two bf16 planes against the exact K.
+        halfx8 ub[CB][2];
+        bf16x8 udb[NS][CB][2];
 #pragma unroll
         for (int kb = 0; kb < CB; ++kb) {
 #pragma unroll
@@ -584,10 +587,10 @@ __device__ __forceinline__ void scan_workgroup(
 #pragma unroll
             for (int e2 = 0; e2 < 8; ++e2) {
               const int a0 = 2 * kb + e2 / 4, e = e2 & 3;
-              x[e2] = U[ch][a0][e];
+              x[e2] = U[ch][a0][e] * (1.f / kPScale);  // exact: a power of two
               xd[e2] = Gl[C + 16 * a0 + 4 * g4 + e] * U[ch][a0][e];
             }
-            if constexpr (OUT) split8<2>(x, ub[kb]);
+            if constexpr (OUT) split8_h<2>(x, ub[kb]);
             split8<2>(xd, udb[ch][kb]);
           }
         }
@@ -607,26 +610,21 @@ __device__ __forceinline__ void scan_workgroup(
 #pragma unroll
           for (int kb = 0; kb < CB; ++kb) {
             // tiles with a / 2 >= kb: NH = 1: a >= 2 kb; NH = 2: u >= kb
-            bf16x8 pa[NO][2];
+            halfx8 pa[NO];
 #pragma unroll
             for (int u = 0; u < NO; ++u) {
               if (NH == 1 ? u < 2 * kb : u < kb) continue;
               const int t = 16 * at[u] + c16;
               const int ch = (NH == 1 ? u < NT / 2 : u == 0) ? CHC / 2 : CHC;
-#pragma unroll
-              for (int p = 0; p < 2; ++p)
-                pa[u][p] = *reinterpret_cast<const bf16x8*>(Pl + p * TL + tl_row<C>(t) +
-                                                            8 * ((4 * kb + g4) ^ swz(t, ch)));
+              pa[u] = *reinterpret_cast<const halfx8*>(Pl + tl_row<C>(t) +
+                                                       8 * ((4 * kb + g4) ^ swz(t, ch)));
             }
 #pragma unroll
             for (int u = 0; u < NO; ++u)
-              if (NH == 1 ? u >= 2 * kb : u >= kb) oa[u] = mfma16x16x32(ub[kb][1], pa[u][0], oa[u]);
+              if (NH == 1 ? u >= 2 * kb : u >= kb) oa[u] = mfma16x16x32(ub[kb][1], pa[u], oa[u]);
 #pragma unroll
             for (int u = 0; u < NO; ++u)
-              if (NH == 1 ? u >= 2 * kb : u >= kb) oa[u] = mfma16x16x32(ub[kb][0], pa[u][1], oa[u]);
-#pragma unroll
-            for (int u = 0; u < NO; ++u)
-              if (NH == 1 ? u >= 2 * kb : u >= kb) oa[u] = mfma16x16x32(ub[kb][0], pa[u][0], oa[u]);
+              if (NH == 1 ? u >= 2 * kb : u >= kb) oa[u] = mfma16x16x32(ub[kb][0], pa[u], oa[u]);
           }
           int tok0;
           const int cl = chunk_range(s, tok0);

@@ -215,11 +215,11 @@ size_t gdr_chunk_prefill_workspace_bytes(int T_total, int N, int H, int dk, int 
  *     transfer matrices), the segment-level fixup, and a final pass from every
  *     segment's true start.  When L_out or
  *     M_out is given, the chunk-local kernel of the chunk-parallel form writes
- *     them in parallel, before the scan.  The scan holds T as one fp16 plane
- *     (scaled by 16) and beta (V - diag(gamma) K S^T) / 16 as two fp16 planes:
- *     entries of beta (v - gamma S k) beyond about 1e6 in magnitude overflow
- *     to non-finite results (keys are expected L2-normalised, as the method
- *     assumes).
+ *     them in parallel, before the scan.  The scan holds T and P as one fp16
+ *     plane each (scaled by 16), and beta (V - diag(gamma) K S^T) / 16 and
+ *     U / 16 as two fp16 planes each: entries of beta (v - gamma S k) or of U
+ *     beyond about 1e6 in magnitude overflow to non-finite results (keys are
+ *     expected L2-normalised, as the method assumes).
  */
 gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v,
                              const float* g, const float* beta,
@@ -242,7 +242,7 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v,
  * (134,217,728 bytes) on each GPU it runs on, held from the first call on that
  * GPU until the process ends.  A call that needs more than that (see
  * gdr_chunk_prefill_workspace_bytes; e.g. 4 sequences x 4096 tokens x 16 heads
- * at d = 128 needs about 107 MB) returns GDR_ERR_UNSUPPORTED with a message
+ * at d = 128 needs about 55 MB) returns GDR_ERR_UNSUPPORTED with a message
  * and launches nothing.  Nothing is allocated or freed, here or on later
  * calls.  All calls on one GPU share its array, which keeps the last call's
  * contents (no call depends on them): calls that may overlap on one GPU, from

@@ -56,11 +56,11 @@ def test_max_chunks_and_workspace(lib):
     mc = g.gdr_max_chunks(16384, 4, 64)
     assert mc == 260
     # bf16 inputs at chunk 64 take the scan: the layout integers (offsets and
-    # chunk indices, each rounded up to 256 bytes) and the chunk factors, T as
-    # one fp16 plane and P as two bf16 planes of 3072 elements each, plus
-    # 4 x 64 fp32 gate values per chunk-head: 19,456 bytes
+    # chunk indices, each rounded up to 256 bytes) and the chunk factors, T and
+    # P as one fp16 plane of 3072 elements each, plus 4 x 64 fp32 gate values
+    # per chunk-head: 13,312 bytes
     ws = g.gdr_chunk_prefill_workspace_bytes(16384, 4, 16, 128, 128, 64, g.GDR_BF16)
-    assert ws == 256 + 2304 + mc * 16 * 19456
+    assert ws == 256 + 2304 + mc * 16 * 13312
     # fp32 inputs take the chunk-parallel form with L, M and fixed in the workspace
     for chunk in (16, 64):
         mcc = g.gdr_max_chunks(16384, 4, chunk)

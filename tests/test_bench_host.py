@@ -51,8 +51,8 @@ def test_cp_form_bytes():
     # one fixup step per (chunk, head): M_c and L_c read, fixed[c] written
     assert bench.FIX_STEP_BYTES == 3 * STATE
     # L and M returned by the scan schedule: written once, plus the factors
-    # (19,456 B written, read back with 32 KiB of q and k rows) per chunk-head
-    assert bench.lm_request_bytes(2) == bench.PRE_IO_BYTES + 4096 * (2 * STATE + 19456 + 19456 + 32768)
+    # (13,312 B written, read back with 32 KiB of q and k rows) per chunk-head
+    assert bench.lm_request_bytes(2) == bench.PRE_IO_BYTES + 4096 * (2 * STATE + 13312 + 13312 + 32768)
 
 
 def test_records_are_used_only_on_their_sources(tmp_path, monkeypatch):

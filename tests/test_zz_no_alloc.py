@@ -91,7 +91,7 @@ def test_noalloc_full_prefill_workload():
 
 def test_noalloc_refuses_calls_beyond_its_scratch():
     import gated_delta_rule_100_amd as gdr
-    # 8 x 4096 tokens, 32 heads: about 320 MB of chunk factors
+    # 8 x 4096 tokens, 32 heads: about 220 MB of chunk factors
     T, H, D, N = 32768, 32, 128, 8
     need = gdr.gdr_chunk_prefill_workspace_bytes(T, N, H, D, D, 64, gdr.GDR_BF16)
     assert need > SCRATCH_BYTES
