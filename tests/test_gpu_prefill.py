@@ -221,14 +221,20 @@ def test_prefill_scan_forms_agree_bitwise():
 def test_prefill_mixed_scan_agrees_bitwise(dk):
     # A batch whose column-split workgroups do not all fit the GPU at once but
     # whose longest sequence dominates: the scan runs that sequence in the
-    # split form and the others in whole tiles, in one launch.  Each sequence
-    # run alone takes the split form; both agree bit for bit, wherever the long
+    # split form and the others in whole tiles, in one launch (also with L and
+    # M requested, when the chunk-local kernel runs first).  Each sequence run
+    # alone takes the split form; all agree bit for bit, wherever the long
     # sequence sits in the batch.
     lens = [37, 0, 64, 5, 1, 650, 20, 129]
     d = workload(3, seed=131, seqlens=lens, H=32, dk=dk, dv=dk)
     say(f"prefill mixed scan: N={len(lens)} H=32 d={dk} T={d['T']} (long sequence 5)")
     packed = run_prefill(d, schedule="scan")
     check_against_oracle(d, packed, d["chunk"], check_locals=False)
+    with_lm = run_prefill(d, schedule="cp")  # L and M requested
+    nc = int(np.sum((np.array(lens) + 63) // 64))  # chunk slots written
+    assert torch.equal(with_lm["o"], packed["o"])
+    assert torch.equal(with_lm["state_out"], packed["state_out"])
+    assert torch.equal(with_lm["fixed"][:nc], packed["fixed"][:nc])
     cu = d["cu_seqlens"]
     for n in range(len(lens)):
         a, b = int(cu[n]), int(cu[n + 1])
@@ -299,6 +305,44 @@ def test_prefill_in_place_state():
     torch.cuda.synchronize()
     assert torch.equal(o, ref["o"])
     assert torch.equal(st, ref["state_out"])
+
+
+def test_prefill_mixed_scan_repeated():
+    """The mixed scan (the long sequence in the split form beside the others in
+    whole tiles) gives the same bits on every call, with and without L and M
+    requested."""
+    lens = [4000, 50, 300, 64, 1, 0, 700, 129]
+    d = workload(3, seed=141, seqlens=lens, H=32)
+    say(f"prefill mixed scan x8 against the same call with L and M, T={d['T']}")
+    ref = run_prefill(d, schedule="cp")
+    nc = int(np.sum((np.array(lens) + 63) // 64))  # chunk slots written
+    for _ in range(8):
+        got = run_prefill(d, schedule="scan")
+        assert torch.equal(got["o"], ref["o"])
+        assert torch.equal(got["state_out"], ref["state_out"])
+        assert torch.equal(got["fixed"][:nc], ref["fixed"][:nc])
+
+
+def test_prefill_in_place_state_mixed():
+    """The mixed scan in place gives the same bits as with a separate output,
+    and without initial states it matches the oracle from zero states."""
+    lens = [300, 1, 900, 0, 64, 70, 5, 200]
+    d = workload(3, seed=139, seqlens=lens, H=32, gate="slow")
+    say(f"prefill in-place state, mixed scan, T={d['T']}")
+    import gated_delta_rule_100_amd as gdr
+    di = dev_inputs(d)
+    ref = run_prefill(d, schedule="none")
+    st = di["state0"].clone()
+    o = torch.empty_like(ref["o"])
+    gdr.gdr_chunk_prefill(di["q"], di["k"], di["v"], di["g"], di["beta"], di["cu"], st, st, o,
+                          chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref["o"])
+    assert torch.equal(st, ref["state_out"])
+    zero = run_prefill(d, schedule="none", state_in="none")
+    d0 = dict(d)
+    d0["state0"] = np.zeros_like(d["state0"])
+    check_against_oracle(d0, zero, d["chunk"], check_locals=False)
 
 
 def test_prefill_in_place_state_segmented():
