@@ -887,7 +887,7 @@ __global__ __launch_bounds__(256, 2) void chunk_out_kernel(
 // Per-chunk factors of the sequential schedule (bf16 inputs, C = 64): the
 // matrices of the chunk that do not depend on the state,
 //   T = (I + A)^{-1}  and  P = (Q K^T) (.) Gamma  (both lower triangular in
-//   compact rows; 16 T as one fp16 plane, P as two bf16 planes),  gamma_t,
+//   compact rows; 16 T and 16 P as one fp16 plane each),  gamma_t,
 //   D_t, beta_t / 16,
 // laid out the way the scan kernel stages them.  The scan takes q, k, v
 // straight from the inputs and applies the UT transform itself:
