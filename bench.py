@@ -25,7 +25,7 @@ before each timed batch, so the host has enqueued the launches before the GPU
 reaches them and they run back to back (host overhead between launches does
 not enter the events).  Prefill figures are the median over per-launch
 durations (two events around each launch).  The decode and multi-token
-kernels (43 and 65 us) are timed as the average launch duration over a region
+kernels (42 and 49 us) are timed as the average launch duration over a region
 of back-to-back launches between two events, because an event pair around
 every launch adds about 1.5 us of marker gap to each; the per-launch median is
 reported beside it.  Decode is cold: four state buffers (512 MiB, more than
