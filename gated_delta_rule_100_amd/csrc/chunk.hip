@@ -378,7 +378,8 @@ struct ChunkWork {
   //   A_ts = beta_t Gamma_ts (k_t . k_s), s < t: diagonal blocks fp32 (zero on
   //     and above the diagonal), strictly lower blocks as planes;
   //   P = (Q K^T) (.) Gamma (s <= t, zero elsewhere) as one fp16 plane of
-  //     kPScale P (round to nearest even) in the compact lower layout (rows t < C/2 keep C/2 columns), each row in operand-slot
+  //     kPScale P (round to nearest even) in the compact lower layout (rows
+  //     t < C/2 keep C/2 columns), each row in operand-slot
   //     order: column 16 tj + c of 32-block tj/2 sits at slot
   //     8 (c/4) + 4 (tj % 2) + c % 4; in LDS the 16-byte pieces of a row are
   //     permuted (tl_piece).
