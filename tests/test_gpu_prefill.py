@@ -252,6 +252,28 @@ def test_prefill_mixed_scan_agrees_bitwise(dk):
         assert torch.equal(single["fixed"][:nc], packed["fixed"][c0:c0 + nc])
 
 
+def test_prefill_mixed_scan_eligibility_boundary():
+    # Up to 63 sequences a batch whose split form does not fit may take the
+    # mixed launch (here: one long sequence among short ones); with a 64th,
+    # empty sequence the same batch runs in whole tiles.  Same bits.
+    rng = np.random.default_rng(143)
+    lens = [int(x) for x in rng.integers(1, 100, size=63)]
+    lens[17], lens[40] = 1200, 0
+    d = workload(3, seed=143, seqlens=lens, H=2)
+    say(f"prefill mixed/whole boundary: N=63 and 64, H=2, T={d['T']}")
+    mixed = run_prefill(d, schedule="scan")
+    check_against_oracle(d, mixed, d["chunk"], check_locals=False)
+    d64 = dict(d)
+    d64["cu_seqlens"] = np.concatenate([d["cu_seqlens"], d["cu_seqlens"][-1:]]).astype(np.int32)
+    d64["state0"] = np.concatenate([d["state0"], d["state0"][:1]], axis=0)
+    d64["N"] = 64
+    whole = run_prefill(d64, schedule="scan")
+    nc = int(np.sum((np.array(lens) + 63) // 64))
+    assert torch.equal(mixed["o"], whole["o"])
+    assert torch.equal(mixed["state_out"], whole["state_out"][:63])
+    assert torch.equal(mixed["fixed"][:nc], whole["fixed"][:nc])
+
+
 def test_prefill_workspace_on_side_stream():
     """With no workspace given, the binding allocates one on the launch stream:
     a prefill on a side stream followed at once by allocations and writes on
