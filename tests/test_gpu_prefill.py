@@ -217,8 +217,8 @@ def test_prefill_scan_forms_agree_bitwise():
         assert torch.equal(single["fixed"][:nc], packed["fixed"][c0:c0 + nc])
 
 
-@pytest.mark.parametrize("dk", [128, 64])
-def test_prefill_mixed_scan_agrees_bitwise(dk):
+@pytest.mark.parametrize("dk,H", [(128, 32), (64, 32), (128, 12)])
+def test_prefill_mixed_scan_agrees_bitwise(dk, H):
     # A batch whose column-split workgroups do not all fit the GPU at once but
     # whose longest sequence dominates: the scan runs that sequence in the
     # split form and the others in whole tiles, in one launch (also with L and
@@ -226,8 +226,8 @@ def test_prefill_mixed_scan_agrees_bitwise(dk):
     # alone takes the split form; all agree bit for bit, wherever the long
     # sequence sits in the batch.
     lens = [37, 0, 64, 5, 1, 650, 20, 129]
-    d = workload(3, seed=131, seqlens=lens, H=32, dk=dk, dv=dk)
-    say(f"prefill mixed scan: N={len(lens)} H=32 d={dk} T={d['T']} (long sequence 5)")
+    d = workload(3, seed=131, seqlens=lens, H=H, dk=dk, dv=dk)
+    say(f"prefill mixed scan: N={len(lens)} H={H} d={dk} T={d['T']} (long sequence 5)")
     packed = run_prefill(d, schedule="scan")
     check_against_oracle(d, packed, d["chunk"], check_locals=False)
     with_lm = run_prefill(d, schedule="cp")  # L and M requested
